@@ -1,0 +1,390 @@
+"""Pins of the oracle's boundary and coefficient path: closed forms, invariants, brute force.
+
+CPU only. Each test is chosen so that a plausible slip in the oracle (a
+dropped term, a wrong sign or index, a transposed operand, sum for mean, eps
+outside the root, the wrong flatten order or scale group) fails at least one.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import codecs
+from mhc_hyper_connection_02_amd import synth
+
+bf = codecs.f64_to_bf16_bits
+dec = codecs.bf16_bits_to_f64
+
+
+def _tiny_boundary(seed=0, R=3, n=4, H=64, T=2):
+    return synth.boundary_inputs(seed, rows=R, hidden=H, tp=T)
+
+
+# ---------------------------------------------------------------------------
+# a1 / a2: the sublayer output
+# ---------------------------------------------------------------------------
+
+def test_tp_reduce_order_invariant_and_single_slice_copy():
+    d = _tiny_boundary(T=5)
+    xp = d["x_partials"]
+    a = oracle.tp_reduce(xp)
+    b = oracle.tp_reduce(xp[::-1])
+    assert np.array_equal(a, b)  # fp64 sums of 5 bf16 values are exact
+    assert np.array_equal(oracle.tp_reduce(xp[:1]), dec(xp[0]))
+
+
+def test_finalize_sum_brute_force():
+    d = synth.finalize_inputs(1, rows=3, hidden=64, top_k=2)
+    g, w, idx, sh = (d["gemm2_permuted"], d["expert_weights"],
+                     d["expanded_idx_to_permuted_idx"], d["shared_output"])
+    got = oracle.moe_finalize_sum(g, w, idx, sh)
+    gv, shv = dec(g), dec(sh)
+    for r in range(3):
+        for h in range(64):
+            acc = shv[r, h]
+            for k in range(2):
+                acc += float(w[r, k]) * gv[int(idx[r * 2 + k]), h]
+            assert got[r, h] == pytest.approx(acc, rel=1e-15, abs=1e-300)
+
+
+def test_finalize_one_hot_gather_is_bit_exact():
+    """One-hot weights, zero shared output, comb = 0, post = 1: the streams are g[idx] exactly."""
+    R, K, H, n = 4, 3, 96, 4
+    d = synth.finalize_inputs(2, rows=R, hidden=H, top_k=K)
+    rng = np.random.default_rng(0)
+    pick = rng.integers(0, K, size=R)
+    w = np.zeros((R, K), np.float32)
+    w[np.arange(R), pick] = 1.0
+    comb = np.zeros((R, n, n), np.float32)
+    post = np.ones((R, n), np.float32)
+    out = oracle.finalize(d["gemm2_permuted"], w, d["expanded_idx_to_permuted_idx"],
+                          np.zeros((R, H), np.uint16), d["residual"], post, comb, None, None, 0.0)
+    idx = d["expanded_idx_to_permuted_idx"]
+    for r in range(R):
+        want = d["gemm2_permuted"][idx[r * K + pick[r]]]
+        for i in range(n):
+            assert np.array_equal(out["residual"][r, i], want)
+
+
+def test_finalize_out_of_range_index_contributes_nothing():
+    d = synth.finalize_inputs(3, rows=2, hidden=32, top_k=2)
+    idx = d["expanded_idx_to_permuted_idx"].copy()
+    idx[1] = -1
+    idx[2] = 10_000
+    got = oracle.moe_finalize_sum(d["gemm2_permuted"], d["expert_weights"], idx, d["shared_output"])
+    g, w, sh = dec(d["gemm2_permuted"]), d["expert_weights"].astype(np.float64), dec(d["shared_output"])
+    want0 = sh[0] + w[0, 0] * g[idx[0]]
+    want1 = sh[1] + w[1, 1] * g[idx[3]]
+    assert np.allclose(got[0], want0, rtol=1e-15) and np.allclose(got[1], want1, rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# a3: the mHC post
+# ---------------------------------------------------------------------------
+
+def test_post_identity_comb_zero_post_is_identity():
+    d = _tiny_boundary()
+    R, n = d["post"].shape
+    eye = np.broadcast_to(np.eye(n, dtype=np.float32), (R, n, n)).copy()
+    out = oracle.boundary(d["x_partials"], d["residual"], np.zeros((R, n), np.float32), eye,
+                          None, None, 0.0)
+    assert np.array_equal(out["residual"], d["residual"])
+
+
+def test_post_permutation_comb_moves_streams():
+    """comb[r,i,j] = [j == pi(i)] sends input stream pi(i) to output stream i (bit-exact)."""
+    d = _tiny_boundary()
+    R, n = d["post"].shape
+    pi = np.array([2, 0, 3, 1])  # not an involution: a transposed comb gives pi^-1 instead
+    comb = np.zeros((R, n, n), np.float32)
+    comb[:, np.arange(n), pi] = 1.0
+    out = oracle.boundary(d["x_partials"], d["residual"], np.zeros((R, n), np.float32), comb,
+                          None, None, 0.0)
+    for i in range(n):
+        assert np.array_equal(out["residual"][:, i], d["residual"][:, pi[i]])
+
+
+def test_post_adds_post_times_rounded_x():
+    d = _tiny_boundary()
+    R, n = d["post"].shape
+    post = np.tile(np.array([1.0, 2.0, -0.5, 0.25], np.float32), (R, 1))
+    out = oracle.boundary(d["x_partials"], d["residual"], post, np.zeros((R, n, n), np.float32),
+                          None, None, 0.0)
+    x = dec(bf(oracle.tp_reduce(d["x_partials"])))  # x is rounded to bf16 first
+    for i in range(n):
+        assert np.array_equal(out["residual"][:, i], bf(post[0, i] * x))
+
+
+def test_post_doubly_stochastic_conserves_stream_sum():
+    d = _tiny_boundary(H=256)
+    R, n = d["post"].shape
+    out = oracle.boundary(d["x_partials"], d["residual"], np.zeros((R, n), np.float32), d["comb"],
+                          None, None, 0.0)
+    s_in = dec(d["residual"]).sum(axis=1)
+    s_out = dec(out["residual"]).sum(axis=1)
+    bound = n * 2.0 ** -8 * np.abs(dec(out["residual"])).max(axis=1) + 1e-6 * np.abs(s_in).max()
+    assert np.all(np.abs(s_in - s_out) <= bound)
+
+
+def test_post_uniform_comb_gives_stream_mean():
+    d = _tiny_boundary()
+    R, n = d["post"].shape
+    comb = np.full((R, n, n), 1.0 / n, np.float32)  # 0.25 is exact
+    out = oracle.boundary(d["x_partials"], d["residual"], np.zeros((R, n), np.float32), comb,
+                          None, None, 0.0)
+    m = oracle.collapse_mean(d["residual"])
+    for i in range(n):
+        assert np.array_equal(out["residual"][:, i], m)
+
+
+# ---------------------------------------------------------------------------
+# a4 / a5: collapse and RMSNorm
+# ---------------------------------------------------------------------------
+
+def test_collapse_unit_pre_selects_stream():
+    d = _tiny_boundary()
+    R, n = d["pre"].shape
+    for k in range(n):
+        pre = np.zeros((R, n), np.float32)
+        pre[:, k] = 1.0
+        assert np.array_equal(oracle.collapse(d["residual"], pre), dec(d["residual"][:, k]))
+
+
+def test_rmsnorm_closed_forms():
+    H = 64
+    alt = np.where(np.arange(H) % 2 == 0, 1.0, -1.0)[None, :]
+    one = bf(np.ones(H))
+    # mean(y^2) = 1, eps = 3: out = +-1/sqrt(4) = +-0.5 (pins eps inside the root, mean not sum)
+    assert np.array_equal(dec(oracle.rms_norm(alt, one, 3.0)), 0.5 * alt)
+    # scale invariance without eps: c * alt -> +-1 for any c > 0
+    assert np.array_equal(dec(oracle.rms_norm(37.5 * alt, one, 0.0)), alt)
+    # the weight multiplies after normalizing
+    two = bf(np.full(H, 2.0))
+    assert np.array_equal(dec(oracle.rms_norm(alt, two, 0.0)), 2 * alt)
+    # a constant row c with eps: c / sqrt(c^2 + eps)
+    c, eps = 0.75, 0.4375  # c^2 + eps = 1
+    got = dec(oracle.rms_norm(np.full((1, H), c), one, eps))
+    assert np.array_equal(got, np.full((1, H), c))
+
+
+def test_identity_premix_selects_stream_zero_rms_normed():
+    """comb = I, post = 0, pre = e0: streams unchanged, layer input = RMSNorm(stream 0)."""
+    R, n, H = 2, 4, 64
+    rng = np.random.default_rng(11)
+    res = bf(rng.normal(size=(R, n, H)))
+    alt = np.where(np.arange(H) % 2 == 0, 1.0, -1.0)
+    res[:, 0] = bf(np.stack([3.0 * alt, -0.5 * alt]))  # RMS 3 and 0.5: closed-form output +-1, -+1
+    eye = np.broadcast_to(np.eye(n, dtype=np.float32), (R, n, n)).copy()
+    pre = np.zeros((R, n), np.float32)
+    pre[:, 0] = 1.0
+    xp = bf(rng.normal(size=(1, R, H)))
+    out = oracle.boundary(xp, res, np.zeros((R, n), np.float32), eye, pre, bf(np.ones(H)), 0.0)
+    assert np.array_equal(out["residual"], res)
+    assert np.array_equal(dec(out["layer_input"]), np.stack([alt, -alt]))
+
+
+def test_layer_input_scale_invariance_of_premix():
+    d = _tiny_boundary()
+    a = oracle.boundary(d["x_partials"], d["residual"], d["post"], d["comb"], d["pre"],
+                        d["norm_weight"], 0.0)
+    b = oracle.boundary(d["x_partials"], d["residual"], d["post"], d["comb"], 4.0 * d["pre"],
+                        d["norm_weight"], 0.0)
+    assert np.array_equal(a["layer_input"], b["layer_input"])
+
+
+def test_residual_only_streams_equal_full_boundary_streams():
+    d = _tiny_boundary()
+    full = oracle.boundary(d["x_partials"], d["residual"], d["post"], d["comb"], d["pre"],
+                           d["norm_weight"], d["eps"])
+    ro = oracle.residual_only(d["x_partials"], d["residual"], d["post"], d["comb"])
+    assert np.array_equal(full["residual"], ro)
+    assert set(full) == {"residual", "layer_input"}
+
+
+def test_mxfp8_output_is_quantized_layer_input():
+    d = synth.boundary_inputs(4, rows=2, hidden=128, tp=3)
+    out = oracle.boundary(d["x_partials"], d["residual"], d["post"], d["comb"], d["pre"],
+                          d["norm_weight"], d["eps"], mxfp8=True)
+    codes, scales = codecs.mxfp8_quantize(out["layer_input"])
+    assert np.array_equal(out["mx_data"], codes) and np.array_equal(out["mx_scale"], scales)
+    assert out["mx_scale"].shape == (2, 4)
+
+
+def test_collapse_mean_of_identical_streams():
+    rng = np.random.default_rng(2)
+    s = bf(rng.normal(size=(3, 1, 40)))
+    s4 = np.repeat(s, 4, axis=1)
+    assert np.array_equal(oracle.collapse_mean(s4), s[:, 0])
+
+
+# ---------------------------------------------------------------------------
+# a9 - a12: the coefficient path
+# ---------------------------------------------------------------------------
+
+def _golden_sinkhorn(golden_dir):
+    with open(os.path.join(golden_dir, "sinkhorn_2x2.json")) as f:
+        return json.load(f)
+
+
+def test_sinkhorn_one_iteration_golden(golden_dir):
+    g = _golden_sinkhorn(golden_dir)
+    logits = np.log(np.array(g["matrix"], np.float64))
+    got = oracle.sinkhorn(logits, 1, 0.0)
+    want = np.array([[eval(v) for v in row] for row in g["one_iteration"]])
+    assert np.allclose(got, want, rtol=1e-14, atol=0)
+
+
+def test_sinkhorn_converges_to_2x2_closed_form(golden_dir):
+    g = _golden_sinkhorn(golden_dir)
+    p = eval(g["converged_p_expr"], {"__builtins__": {}}, {})
+    got = oracle.sinkhorn(np.log(np.array(g["matrix"], np.float64)), 200, 0.0)
+    assert np.allclose(got, [[p, 1 - p], [1 - p, p]], rtol=0, atol=1e-13)
+
+
+def test_sinkhorn_shift_invariance():
+    """Row shifts of the logits scale rows of exp(logits): the first (row) step removes them at
+    any iteration count. Column shifts are removed only in the limit (the unique scaling)."""
+    rng = np.random.default_rng(3)
+    z = rng.normal(size=(4, 4))
+    rows = rng.normal(size=(4, 1))
+    cols = rng.normal(size=(1, 4))
+    assert np.allclose(oracle.sinkhorn(z, 7, 0.0), oracle.sinkhorn(z + rows, 7, 0.0),
+                       rtol=1e-12, atol=1e-14)
+    assert np.allclose(oracle.sinkhorn(z, 500, 0.0), oracle.sinkhorn(z + rows + cols, 500, 0.0),
+                       rtol=1e-10, atol=1e-12)
+
+
+def test_sinkhorn_columns_after_every_call_rows_only_at_convergence():
+    rng = np.random.default_rng(4)
+    eps = 1e-6
+    for _ in range(20):
+        z = rng.normal(0, 2, size=(4, 4))
+        for iters in (1, 3, 20):
+            # a column whose mass was S before its step sums to S / (S + eps) after it:
+            # never above 1, and within 2 eps of 1 once S is near 1 (a few iterations in)
+            A = oracle.sinkhorn(z, iters, eps)
+            assert np.all(A.sum(axis=0) <= 1 + 1e-15)
+            assert np.allclose(oracle.sinkhorn(z, iters, 0.0).sum(axis=0), 1, rtol=0, atol=1e-15)
+        A = oracle.sinkhorn(z, 20, eps)
+        assert np.all(np.abs(A.sum(axis=0) - 1) <= 2 * eps)
+        A = oracle.sinkhorn(z, 1000, eps)
+        assert np.all(np.abs(A.sum(axis=1) - 1) <= 1e-5)
+        assert np.all(np.abs(A.sum(axis=0) - 1) <= 2 * eps)
+    # the last half-step is the column one: after one iteration rows are generally off
+    A = oracle.sinkhorn(np.array([[0.0, 3.0], [1.0, 0.0]]), 1, 0.0)
+    assert np.allclose(A.sum(axis=0), 1, atol=1e-15) and not np.allclose(A.sum(axis=1), 1, atol=1e-3)
+
+
+def test_sinkhorn_equal_logits_uniform():
+    A = oracle.sinkhorn(np.full((4, 4), 0.7), 20, 1e-6)
+    assert np.all(np.abs(A - 0.25) <= 1e-6)
+
+
+def _pre_case(R=3, n=4, H=32, seed=0):
+    return synth.pre_inputs(seed, rows=R, hidden=H, n=n)
+
+
+def _call_pre(d, **kw):
+    args = dict(d)
+    args.update(kw)
+    return oracle.pre_coeffs(args["residual"], args["fn"], args["scale"], args["base"],
+                             args["rms_eps"], args["pre_eps"], args["sinkhorn_eps"],
+                             args["post_alpha"], args["sinkhorn_iters"])
+
+
+def test_pre_zero_fn_zero_base_closed_form():
+    d = _pre_case()
+    R, n = 3, 4
+    fn0 = np.zeros_like(d["fn"])
+    pre, post, comb = _call_pre(d, fn=fn0, base=np.zeros(24, np.float32))
+    assert np.allclose(pre, 0.5 + d["pre_eps"], rtol=0, atol=1e-15)
+    assert np.allclose(post, 1.0, rtol=0, atol=1e-15)  # alpha * sigmoid(0) = 2 * 0.5
+    assert np.all(np.abs(comb - 0.25) <= 1e-6)
+
+
+def test_pre_base_only_closed_form_and_group_order():
+    """fn = 0 gives l' = base: pre = sigmoid(base[0:n]) + eps, post = alpha * sigmoid(base[n:2n])."""
+    d = _pre_case()
+    n = 4
+    base = np.zeros(24, np.float32)
+    base[:n] = [0.0, math.log(3.0), -math.log(3.0), 2.0]
+    base[n:2 * n] = [math.log(3.0), 0.0, 0.0, -1.0]
+    pre, post, comb = _call_pre(d, fn=np.zeros_like(d["fn"]), base=base)
+    b = base.astype(np.float64)
+    assert np.allclose(pre[0], [0.5 + 1e-6, 0.75 + 1e-6, 0.25 + 1e-6, 1 / (1 + math.exp(-b[3])) + 1e-6],
+                       rtol=0, atol=1e-7)
+    assert np.allclose(post[0], [1.5, 1.0, 1.0, 2 / (1 + math.e)], rtol=0, atol=1e-7)
+
+
+def test_pre_one_hot_fn_pins_flatten_order_rms_and_scale_groups():
+    """fn with one 1 per column picks v[k_c]: l_c = inv * v[k_c], k = i*H + h (stream-major)."""
+    R, n, H = 2, 4, 32
+    d = _pre_case(R=R, n=n, H=H, seed=9)
+    nc = 2 * n + n * n
+    ks = [(c * 5 + 3) % (n * H) for c in range(nc)]
+    fn = np.zeros((n * H, nc))
+    for c, k in enumerate(ks):
+        fn[k, c] = 1.0
+    scale = np.array([2.0, 0.5, 1.5], np.float32)
+    base = np.linspace(-0.2, 0.3, nc).astype(np.float32)
+    pre, post, comb = _call_pre(d, fn=bf(fn), scale=scale, base=base, sinkhorn_iters=0)
+    s = dec(d["residual"])
+    for r in range(R):
+        v = [s[r, k // H, k % H] for k in range(n * H)]  # stream-major flatten by hand
+        inv = 1.0 / math.sqrt(sum(x * x for x in v) / (n * H) + d["rms_eps"])
+        lp = [inv * v[ks[c]] * float(scale[0 if c < n else 1 if c < 2 * n else 2]) + float(base[c])
+              for c in range(nc)]
+        for i in range(n):
+            assert pre[r, i] == pytest.approx(1 / (1 + math.exp(-lp[i])) + d["pre_eps"], abs=1e-13)
+            assert post[r, i] == pytest.approx(2 / (1 + math.exp(-lp[n + i])), abs=1e-13)
+        # zero Sinkhorn iterations leave exp(l' - rowmax): row i, column j is column 2n + n*i + j
+        for i in range(n):
+            row = [lp[2 * n + n * i + j] for j in range(n)]
+            m = max(row)
+            for j in range(n):
+                assert comb[r, i, j] == pytest.approx(math.exp(row[j] - m), abs=1e-13)
+
+
+def test_pre_rms_scale_invariance():
+    d = _pre_case(seed=5)
+    a = _call_pre(d, rms_eps=0.0)
+    b = _call_pre(d, residual=bf(4.0 * dec(d["residual"])), rms_eps=0.0)
+    for x, y in zip(a, b):
+        assert np.allclose(x, y, rtol=1e-13, atol=1e-15)
+
+
+def test_pre_ranges():
+    d = _pre_case(R=6, seed=6)
+    pre, post, comb = _call_pre(d)
+    assert np.all(pre > d["pre_eps"]) and np.all(pre < 1 + d["pre_eps"])
+    assert np.all(post > 0) and np.all(post < d["post_alpha"])
+    assert np.all(comb >= 0)
+    assert np.all(np.abs(comb.sum(axis=1) - 1) <= 2 * d["sinkhorn_eps"])  # column sums
+
+
+# ---------------------------------------------------------------------------
+# The chained step's plumbing
+# ---------------------------------------------------------------------------
+
+def test_decode_chain_uses_the_delayed_pre():
+    rows, hidden, n = 4, 64, 4
+    emb = synth.chain_embedding(rows, hidden)
+    subs = [synth.chain_sublayer(L, ffn, rows=rows, hidden=hidden, tp=2, top_k=2)
+            for L in range(2) for ffn in (False, True)]
+    p = synth.chain_params()
+    rec = []
+    streams, mean = oracle.decode_chain(emb, subs, p["rms_eps"], p["hc_eps"], p["post_alpha"],
+                                        p["sinkhorn_iters"], p["norm_eps"], record=rec)
+    assert len(rec) == 1 + len(subs)
+    for b in range(1, len(subs)):
+        prev, cur = rec[b - 1], rec[b]
+        want = oracle.rms_norm(oracle.collapse(cur["residual"], prev["pre"].astype(np.float32)),
+                               subs[b]["norm_w"], p["norm_eps"])
+        assert np.array_equal(cur["layer_input"], want)
+        assert ("mx_data" in cur) == subs[b]["mxfp8"]
+    assert "layer_input" not in rec[-1]
+    assert np.array_equal(mean, oracle.collapse_mean(streams))
