@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused mHC boundary on one MI355X.
+
+Prints ONE JSON line. The headline is the decode boundary with the MXFP8 layer
+input at rows=32, hidden=7168, hc_mult=4, tp=8: achieved HBM GB/s over the
+algorithmic bytes of a call (read-once inputs plus written outputs), with the
+inputs already resident in HBM. Every input and output rotates over enough
+buffer sets (>= 512 MB) that no call finds its data in the 256 MB Infinity
+Cache left there by an earlier call. The other calls of the path are timed the
+same way and reported under "rows"; ``--chain`` adds the 61-layer chained
+decode step.
+
+Timing: W eager warm-up calls, then EXACTLY K calls captured in one HIP graph
+and replayed once between two events recorded on the launch stream (the
+caller's graph is how the path runs in a decode step); the eager per-call
+time of the same K calls is reported beside it.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused mHC boundary µs/call + achieved HBM GB/s (rows=32, hidden=7168, hc=4)"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "boundary_decode_r32_h7168_traffic.json")
+KERNEL_SOURCES = ["boundary.hip", "device_common.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--block", type=int, default=None, help="boundary workgroup size (64/128/256)")
+    ap.add_argument("--chain", action="store_true", help="also time the 61-layer chained step")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--no-rows", action="store_true", help="time only the headline call")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes per call (read-once inputs + written outputs)
+# ---------------------------------------------------------------------------
+
+def bytes_boundary(rows, hidden, tp, n=4, pre=True, mxfp8=False):
+    per_row = tp * hidden * 2 + 2 * n * hidden * 2 + (n + n * n) * 4
+    if pre:
+        per_row += n * 4 + hidden * 2
+    if mxfp8:
+        per_row += hidden + hidden // 32
+    return rows * per_row + (hidden * 2 if pre else 0)
+
+
+def bytes_finalize(rows, hidden, top_k, n=4, pre=True, mxfp8=False):
+    # gathered expert rows + weights + indices + shared row replace the tp partials
+    per_row = top_k * (hidden * 2 + 4 + 4) + hidden * 2 + 2 * n * hidden * 2 + (n + n * n) * 4
+    if pre:
+        per_row += n * 4 + hidden * 2
+    if mxfp8:
+        per_row += hidden + hidden // 32
+    return rows * per_row + (hidden * 2 if pre else 0)
+
+
+def bytes_pre(rows, hidden, n=4):
+    nc = 2 * n + n * n
+    return rows * n * hidden * 2 + n * hidden * nc * 2 + (3 + nc) * 4 + rows * nc * 4
+
+
+def bytes_mean(rows, hidden, n=4):
+    return rows * n * hidden * 2 + rows * hidden * 2
+
+
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+
+def time_calls(torch, calls, steps, warmup):
+    """calls: list of zero-argument launchers, one per buffer set; call i uses set i % len."""
+    nset = len(calls)
+    for i in range(warmup):
+        calls[i % nset]()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        calls[i % nset]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            calls[i % nset]()
+    g.replay()  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1)
+    del g
+    return eager_ms / steps * 1e3, graph_ms / steps * 1e3  # us per call
+
+
+def n_sets(bytes_per_set):
+    return max(2, int((2 * MALL_BYTES + bytes_per_set - 1) // bytes_per_set))
+
+
+def row_entry(name, nbytes, us_eager, us_graph, sets):
+    us = us_graph
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us_per_call": round(us, 3), "us_per_call_eager": round(us_eager, 3),
+            "algorithmic_bytes": int(nbytes), "gb_per_s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "buffer_sets": sets}
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mhc_hyper_connection_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(block):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
+    the current kernel source at this block size; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash() or t.get("block") != block:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# the benchmark
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path has no "
+              "collectives; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from mhc_hyper_connection_02_amd import binding, synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    T = lambda a: synth.to_torch(a, dev)  # noqa: E731
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    # --- headline: config 1, decode boundary + MXFP8 --------------------------------
+    R, H, TP = 32, 7168, 8
+    d1 = synth.config(1)
+    h = binding.Handle(H, 4, max_rows=128, max_tp=8, top_k=8)
+    if args.block:
+        h.set_option(binding.MHC_OPT_BOUNDARY_BLOCK, args.block)
+    block = args.block or 64
+    nb = bytes_boundary(R, H, TP, pre=True, mxfp8=True)
+    sets = n_sets(nb)
+    base = {k: T(d1[k]) for k in ("x_partials", "residual", "post", "comb", "pre", "norm_weight")}
+    bufs = []
+    for _ in range(sets):
+        bufs.append({
+            "x": base["x_partials"].clone(), "s": base["residual"].clone(),
+            "so": torch.empty_like(base["residual"]),
+            "li": torch.empty((R, H), dtype=torch.bfloat16, device=dev),
+            "md": torch.empty((R, H), dtype=torch.uint8, device=dev),
+            "ms": torch.empty((R, H // 32), dtype=torch.uint8, device=dev),
+        })
+    log(f"headline: boundary rows={R} hidden={H} tp={TP} mxfp8, {sets} buffer sets, block {block}")
+
+    def mk(b):
+        return lambda: binding.boundary(h, b["x"], b["s"], base["post"], base["comb"], base["pre"],
+                                        base["norm_weight"], d1["eps"], mxfp8=True,
+                                        residual_out=b["so"], layer_input_out=b["li"],
+                                        mx_out=(b["md"], b["ms"]))
+
+    us_e, us_g = time_calls(torch, [mk(b) for b in bufs], args.steps, args.warmup)
+    rows = {"boundary_decode_mxfp8": row_entry("boundary", nb, us_e, us_g, sets)}
+    log(f"  {rows['boundary_decode_mxfp8']}")
+    del bufs
+
+    if not args.no_rows:
+        # residual-only at config 1
+        nro = bytes_boundary(R, H, TP, pre=False)
+        s2 = n_sets(nro)
+        bufs = [{"x": base["x_partials"].clone(), "s": base["residual"].clone(),
+                 "so": torch.empty_like(base["residual"])} for _ in range(s2)]
+        calls = [(lambda b=b: binding.residual_only(h, b["x"], b["s"], base["post"], base["comb"],
+                                                    residual_out=b["so"])) for b in bufs]
+        e, g = time_calls(torch, calls, args.steps, args.warmup)
+        rows["residual_only_decode"] = row_entry("residual_only", nro, e, g, s2)
+        log(f"  residual-only {rows['residual_only_decode']}")
+        del bufs, calls
+
+        # finalize at config 2
+        d2 = synth.config(2)
+        R2, K2 = 64, 8
+        nf = bytes_finalize(R2, H, K2, pre=True, mxfp8=True)
+        s3 = n_sets(nf)
+        c2 = {k: T(d2[k]) for k in ("expert_weights", "expanded_idx_to_permuted_idx", "post",
+                                     "comb", "pre", "norm_weight")}
+        g0, sh0, r0 = T(d2["gemm2_permuted"]), T(d2["shared_output"]), T(d2["residual"])
+        bufs = [{"g": g0.clone(), "sh": sh0.clone(), "s": r0.clone(), "so": torch.empty_like(r0),
+                 "li": torch.empty((R2, H), dtype=torch.bfloat16, device=dev),
+                 "md": torch.empty((R2, H), dtype=torch.uint8, device=dev),
+                 "ms": torch.empty((R2, H // 32), dtype=torch.uint8, device=dev)}
+                for _ in range(s3)]
+        calls = [(lambda b=b: binding.finalize(
+            h, b["g"], c2["expert_weights"], c2["expanded_idx_to_permuted_idx"], b["sh"], b["s"],
+            c2["post"], c2["comb"], c2["pre"], c2["norm_weight"], d2["eps"], mxfp8=True,
+            residual_out=b["so"], layer_input_out=b["li"], mx_out=(b["md"], b["ms"])))
+            for b in bufs]
+        e, g = time_calls(torch, calls, args.steps, args.warmup)
+        rows["finalize_moe_mxfp8"] = row_entry("finalize", nf, e, g, s3)
+        log(f"  finalize {rows['finalize_moe_mxfp8']}")
+        del bufs, calls
+
+        # coefficient path at config 3
+        d3 = synth.config(3)
+        npb = bytes_pre(64, H)
+        s4 = n_sets(npb)
+        sc, bs = T(d3["scale"]), T(d3["base"])
+        r3, fn3 = T(d3["residual"]), T(d3["fn"])
+        bufs = [{"s": r3.clone(), "fn": fn3.clone(),
+                 "o": (torch.empty((64, 4), device=dev), torch.empty((64, 4), device=dev),
+                       torch.empty((64, 4, 4), device=dev))} for _ in range(s4)]
+        calls = [(lambda b=b: binding.pre_coeffs(h, b["s"], b["fn"], sc, bs, d3["rms_eps"],
+                                                 d3["pre_eps"], d3["sinkhorn_eps"],
+                                                 d3["post_alpha"], d3["sinkhorn_iters"],
+                                                 out=b["o"])) for b in bufs]
+        e, g = time_calls(torch, calls, args.steps, args.warmup)
+        rows["pre_coeffs"] = row_entry("pre_coeffs", npb, e, g, s4)
+        log(f"  pre_coeffs {rows['pre_coeffs']}")
+        del bufs, calls
+
+        # mean-collapse at the chained step's 128 rows
+        nm = bytes_mean(128, H)
+        s5 = n_sets(nm)
+        sm = T(synth.boundary_inputs(5, rows=128, hidden=H, tp=1)["residual"])
+        bufs = [{"s": sm.clone(), "o": torch.empty((128, H), dtype=torch.bfloat16, device=dev)}
+                for _ in range(s5)]
+        calls = [(lambda b=b: binding.collapse_mean(h, b["s"], out=b["o"])) for b in bufs]
+        e, g = time_calls(torch, calls, args.steps, args.warmup)
+        rows["collapse_mean_r128"] = row_entry("collapse_mean", nm, e, g, s5)
+        log(f"  collapse_mean {rows['collapse_mean_r128']}")
+        del bufs, calls
+
+    if args.chain:
+        from mhc_hyper_connection_02_amd import chain as chain_mod
+        log("chain: generating 122 sublayers of synthetic inputs")
+        t0 = time.time()
+        step = chain_mod.DecodeChain.from_synth(dev)
+        log(f"  inputs ready in {time.time() - t0:.1f} s ({step.input_bytes() / 1e9:.2f} GB)")
+        us_e, us_g = time_calls(torch, [step.run], max(3, args.steps // 40), 2)
+        rows["chain_decode_step"] = {"us_per_step": round(us_g, 1),
+                                     "us_per_step_eager": round(us_e, 1),
+                                     "algorithmic_bytes": int(step.algorithmic_bytes()),
+                                     "gb_per_s": round(step.algorithmic_bytes() / us_g / 1e3, 1)}
+        log(f"  chain {rows['chain_decode_step']}")
+        del step
+
+    head = rows["boundary_decode_mxfp8"]
+    us = head["us_per_call"]
+    achieved = head["gb_per_s"]
+    traffic = measured_traffic(block)
+    out = {
+        "metric": METRIC,
+        "value": achieved,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
+        "us_per_call": us,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode boundary + MXFP8 layer input: rows=32 hidden=7168 "
+                               "hc_mult=4 tp=8 (bf16 in/out, fp32 arithmetic)",
+                   "rows": R, "hidden": H, "hc_mult": 4, "tp": TP, "mxfp8": True,
+                   "block": block, "buffer_sets": head["buffer_sets"],
+                   "timing": "one HIP graph of the K calls, events on the launch stream"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": nb},
+        "rows": rows,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(d1, nb, args.cpu_seconds, log)
+    print(json.dumps(out), flush=True)
+    h.close()
+
+
+def cpu_baseline(d, nbytes, seconds, log):
+    """The oracle as it stands (numpy fp64) on the same config-1 inputs, repeated for about
+    `seconds` of host time."""
+    import oracle
+    log(f"cpu baseline: oracle boundary on config 1, ~{seconds:.0f} s")
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.boundary(d["x_partials"], d["residual"], d["post"], d["comb"], d["pre"],
+                        d["norm_weight"], d["eps"], mxfp8=True)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / n
+    return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "ms_per_call": round(per * 1e3, 2),
+            "sample": f"{n} full calls of the config-1 boundary (32 rows, MXFP8) in {el:.1f} s; "
+                      "numpy fp64 loops, one thread"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * mhc.h -- C ABI of the MI355X (gfx950) fused mHC boundary library, libmhc_amd.so.
+ *
+ * Pages cited (by title and section):
+ *   boundary page   vllm.models.deepseek_v41.nvidia.specialized_decode.boundary.boundary
+ *   all_reduce page vllm.models.deepseek_v41.nvidia.specialized_decode.boundary.all_reduce
+ *   decode page     vllm.models.deepseek_v41.nvidia.specialized_decode.runtime.decode
+ *
+ * Conventions for every entry point
+ *   - Tensor arguments are DEVICE pointers owned by the caller; the library
+ *     never frees or keeps them. They must stay valid until the stream has
+ *     passed the call.
+ *   - bf16 tensors are passed as raw bit patterns (uint16_t), fp32 as float,
+ *     E4M3 data and E8M0 scales as uint8_t. Every tensor is dense row-major in
+ *     the shape given beside it. R = rows, n = hc_mult, H = hidden,
+ *     T = tp, K = top_k.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *     stream), in stream order; nothing synchronizes the host.
+ *   - Every call validates all of its arguments before any device work and
+ *     returns an mhc_status. Nothing is launched when the status is not
+ *     MHC_OK. Faults inside a launched kernel surface at the caller's next
+ *     synchronization, as HIP reports them.
+ *   - rows == 0 is a valid empty call: it returns MHC_OK and touches nothing
+ *     (pointers are then not checked).
+ *   - A handle owns a small device scratch area (per-row partial sums,
+ *     arrival counters, coefficient partials). Calls on one handle must be
+ *     serialized, i.e. issued on one stream or ordered by the caller; two
+ *     overlapping calls on one handle race on its scratch.
+ *   - The only aliasing allowed is residual_out == residual (in-place update
+ *     of the streams); any other overlap of inputs and outputs is undefined.
+ *   - Alignment: bf16 tensors 16 bytes; fp32 and int32 tensors 4 bytes;
+ *     mx_data_out 8 bytes. Otherwise MHC_ERR_ALIGN.
+ */
+#ifndef MHC_AMD_H
+#define MHC_AMD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mhc_ctx* mhc_handle; /* opaque */
+typedef void* mhc_stream_t;         /* a hipStream_t */
+
+enum mhc_status {
+  MHC_OK = 0,
+  MHC_ERR_INVALID_ARG = 1, /* null handle or required pointer, inconsistent optional outputs */
+  MHC_ERR_SHAPE = 2,       /* a size that is negative, zero where it must be positive, or too large */
+  MHC_ERR_ALIGN = 3,       /* a pointer not aligned as stated above */
+  MHC_ERR_LIMIT = 4,       /* rows > max_rows or tp > max_tp of the handle */
+  MHC_ERR_UNSUPPORTED = 5, /* hc_mult other than 4, or MXFP8 with hidden % 32 != 0 */
+  MHC_ERR_HIP = 6,         /* a HIP runtime call failed (allocation, launch) */
+  MHC_ERR_DEVICE = 7       /* the current HIP device is not the handle's device */
+};
+
+/* Human-readable name of a status code (a static string; never NULL). */
+const char* mhc_status_string(int status);
+
+/*
+ * mhc_create -- a handle sized for every call it will serve.
+ *
+ * all_reduce page, BoundaryAllReduce.__init__: the fused kernel is sized once
+ * by the model's hidden size, hc_mult, the largest row count it serves and
+ * the MoE top_k, on one device. Here also by the largest number of TP
+ * partial slices, max_tp.
+ *   hidden   > 0, a multiple of 8 (16-byte vectors)       else MHC_ERR_SHAPE
+ *   hc_mult  == 4                                         else MHC_ERR_UNSUPPORTED
+ *   max_rows in [1, 65536], max_tp in [1, 64], top_k in [1, 64]  else MHC_ERR_SHAPE
+ *   device   a valid HIP device index                     else MHC_ERR_HIP
+ * Allocates the handle's device scratch on `device` (hipMalloc) and zeroes it
+ * (synchronously). On failure *out is set to NULL. The sizes are checked
+ * before any HIP call.
+ */
+int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int device,
+               mhc_handle* out);
+
+/*
+ * mhc_set_option -- performance knobs of a handle (results do not depend on them).
+ *   MHC_OPT_BOUNDARY_BLOCK: threads per workgroup of the boundary kernels, 64, 128 or
+ *   256 (default 64). Each thread owns 8 hidden elements of a row, so a row is split
+ *   into ceil(H / (8 * block)) workgroups. Other values: MHC_ERR_SHAPE.
+ * Unknown options: MHC_ERR_INVALID_ARG. Takes effect for calls issued afterwards.
+ */
+enum mhc_option { MHC_OPT_BOUNDARY_BLOCK = 1 };
+int mhc_set_option(mhc_handle h, int option, int value);
+
+/* Frees the handle and its scratch (synchronizes the device first). NULL is a no-op. */
+int mhc_destroy(mhc_handle h);
+
+/*
+ * mhc_reset -- re-zero the handle's arrival counters on `stream`.
+ *
+ * all_reduce page, BoundaryAllReduce.reset: drop what an aborted step left
+ * behind. The counters return to zero by themselves after every completed
+ * call; this is only needed after a call whose kernels did not complete.
+ */
+int mhc_reset(mhc_handle h, mhc_stream_t stream);
+
+/*
+ * mhc_boundary -- the fused boundary on TP-partial slices.
+ *
+ * boundary page, module docstring and Boundaries._reduce; all_reduce page,
+ * BoundaryAllReduce.__call__. For each row r and hidden index h:
+ *   x[r,h]      = bf16( sum_t x_partials[t,r,h] )                (t ascending, fp32)
+ *   s'[r,i,h]   = bf16( sum_j comb[r,i,j] * residual[r,j,h] + post[r,i] * x[r,h] )
+ *   y[r,h]      = sum_j pre[r,j] * s'[r,j,h]
+ *   layer[r,h]  = bf16( y[r,h] * (mean_h y[r,:]^2 + norm_eps)^(-1/2) * norm_weight[h] )
+ * and optionally the MXFP8 form of layer[]: per block of 32 contiguous
+ * elements of a row, e = the smallest integer with max|block| <= 448 * 2^e
+ * (-127 for an all-zero block, clamped to [-127,127]); scale byte = e + 127;
+ * data = E4M3 (OCP, FN variant) of layer * 2^-e, nearest-even.
+ *
+ *   x_partials      [T, R, H] bf16, T = tp in [1, max_tp]
+ *   residual        [R, n, H] bf16 (the hc residual streams)
+ *   post            [R, n] fp32;  comb [R, n, n] fp32 (i = output stream, j = input stream)
+ *   pre             [R, n] fp32, or NULL for residual-only (then norm_weight and
+ *                   layer_input_out must be NULL and no MXFP8 may be asked for)
+ *   norm_weight     [H] bf16;  norm_eps >= 0
+ *   residual_out    [R, n, H] bf16, may equal residual
+ *   layer_input_out [R, H] bf16
+ *   mx_data_out     [R, H] E4M3 bytes and mx_scale_out [R, H/32] E8M0 bytes, both
+ *                   NULL (no MXFP8) or both set (needs pre and H % 32 == 0)
+ */
+int mhc_boundary(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_t* residual,
+                 const float* post, const float* comb, const float* pre,
+                 const uint16_t* norm_weight, float norm_eps, int rows, uint16_t* residual_out,
+                 uint16_t* layer_input_out, uint8_t* mx_data_out, uint8_t* mx_scale_out,
+                 mhc_stream_t stream);
+
+/*
+ * mhc_residual_only -- reduce and mix only: writes residual_out and nothing else.
+ *
+ * boundary page, Boundaries.post_only and Boundaries._reduce (without a pre
+ * the kernel writes only the streams: before an Engram injection and for the
+ * final collapse). Same as mhc_boundary with pre = NULL.
+ */
+int mhc_residual_only(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_t* residual,
+                      const float* post, const float* comb, int rows, uint16_t* residual_out,
+                      mhc_stream_t stream);
+
+/*
+ * mhc_finalize -- the fused boundary on an unfinalized MoE output.
+ *
+ * boundary page, Boundaries._reduce (MoE branch); all_reduce page,
+ * BoundaryAllReduce.finalize. Identical to mhc_boundary except that
+ *   x[r,h] = bf16( shared_output[r,h] + sum_k expert_weights[r,k] *
+ *                  gemm2_permuted[ expanded_idx_to_permuted_idx[r*K + k], h ] )
+ * (k ascending, fp32), with K the handle's top_k.
+ *   gemm2_permuted               [num_permuted, H] bf16, num_permuted >= 1
+ *   expert_weights               [R, K] fp32
+ *   expanded_idx_to_permuted_idx [R*K] int32; an entry outside [0, num_permuted)
+ *                                contributes nothing (it is never dereferenced)
+ *   shared_output                [R, H] bf16 (required)
+ * pre == NULL gives the residual-only form, as for mhc_boundary.
+ */
+int mhc_finalize(mhc_handle h, const uint16_t* gemm2_permuted, int num_permuted,
+                 const float* expert_weights, const int32_t* expanded_idx_to_permuted_idx,
+                 const uint16_t* shared_output, const uint16_t* residual, const float* post,
+                 const float* comb, const float* pre, const uint16_t* norm_weight, float norm_eps,
+                 int rows, uint16_t* residual_out, uint16_t* layer_input_out,
+                 uint8_t* mx_data_out, uint8_t* mx_scale_out, mhc_stream_t stream);
+
+/*
+ * mhc_collapse_mean -- out[r,h] = bf16( (1/n) * sum_i streams[r,i,h] ).
+ *
+ * boundary page, Boundaries.sublayer (the aux output is the mean of the
+ * streams over the stream axis); decode page, SpecializedDecode.run (the
+ * same mean after the final residual-only reduction).
+ *   streams [R, n, H] bf16 -> out [R, H] bf16
+ */
+int mhc_collapse_mean(mhc_handle h, const uint16_t* streams, int rows, uint16_t* out,
+                      mhc_stream_t stream);
+
+/*
+ * mhc_pre_coeffs -- the next sublayer's mHC coefficients from the streams.
+ *
+ * boundary page, Boundaries.sublayer and Boundaries._pre: the coefficient
+ * call takes the streams, fn, scale, base, rms_norm_eps, hc_eps (as the pre
+ * eps and again as the Sinkhorn eps), hc_post_alpha and hc_sinkhorn_iters.
+ * With v = residual[r] flattened stream-major (k = i*H + h), NC = 2n + n*n:
+ *   inv     = (mean_k v[k]^2 + rms_eps)^(-1/2)
+ *   l[c]    = inv * sum_k v[k] * fn[k, c]                     (c < NC)
+ *   l'[c]   = l[c] * scale[g(c)] + base[c],  g = 0 for c < n, 1 for c < 2n, else 2
+ *   pre[i]  = sigmoid(l'[i]) + pre_eps
+ *   post[i] = post_alpha * sigmoid(l'[n + i])
+ *   comb    = A after sinkhorn_iters rounds of {A <- A / (rowsum + sinkhorn_eps);
+ *             A <- A / (colsum + sinkhorn_eps)}, starting from
+ *             A[i,j] = exp(l'[2n+n*i+j] - max_j l'[2n+n*i+j])
+ *   residual [R, n, H] bf16;  fn [n*H, NC] bf16 row-major
+ *   scale [3] fp32;  base [NC] fp32;  sinkhorn_iters in [0, 1000]
+ *   pre_out [R, n], post_out [R, n], comb_out [R, n, n], fp32
+ */
+int mhc_pre_coeffs(mhc_handle h, const uint16_t* residual, const uint16_t* fn,
+                   const float* scale, const float* base, float rms_eps, float pre_eps,
+                   float sinkhorn_eps, float post_alpha, int sinkhorn_iters, int rows,
+                   float* pre_out, float* post_out, float* comb_out, mhc_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_AMD_H */

@@ -1,0 +1,338 @@
+// C ABI of libmhc_amd.so: handle lifetime, argument validation and launches.
+// The contract of every entry point is stated in include/mhc.h.
+#include "mhc.h"
+
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kHcMult = 4;
+constexpr int kMaxRows = 65536;
+constexpr int kMaxTp = 64;
+constexpr int kMaxTopK = 64;
+constexpr int kMaxSinkhornIters = 1000;
+constexpr int kMinBlock = 64;       // smallest boundary workgroup: sizes the partial-sum scratch
+constexpr int kDefaultBlock = 64;
+
+}  // namespace
+
+struct mhc_ctx {
+  int hidden, hc_mult, max_rows, max_tp, top_k, device;
+  int part_stride;     // partial sums per row (chunks at the smallest block)
+  int block;           // boundary workgroup size in use
+  size_t pre_floats;   // coefficient-path scratch
+  void* scratch;       // one allocation: ywork | part | pre_part | counters
+  float* ywork;
+  float* part;
+  float* pre_part;
+  unsigned* counters;
+};
+
+namespace {
+
+inline bool aligned(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_device(const mhc_ctx* h) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return MHC_ERR_HIP;
+  return cur == h->device ? MHC_OK : MHC_ERR_DEVICE;
+}
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? MHC_OK : MHC_ERR_HIP; }
+
+// Common validation of the mHC half of a boundary call (streams, mixes, pre,
+// norm, outputs). Returns MHC_OK or the first failing status.
+int check_mix(const mhc_ctx* h, const uint16_t* residual, const float* post, const float* comb,
+              const float* pre, const uint16_t* norm_weight, float norm_eps, uint16_t* residual_out,
+              uint16_t* layer_input_out, uint8_t* mx_data_out, uint8_t* mx_scale_out) {
+  if (!residual || !post || !comb || !residual_out) return MHC_ERR_INVALID_ARG;
+  const bool has_pre = pre != nullptr;
+  if (has_pre != (norm_weight != nullptr) || has_pre != (layer_input_out != nullptr))
+    return MHC_ERR_INVALID_ARG;
+  if ((mx_data_out == nullptr) != (mx_scale_out == nullptr)) return MHC_ERR_INVALID_ARG;
+  if (mx_data_out && !has_pre) return MHC_ERR_INVALID_ARG;
+  if (mx_data_out && (h->hidden % 32) != 0) return MHC_ERR_UNSUPPORTED;
+  if (has_pre && !(norm_eps >= 0.0f)) return MHC_ERR_SHAPE;  // also rejects NaN
+  if (!aligned(residual, 16) || !aligned(residual_out, 16) || !aligned(post, 4) ||
+      !aligned(comb, 4))
+    return MHC_ERR_ALIGN;
+  if (has_pre && (!aligned(pre, 4) || !aligned(norm_weight, 16) || !aligned(layer_input_out, 16)))
+    return MHC_ERR_ALIGN;
+  if (mx_data_out && !aligned(mx_data_out, 8)) return MHC_ERR_ALIGN;
+  return MHC_OK;
+}
+
+void fill_mix(const mhc_ctx* h, mhc::BoundaryLaunch& L, const uint16_t* residual, const float* post,
+              const float* comb, const float* pre, const uint16_t* norm_weight, float norm_eps,
+              int rows, uint16_t* residual_out, uint16_t* layer_input_out, uint8_t* mx_data_out,
+              uint8_t* mx_scale_out) {
+  L.residual = residual;
+  L.residual_out = residual_out;
+  L.post = post;
+  L.comb = comb;
+  L.pre = pre;
+  L.norm_weight = norm_weight;
+  L.eps = norm_eps;
+  L.rows = rows;
+  L.hidden = h->hidden;
+  L.layer_input_out = layer_input_out;
+  L.mx_data_out = mx_data_out;
+  L.mx_scale_out = mx_scale_out;
+  L.ywork = h->ywork;
+  L.part = h->part;
+  L.counters = h->counters;
+  L.part_stride = h->part_stride;
+  L.block = h->block;
+}
+
+}  // namespace
+
+namespace mhc {
+
+__global__ void fill_u32_kernel(unsigned* p, size_t n, unsigned value) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = value;
+}
+
+hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned value, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int grid = (int)((n + 255) / 256);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid), dim3(256), 0, stream, p, n, value);
+  return hipGetLastError();
+}
+
+}  // namespace mhc
+
+extern "C" {
+
+const char* mhc_status_string(int status) {
+  switch (status) {
+    case MHC_OK: return "MHC_OK";
+    case MHC_ERR_INVALID_ARG: return "MHC_ERR_INVALID_ARG: null or inconsistent argument";
+    case MHC_ERR_SHAPE: return "MHC_ERR_SHAPE: invalid size";
+    case MHC_ERR_ALIGN: return "MHC_ERR_ALIGN: misaligned pointer";
+    case MHC_ERR_LIMIT: return "MHC_ERR_LIMIT: rows or tp above the handle's limit";
+    case MHC_ERR_UNSUPPORTED: return "MHC_ERR_UNSUPPORTED: unsupported configuration";
+    case MHC_ERR_HIP: return "MHC_ERR_HIP: HIP runtime call failed";
+    case MHC_ERR_DEVICE: return "MHC_ERR_DEVICE: current device is not the handle's device";
+    default: return "MHC: unknown status";
+  }
+}
+
+int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int device,
+               mhc_handle* out) {
+  if (!out) return MHC_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (hidden <= 0 || hidden % 8 != 0 || hidden > (1 << 24)) return MHC_ERR_SHAPE;
+  if (max_rows < 1 || max_rows > kMaxRows || max_tp < 1 || max_tp > kMaxTp || top_k < 1 ||
+      top_k > kMaxTopK || device < 0)
+    return MHC_ERR_SHAPE;
+  if (hc_mult != kHcMult) return MHC_ERR_UNSUPPORTED;
+
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || device >= ndev) return MHC_ERR_HIP;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return MHC_ERR_HIP;
+  if (hipSetDevice(device) != hipSuccess) return MHC_ERR_HIP;
+
+  mhc_ctx* h = new (std::nothrow) mhc_ctx();
+  if (!h) {
+    (void)hipSetDevice(prev);
+    return MHC_ERR_HIP;
+  }
+  h->hidden = hidden;
+  h->hc_mult = hc_mult;
+  h->max_rows = max_rows;
+  h->max_tp = max_tp;
+  h->top_k = top_k;
+  h->device = device;
+  h->block = kDefaultBlock;
+  h->part_stride = mhc::boundary_chunks(hidden, kMinBlock);
+  size_t pre_floats = 0;
+  for (int r = 1; r <= max_rows; r += 16) {  // the split plan changes only every 16 rows
+    const size_t f = mhc::pre_scratch_floats_for(r, hidden);
+    if (f > pre_floats) pre_floats = f;
+  }
+  h->pre_floats = pre_floats;
+
+  const size_t y_bytes = round_up((size_t)max_rows * hidden * sizeof(float), 256);
+  const size_t part_bytes = round_up((size_t)max_rows * h->part_stride * sizeof(float), 256);
+  const size_t pre_bytes = round_up(pre_floats * sizeof(float), 256);
+  const size_t cnt_bytes = round_up((size_t)max_rows * sizeof(unsigned), 256);
+  const size_t total = y_bytes + part_bytes + pre_bytes + cnt_bytes;
+  void* base = nullptr;
+  if (hipMalloc(&base, total) != hipSuccess) {
+    delete h;
+    (void)hipSetDevice(prev);
+    return MHC_ERR_HIP;
+  }
+  char* b = static_cast<char*>(base);
+  h->scratch = base;
+  h->ywork = reinterpret_cast<float*>(b);
+  h->part = reinterpret_cast<float*>(b + y_bytes);
+  h->pre_part = reinterpret_cast<float*>(b + y_bytes + part_bytes);
+  h->counters = reinterpret_cast<unsigned*>(b + y_bytes + part_bytes + pre_bytes);
+  hipError_t e = mhc::launch_fill_u32(reinterpret_cast<unsigned*>(base), total / 4, 0u, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  (void)hipSetDevice(prev);
+  if (e != hipSuccess) {
+    (void)hipFree(base);
+    delete h;
+    return MHC_ERR_HIP;
+  }
+  *out = h;
+  return MHC_OK;
+}
+
+int mhc_set_option(mhc_handle h, int option, int value) {
+  if (!h) return MHC_ERR_INVALID_ARG;
+  switch (option) {
+    case MHC_OPT_BOUNDARY_BLOCK:
+      if (value != 64 && value != 128 && value != 256) return MHC_ERR_SHAPE;
+      h->block = value;
+      return MHC_OK;
+    default:
+      return MHC_ERR_INVALID_ARG;
+  }
+}
+
+int mhc_destroy(mhc_handle h) {
+  if (!h) return MHC_OK;
+  int prev = 0;
+  int st = MHC_OK;
+  if (hipGetDevice(&prev) != hipSuccess) st = MHC_ERR_HIP;
+  if (hipSetDevice(h->device) != hipSuccess) st = MHC_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) st = MHC_ERR_HIP;
+  if (hipFree(h->scratch) != hipSuccess) st = MHC_ERR_HIP;
+  (void)hipSetDevice(prev);
+  delete h;
+  return st;
+}
+
+int mhc_reset(mhc_handle h, mhc_stream_t stream) {
+  if (!h) return MHC_ERR_INVALID_ARG;
+  int st = check_device(h);
+  if (st != MHC_OK) return st;
+  return launch_status(mhc::launch_fill_u32(h->counters, (size_t)h->max_rows, 0u,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int mhc_boundary(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_t* residual,
+                 const float* post, const float* comb, const float* pre,
+                 const uint16_t* norm_weight, float norm_eps, int rows, uint16_t* residual_out,
+                 uint16_t* layer_input_out, uint8_t* mx_data_out, uint8_t* mx_scale_out,
+                 mhc_stream_t stream) {
+  if (!h) return MHC_ERR_INVALID_ARG;
+  if (rows < 0 || tp < 1) return MHC_ERR_SHAPE;
+  if (rows > h->max_rows || tp > h->max_tp) return MHC_ERR_LIMIT;
+  if (rows == 0) return MHC_OK;
+  if (!x_partials) return MHC_ERR_INVALID_ARG;
+  int st = check_mix(h, residual, post, comb, pre, norm_weight, norm_eps, residual_out,
+                     layer_input_out, mx_data_out, mx_scale_out);
+  if (st != MHC_OK) return st;
+  if (!aligned(x_partials, 16)) return MHC_ERR_ALIGN;
+  st = check_device(h);
+  if (st != MHC_OK) return st;
+  mhc::BoundaryLaunch L = {};
+  L.x_partials = x_partials;
+  L.tp = tp;
+  fill_mix(h, L, residual, post, comb, pre, norm_weight, norm_eps, rows, residual_out,
+           layer_input_out, mx_data_out, mx_scale_out);
+  return launch_status(mhc::launch_boundary(L, static_cast<hipStream_t>(stream)));
+}
+
+int mhc_residual_only(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_t* residual,
+                      const float* post, const float* comb, int rows, uint16_t* residual_out,
+                      mhc_stream_t stream) {
+  return mhc_boundary(h, x_partials, tp, residual, post, comb, nullptr, nullptr, 0.0f, rows,
+                      residual_out, nullptr, nullptr, nullptr, stream);
+}
+
+int mhc_finalize(mhc_handle h, const uint16_t* gemm2_permuted, int num_permuted,
+                 const float* expert_weights, const int32_t* expanded_idx_to_permuted_idx,
+                 const uint16_t* shared_output, const uint16_t* residual, const float* post,
+                 const float* comb, const float* pre, const uint16_t* norm_weight, float norm_eps,
+                 int rows, uint16_t* residual_out, uint16_t* layer_input_out,
+                 uint8_t* mx_data_out, uint8_t* mx_scale_out, mhc_stream_t stream) {
+  if (!h) return MHC_ERR_INVALID_ARG;
+  if (rows < 0 || num_permuted < 1) return MHC_ERR_SHAPE;
+  if (rows > h->max_rows) return MHC_ERR_LIMIT;
+  if (rows == 0) return MHC_OK;
+  if (!gemm2_permuted || !expert_weights || !expanded_idx_to_permuted_idx || !shared_output)
+    return MHC_ERR_INVALID_ARG;
+  int st = check_mix(h, residual, post, comb, pre, norm_weight, norm_eps, residual_out,
+                     layer_input_out, mx_data_out, mx_scale_out);
+  if (st != MHC_OK) return st;
+  if (!aligned(gemm2_permuted, 16) || !aligned(shared_output, 16) || !aligned(expert_weights, 4) ||
+      !aligned(expanded_idx_to_permuted_idx, 4))
+    return MHC_ERR_ALIGN;
+  st = check_device(h);
+  if (st != MHC_OK) return st;
+  mhc::BoundaryLaunch L = {};
+  L.gemm2_permuted = gemm2_permuted;
+  L.num_permuted = num_permuted;
+  L.expert_weights = expert_weights;
+  L.idx = expanded_idx_to_permuted_idx;
+  L.shared_output = shared_output;
+  L.top_k = h->top_k;
+  fill_mix(h, L, residual, post, comb, pre, norm_weight, norm_eps, rows, residual_out,
+           layer_input_out, mx_data_out, mx_scale_out);
+  return launch_status(mhc::launch_boundary(L, static_cast<hipStream_t>(stream)));
+}
+
+int mhc_collapse_mean(mhc_handle h, const uint16_t* streams, int rows, uint16_t* out,
+                      mhc_stream_t stream) {
+  if (!h) return MHC_ERR_INVALID_ARG;
+  if (rows < 0) return MHC_ERR_SHAPE;
+  if (rows > h->max_rows) return MHC_ERR_LIMIT;
+  if (rows == 0) return MHC_OK;
+  if (!streams || !out) return MHC_ERR_INVALID_ARG;
+  if (!aligned(streams, 16) || !aligned(out, 16)) return MHC_ERR_ALIGN;
+  int st = check_device(h);
+  if (st != MHC_OK) return st;
+  return launch_status(
+      mhc::launch_collapse_mean(streams, rows, h->hidden, out, static_cast<hipStream_t>(stream)));
+}
+
+int mhc_pre_coeffs(mhc_handle h, const uint16_t* residual, const uint16_t* fn,
+                   const float* scale, const float* base, float rms_eps, float pre_eps,
+                   float sinkhorn_eps, float post_alpha, int sinkhorn_iters, int rows,
+                   float* pre_out, float* post_out, float* comb_out, mhc_stream_t stream) {
+  if (!h) return MHC_ERR_INVALID_ARG;
+  if (rows < 0 || sinkhorn_iters < 0 || sinkhorn_iters > kMaxSinkhornIters) return MHC_ERR_SHAPE;
+  if (!(rms_eps >= 0.0f) || !(sinkhorn_eps >= 0.0f)) return MHC_ERR_SHAPE;
+  if (rows > h->max_rows) return MHC_ERR_LIMIT;
+  if (rows == 0) return MHC_OK;
+  if (!residual || !fn || !scale || !base || !pre_out || !post_out || !comb_out)
+    return MHC_ERR_INVALID_ARG;
+  if (!aligned(residual, 16) || !aligned(fn, 2) || !aligned(scale, 4) || !aligned(base, 4) ||
+      !aligned(pre_out, 4) || !aligned(post_out, 4) || !aligned(comb_out, 4))
+    return MHC_ERR_ALIGN;
+  int st = check_device(h);
+  if (st != MHC_OK) return st;
+  mhc::PreLaunch L;
+  L.residual = residual;
+  L.fn = fn;
+  L.scale = scale;
+  L.base = base;
+  L.rms_eps = rms_eps;
+  L.pre_eps = pre_eps;
+  L.sinkhorn_eps = sinkhorn_eps;
+  L.post_alpha = post_alpha;
+  L.sinkhorn_iters = sinkhorn_iters;
+  L.rows = rows;
+  L.hidden = h->hidden;
+  L.pre_out = pre_out;
+  L.post_out = post_out;
+  L.comb_out = comb_out;
+  L.part = h->pre_part;
+  return launch_status(mhc::launch_pre_coeffs(L, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal interface between the C ABI (api.hip) and the kernel launchers.
+// Arguments are validated by the caller; the launchers only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mhc {
+
+struct BoundaryLaunch {
+  // exactly one sublayer-output source: x_partials (tp slices) or gemm2_permuted (finalize)
+  const uint16_t* x_partials;
+  int tp;
+  const uint16_t* gemm2_permuted;
+  int num_permuted;
+  const float* expert_weights;
+  const int32_t* idx;
+  const uint16_t* shared_output;
+  int top_k;
+  const uint16_t* residual;
+  uint16_t* residual_out;
+  const float* post;
+  const float* comb;
+  const float* pre;             // NULL: residual-only
+  const uint16_t* norm_weight;
+  float eps;
+  int rows, hidden;
+  uint16_t* layer_input_out;
+  uint8_t* mx_data_out;         // NULL: no MXFP8
+  uint8_t* mx_scale_out;
+  float* ywork;                 // [max_rows][hidden]
+  float* part;                  // [max_rows][part_stride]
+  unsigned* counters;           // [max_rows], zero between calls
+  int part_stride;
+  int block;                    // 64, 128 or 256 threads per workgroup
+};
+
+struct PreLaunch {
+  const uint16_t* residual;
+  const uint16_t* fn;
+  const float* scale;
+  const float* base;
+  float rms_eps, pre_eps, sinkhorn_eps, post_alpha;
+  int sinkhorn_iters, rows, hidden;
+  float* pre_out;
+  float* post_out;
+  float* comb_out;
+  float* part;                  // pre_scratch_floats(max_rows, hidden) floats
+};
+
+int boundary_chunks(int hidden, int block);
+hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream);
+hipError_t launch_collapse_mean(const uint16_t* streams, int rows, int hidden, uint16_t* out,
+                                hipStream_t stream);
+
+void pre_plan(int rows, int hidden, int* ks_count, int* steps_per_wg, int* rows_pad);
+size_t pre_scratch_floats_for(int rows, int hidden);
+hipError_t launch_pre_coeffs(const PreLaunch& L, hipStream_t stream);
+
+hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned value, hipStream_t stream);
+
+}  // namespace mhc

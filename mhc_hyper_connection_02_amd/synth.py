@@ -181,3 +181,26 @@ def chain_sublayer(layer, ffn, rows=CHAIN_ROWS, hidden=CHAIN_HIDDEN, tp=CHAIN_TP
 def chain_params():
     return {"rms_eps": float(np.float32(1e-6)), "hc_eps": float(np.float32(1e-6)),
             "post_alpha": 2.0, "sinkhorn_iters": 20, "norm_eps": float(np.float32(1e-6))}
+
+
+# ---------------------------------------------------------------------------
+# Moving the arrays into torch tensors (marshalling only)
+# ---------------------------------------------------------------------------
+
+def to_torch(a, device):
+    """numpy -> torch on `device`: uint16 arrays become bfloat16 (same bits), float32 and
+    int32 keep their dtype."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    if a.dtype in (np.float32, np.int32, np.uint8):
+        return torch.from_numpy(a).to(device)
+    raise TypeError(f"unsupported array dtype {a.dtype}")
+
+
+def to_numpy(t):
+    """torch -> numpy: bfloat16 comes back as uint16 bit patterns."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

@@ -1,0 +1,119 @@
+"""Shared helpers of the GPU parity tests: run a case through the C ABI and compare it with
+the oracle on the same seeded inputs."""
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import codecs
+from mhc_hyper_connection_02_amd import binding, synth
+
+DEV = torch.device("cuda", 0)
+
+# bf16 outputs: |gpu - oracle| <= 2e-2 + 1e-2 |oracle|; fp32 coefficients: 1e-5 + 1e-5 |oracle|
+BF16_ATOL, BF16_RTOL = 2e-2, 1e-2
+F32_ATOL, F32_RTOL = 1e-5, 1e-5
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def T(a):
+    return synth.to_torch(a, DEV)
+
+
+def N(t):
+    return synth.to_numpy(t)
+
+
+def assert_bf16_close(gpu_bits, ora_bits, what):
+    g = codecs.bf16_bits_to_f64(gpu_bits)
+    o = codecs.bf16_bits_to_f64(ora_bits)
+    assert g.shape == o.shape, (what, g.shape, o.shape)
+    err = np.abs(g - o)
+    bad = err > BF16_ATOL + BF16_RTOL * np.abs(o)
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - BF16_RTOL * np.abs(o)), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements out of tolerance; "
+                             f"worst at {i}: gpu {g[i]} oracle {o[i]}")
+    return float(np.mean(gpu_bits == ora_bits))  # fraction bit-identical
+
+
+def assert_f32_close(gpu, ora, what):
+    g = np.asarray(gpu, np.float64)
+    o = np.asarray(ora, np.float64)
+    assert g.shape == o.shape, (what, g.shape, o.shape)
+    err = np.abs(g - o)
+    bad = err > F32_ATOL + F32_RTOL * np.abs(o)
+    if bad.any():
+        i = np.unravel_index(np.argmax(err), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} out of tolerance; worst at "
+                             f"{i}: gpu {g[i]} oracle {o[i]} (|d| = {err[i]:.3e})")
+    return float(err.max())
+
+
+def handle_for(hidden, rows, tp=8, top_k=8, block=None):
+    h = binding.Handle(hidden, 4, max_rows=max(rows, 1), max_tp=max(tp, 1), top_k=top_k)
+    if block is not None:
+        h.set_option(binding.MHC_OPT_BOUNDARY_BLOCK, block)
+    return h
+
+
+def gpu_boundary(h, d, mxfp8=None, residual_only=False):
+    mx = d["mxfp8"] if mxfp8 is None else mxfp8
+    if residual_only:
+        out = binding.residual_only(h, T(d["x_partials"]), T(d["residual"]), T(d["post"]),
+                                    T(d["comb"]))
+        torch.cuda.synchronize()
+        return {"residual": N(out)}
+    out = binding.boundary(h, T(d["x_partials"]), T(d["residual"]), T(d["post"]), T(d["comb"]),
+                           T(d["pre"]), T(d["norm_weight"]), d["eps"], mxfp8=mx)
+    torch.cuda.synchronize()
+    return {k: N(v) for k, v in out.items()}
+
+
+def oracle_boundary(d, mxfp8=None, residual_only=False):
+    mx = d["mxfp8"] if mxfp8 is None else mxfp8
+    if residual_only:
+        return {"residual": oracle.residual_only(d["x_partials"], d["residual"], d["post"], d["comb"])}
+    return oracle.boundary(d["x_partials"], d["residual"], d["post"], d["comb"], d["pre"],
+                           d["norm_weight"], d["eps"], mxfp8=mx)
+
+
+def gpu_finalize(h, d, pre=True, mxfp8=None, num_permuted=None):
+    mx = d["mxfp8"] if mxfp8 is None else mxfp8
+    out = binding.finalize(h, T(d["gemm2_permuted"]), T(d["expert_weights"]),
+                           T(d["expanded_idx_to_permuted_idx"]), T(d["shared_output"]),
+                           T(d["residual"]), T(d["post"]), T(d["comb"]),
+                           T(d["pre"]) if pre else None, T(d["norm_weight"]) if pre else None,
+                           d["eps"], mxfp8=mx and pre)
+    torch.cuda.synchronize()
+    return {k: N(v) for k, v in out.items()}
+
+
+def oracle_finalize(d, pre=True, mxfp8=None):
+    mx = d["mxfp8"] if mxfp8 is None else mxfp8
+    return oracle.finalize(d["gemm2_permuted"], d["expert_weights"],
+                           d["expanded_idx_to_permuted_idx"], d["shared_output"], d["residual"],
+                           d["post"], d["comb"], d["pre"] if pre else None,
+                           d["norm_weight"] if pre else None, d["eps"], mxfp8=mx and pre)
+
+
+def compare_boundary_outputs(g, o, what):
+    """Streams and layer input within the bf16 tolerance; MXFP8 bit-exact against the oracle's
+    quantizer applied to the GPU's own layer input, and the end-to-end mismatch count returned."""
+    stats = {"residual_exact": assert_bf16_close(g["residual"], o["residual"], what + " streams")}
+    if "layer_input" in o:
+        stats["layer_exact"] = assert_bf16_close(g["layer_input"], o["layer_input"],
+                                                 what + " layer input")
+    if "mx_data" in o:
+        codes, scales = codecs.mxfp8_quantize(g["layer_input"])
+        assert np.array_equal(g["mx_scale"], scales), what + ": E8M0 scales differ from the quantizer"
+        assert np.array_equal(g["mx_data"], codes), what + ": E4M3 codes differ from the quantizer"
+        stats["scale_mismatch_vs_oracle"] = int(np.sum(g["mx_scale"] != o["mx_scale"]))
+        stats["code_mismatch_vs_oracle"] = int(np.sum(g["mx_data"] != o["mx_data"]))
+    return stats

@@ -1,0 +1,316 @@
+"""GPU parity: the HIP library through its C ABI against the oracle, on the same seeded inputs.
+
+Run on an MI355X: ``python -u -m pytest -m gpu tests -x -v --timeout 120 --timeout-method thread``.
+Each test prints its case before the first GPU call.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import codecs
+from mhc_hyper_connection_02_amd import binding, synth
+
+from gpu_helpers import (T, N, say, assert_bf16_close, assert_f32_close, handle_for,
+                         gpu_boundary, oracle_boundary, gpu_finalize, oracle_finalize,
+                         compare_boundary_outputs)
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------
+# The workloads at their full sizes
+# ---------------------------------------------------------------------------
+
+def test_config0_tiny_boundary():
+    say("case: config 0 boundary rows=4 hidden=1024 tp=2")
+    d = synth.config(0)
+    h = handle_for(1024, 4, tp=2)
+    g = gpu_boundary(h, d)
+    o = oracle_boundary(d)
+    st = compare_boundary_outputs(g, o, "config 0")
+    say(f"  {st}")
+    assert set(g) == {"residual", "layer_input"}
+
+
+def test_config1_decode_boundary_mxfp8_and_determinism():
+    say("case: config 1 boundary rows=32 hidden=7168 tp=8 mxfp8")
+    d = synth.config(1)
+    h = handle_for(7168, 32, tp=8)
+    g = gpu_boundary(h, d)
+    o = oracle_boundary(d)
+    st = compare_boundary_outputs(g, o, "config 1")
+    say(f"  {st}")
+    assert st["scale_mismatch_vs_oracle"] <= 2
+    g2 = gpu_boundary(h, d)
+    for k in g:
+        assert np.array_equal(g[k], g2[k]), f"second run differs in {k}"
+
+
+def test_config1_residual_only_equals_full_streams():
+    say("case: config 1 residual-only rows=32 hidden=7168 tp=8")
+    d = synth.config(1)
+    h = handle_for(7168, 32, tp=8)
+    ro = gpu_boundary(h, d, residual_only=True)
+    full = gpu_boundary(h, d)
+    assert np.array_equal(ro["residual"], full["residual"])
+    o = oracle_boundary(d, residual_only=True)
+    assert_bf16_close(ro["residual"], o["residual"], "config 1 residual-only")
+
+
+def test_config2_moe_finalize_mxfp8():
+    say("case: config 2 finalize rows=64 top_k=8 hidden=7168 mxfp8")
+    d = synth.config(2)
+    h = handle_for(7168, 64, tp=1, top_k=8)
+    g = gpu_finalize(h, d)
+    o = oracle_finalize(d)
+    st = compare_boundary_outputs(g, o, "config 2")
+    say(f"  {st}")
+    assert st["scale_mismatch_vs_oracle"] <= 2
+    ro = gpu_finalize(h, d, pre=False)
+    assert np.array_equal(ro["residual"], g["residual"])
+
+
+def test_config3_pre_coeffs():
+    say("case: config 3 pre_coeffs rows=64 hidden=7168")
+    d = synth.config(3)
+    h = handle_for(7168, 64)
+    pre, post, comb = binding.pre_coeffs(h, T(d["residual"]), T(d["fn"]), T(d["scale"]),
+                                         T(d["base"]), d["rms_eps"], d["pre_eps"],
+                                         d["sinkhorn_eps"], d["post_alpha"], d["sinkhorn_iters"])
+    torch.cuda.synchronize()
+    op, oq, oc = oracle.pre_coeffs(d["residual"], d["fn"], d["scale"], d["base"], d["rms_eps"],
+                                   d["pre_eps"], d["sinkhorn_eps"], d["post_alpha"],
+                                   d["sinkhorn_iters"])
+    e1 = assert_f32_close(N(pre), op, "pre")
+    e2 = assert_f32_close(N(post), oq, "post")
+    e3 = assert_f32_close(N(comb), oc, "comb")
+    say(f"  max |err| pre {e1:.2e} post {e2:.2e} comb {e3:.2e}")
+    # reported, not asserted: how far rows are from summing to 1 after 20 iterations
+    say(f"  comb max |rowsum-1| {np.abs(N(comb).sum(axis=2) - 1).max():.2e}")
+
+
+# ---------------------------------------------------------------------------
+# Tiles, ragged tails and block sizes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,hidden,tp,block", [
+    (1, 512, 1, 64), (5, 1056, 3, 64), (9, 2080, 8, 128), (17, 7168, 8, 256),
+    (13, 3072, 5, 128), (8, 33 * 32, 2, 256), (3, 8 * 40, 4, 64),
+])
+def test_boundary_ragged(rows, hidden, tp, block):
+    mx = hidden % 32 == 0
+    say(f"case: boundary rows={rows} hidden={hidden} tp={tp} block={block} mxfp8={mx}")
+    d = synth.boundary_inputs(100 + rows, rows=rows, hidden=hidden, tp=tp, mxfp8=mx)
+    h = handle_for(hidden, rows, tp=tp, block=block)
+    compare_boundary_outputs(gpu_boundary(h, d), oracle_boundary(d), f"ragged {rows}x{hidden}")
+
+
+@pytest.mark.parametrize("rows,hidden,top_k,block", [
+    (1, 512, 1, 64), (7, 1056, 3, 128), (20, 7168, 8, 64), (4, 2048, 12, 256),
+])
+def test_finalize_ragged(rows, hidden, top_k, block):
+    say(f"case: finalize rows={rows} hidden={hidden} top_k={top_k} block={block}")
+    d = synth.finalize_inputs(200 + rows, rows=rows, hidden=hidden, top_k=top_k,
+                              mxfp8=hidden % 32 == 0)
+    h = handle_for(hidden, rows, tp=1, top_k=top_k, block=block)
+    compare_boundary_outputs(gpu_finalize(h, d), oracle_finalize(d), f"finalize {rows}x{hidden}")
+
+
+@pytest.mark.parametrize("rows,hidden,iters", [(1, 256, 20), (17, 1024, 20), (128, 7168, 20),
+                                               (5, 7168, 0), (3, 96, 1)])
+def test_pre_coeffs_ragged(rows, hidden, iters):
+    say(f"case: pre_coeffs rows={rows} hidden={hidden} iters={iters}")
+    d = synth.pre_inputs(300 + rows, rows=rows, hidden=hidden)
+    h = handle_for(hidden, rows)
+    got = binding.pre_coeffs(h, T(d["residual"]), T(d["fn"]), T(d["scale"]), T(d["base"]),
+                             d["rms_eps"], d["pre_eps"], d["sinkhorn_eps"], d["post_alpha"], iters)
+    torch.cuda.synchronize()
+    want = oracle.pre_coeffs(d["residual"], d["fn"], d["scale"], d["base"], d["rms_eps"],
+                             d["pre_eps"], d["sinkhorn_eps"], d["post_alpha"], iters)
+    for name, a, b in zip(("pre", "post", "comb"), got, want):
+        assert_f32_close(N(a), b, f"{name} rows={rows} hidden={hidden}")
+
+
+def test_block_sizes_agree():
+    say("case: config 1 at block 64 / 128 / 256")
+    d = synth.config(1)
+    outs = []
+    for block in (64, 128, 256):
+        h = handle_for(7168, 32, tp=8, block=block)
+        outs.append(gpu_boundary(h, d))
+    for o in outs[1:]:
+        assert np.array_equal(o["residual"], outs[0]["residual"])  # per-element arithmetic
+        assert_bf16_close(o["layer_input"], outs[0]["layer_input"], "block layer input")
+
+
+# ---------------------------------------------------------------------------
+# Special cases with exact answers
+# ---------------------------------------------------------------------------
+
+def test_finalize_one_hot_gather_bit_exact():
+    R, K, H = 16, 8, 7168
+    say(f"case: finalize one-hot gather rows={R} top_k={K} hidden={H}")
+    d = synth.finalize_inputs(7, rows=R, hidden=H, top_k=K)
+    rng = np.random.default_rng(1)
+    pick = rng.integers(0, K, size=R)
+    w = np.zeros((R, K), np.float32)
+    w[np.arange(R), pick] = 1.0
+    d["expert_weights"] = w
+    d["shared_output"] = np.zeros((R, H), np.uint16)
+    d["comb"] = np.zeros((R, 4, 4), np.float32)
+    d["post"] = np.ones((R, 4), np.float32)
+    h = handle_for(H, R, tp=1, top_k=K)
+    g = gpu_finalize(h, d, mxfp8=False)
+    idx = d["expanded_idx_to_permuted_idx"]
+    for r in range(R):
+        want = d["gemm2_permuted"][idx[r * K + pick[r]]]
+        for i in range(4):
+            assert np.array_equal(g["residual"][r, i], want), (r, i)
+
+
+def test_finalize_out_of_range_indices_are_skipped():
+    R, K, H = 6, 4, 1024
+    say(f"case: finalize with out-of-range indices rows={R} top_k={K}")
+    d = synth.finalize_inputs(8, rows=R, hidden=H, top_k=K)
+    idx = d["expanded_idx_to_permuted_idx"].copy()
+    idx[[1, 6, 11]] = [-1, R * K, 1 << 30]
+    d["expanded_idx_to_permuted_idx"] = idx
+    h = handle_for(H, R, tp=1, top_k=K)
+    compare_boundary_outputs(gpu_finalize(h, d), oracle_finalize(d), "skip indices")
+
+
+def test_identity_premix_selects_stream_zero():
+    R, H = 8, 2048
+    say("case: comb = I, post = 0, pre = e0")
+    d = synth.boundary_inputs(9, rows=R, hidden=H, tp=2, mxfp8=True)
+    d["comb"] = np.broadcast_to(np.eye(4, dtype=np.float32), (R, 4, 4)).copy()
+    d["post"] = np.zeros((R, 4), np.float32)
+    pre = np.zeros((R, 4), np.float32)
+    pre[:, 0] = 1.0
+    d["pre"] = pre
+    h = handle_for(H, R, tp=2)
+    g = gpu_boundary(h, d)
+    assert np.array_equal(g["residual"], d["residual"])
+    want = oracle.rms_norm(codecs.bf16_bits_to_f64(d["residual"][:, 0]), d["norm_weight"], d["eps"])
+    assert_bf16_close(g["layer_input"], want, "RMSNorm(stream 0)")
+
+
+def test_in_place_streams_and_zero_layer_input():
+    R, H = 4, 1024
+    say("case: residual_out aliases residual; zero streams give a zero MXFP8 block")
+    d = synth.boundary_inputs(10, rows=R, hidden=H, tp=2, mxfp8=True)
+    d["residual"][1] = 0
+    d["x_partials"][:, 1] = 0
+    o = oracle_boundary(d)
+    h = handle_for(H, R, tp=2)
+    res = T(d["residual"])
+    out = binding.boundary(h, T(d["x_partials"]), res, T(d["post"]), T(d["comb"]), T(d["pre"]),
+                           T(d["norm_weight"]), d["eps"], mxfp8=True, residual_out=res)
+    torch.cuda.synchronize()
+    assert out["residual"].data_ptr() == res.data_ptr()
+    g = {k: N(v) for k, v in out.items()}
+    compare_boundary_outputs(g, o, "in place")
+    assert np.all(g["mx_scale"][1] == 0) and np.all(g["mx_data"][1] == 0)
+    assert np.all(g["layer_input"][1] == 0)
+
+
+def test_zero_rows_is_a_noop():
+    say("case: rows = 0")
+    h = handle_for(1024, 4)
+    lib = binding.load_library()
+    assert lib.mhc_boundary(h.ptr, None, 1, None, None, None, None, None, 0.0, 0, None, None,
+                            None, None, None) == 0
+    assert lib.mhc_finalize(h.ptr, None, 1, None, None, None, None, None, None, None, None, 0.0, 0,
+                            None, None, None, None, None) == 0
+    assert lib.mhc_pre_coeffs(h.ptr, None, None, None, None, 0.0, 0.0, 0.0, 2.0, 20, 0, None,
+                              None, None, None) == 0
+
+
+def test_max_rows_and_tp_limits():
+    say("case: rows == max_rows, tp == max_tp; and one above each (rejected, nothing launched)")
+    R, H, TP = 24, 1024, 3
+    d = synth.boundary_inputs(11, rows=R, hidden=H, tp=TP)
+    h = handle_for(H, R, tp=TP)
+    compare_boundary_outputs(gpu_boundary(h, d), oracle_boundary(d), "max rows")
+    small = handle_for(H, R - 1, tp=TP)
+    with pytest.raises(binding.MhcValueError):
+        gpu_boundary(small, d)
+    d2 = synth.boundary_inputs(12, rows=4, hidden=H, tp=TP + 1)
+    with pytest.raises(binding.MhcValueError):
+        gpu_boundary(handle_for(H, 4, tp=TP), d2)
+
+
+def test_validation_on_a_device_handle():
+    say("case: argument validation (no kernel is launched for any of these)")
+    lib = binding.load_library()
+    H, R = 1024, 4
+    h = handle_for(H, R, tp=2)
+    x = torch.zeros((2, R, H), dtype=torch.bfloat16, device="cuda")
+    s = torch.zeros((R, 4, H), dtype=torch.bfloat16, device="cuda")
+    f4 = torch.zeros((R, 4), dtype=torch.float32, device="cuda")
+    f16 = torch.zeros((R, 4, 4), dtype=torch.float32, device="cuda")
+    w = torch.zeros((H,), dtype=torch.bfloat16, device="cuda")
+    li = torch.zeros((R, H), dtype=torch.bfloat16, device="cuda")
+    md = torch.zeros((R, H), dtype=torch.uint8, device="cuda")
+    ms = torch.zeros((R, H // 32), dtype=torch.uint8, device="cuda")
+    p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+
+    def call(**kw):
+        a = dict(x=x, tp=2, s=s, post=f4, comb=f16, pre=f4, w=w, eps=1e-6, rows=R, out=s, li=li,
+                 md=md, ms=ms)
+        a.update(kw)
+        return lib.mhc_boundary(h.ptr, p(a["x"]), a["tp"], p(a["s"]), p(a["post"]), p(a["comb"]),
+                                p(a["pre"]), p(a["w"]), a["eps"], a["rows"], p(a["out"]),
+                                p(a["li"]), p(a["md"]), p(a["ms"]), None)
+
+    assert call(rows=R + 1) == 4
+    assert call(tp=3) == 4
+    assert call(tp=0) == 2
+    assert call(rows=-1) == 2
+    assert call(x=None) == 1
+    assert call(pre=None) == 1             # pre missing while norm weight / layer input given
+    assert call(li=None) == 1
+    assert call(ms=None) == 1              # MXFP8 outputs come in pairs
+    assert call(pre=None, w=None, li=None) == 1  # MXFP8 needs pre
+    assert call(eps=-1.0) == 2
+    assert call(eps=float("nan")) == 2
+    bad = torch.zeros((2 * R * H + 8,), dtype=torch.bfloat16, device="cuda")
+    assert lib.mhc_boundary(h.ptr, bad.data_ptr() + 2, 2, p(s), p(f4), p(f16), p(f4), p(w), 1e-6,
+                            R, p(s), p(li), p(md), p(ms), None) == 3
+    assert lib.mhc_set_option(h.ptr, binding.MHC_OPT_BOUNDARY_BLOCK, 96) == 2
+    assert lib.mhc_set_option(h.ptr, 77, 64) == 1
+    h2 = binding.Handle(1000, 4, max_rows=R, max_tp=2)  # hidden % 32 != 0: no MXFP8
+    x2 = torch.zeros((2, R, 1000), dtype=torch.bfloat16, device="cuda")
+    s2 = torch.zeros((R, 4, 1000), dtype=torch.bfloat16, device="cuda")
+    w2 = torch.zeros((1000,), dtype=torch.bfloat16, device="cuda")
+    li2 = torch.zeros((R, 1000), dtype=torch.bfloat16, device="cuda")
+    assert lib.mhc_boundary(h2.ptr, p(x2), 2, p(s2), p(f4), p(f16), p(f4), p(w2), 1e-6, R, p(s2),
+                            p(li2), p(md), p(ms), None) == 5
+    assert lib.mhc_pre_coeffs(h.ptr, p(s), p(w), p(f4), p(f4), 1e-6, 1e-6, 1e-6, 2.0, 1001, R,
+                              p(f4), p(f4), p(f16), None) == 2
+    torch.cuda.synchronize()
+
+
+def test_collapse_mean():
+    R, H = 40, 7168
+    say(f"case: collapse_mean rows={R} hidden={H}")
+    d = synth.boundary_inputs(13, rows=R, hidden=H, tp=1)
+    h = handle_for(H, R)
+    g = N(binding.collapse_mean(h, T(d["residual"])))
+    torch.cuda.synchronize()
+    assert_bf16_close(g, oracle.collapse_mean(d["residual"]), "collapse mean")
+    same = np.repeat(d["residual"][:, :1], 4, axis=1)
+    assert np.array_equal(N(binding.collapse_mean(h, T(same))), d["residual"][:, 0])
+
+
+def test_reset_then_reuse():
+    say("case: mhc_reset between calls")
+    d = synth.config(0)
+    h = handle_for(1024, 4, tp=2)
+    a = gpu_boundary(h, d)
+    h.reset()
+    b = gpu_boundary(h, d)
+    for k in a:
+        assert np.array_equal(a[k], b[k])
