@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--block", type=int, default=None, help="boundary workgroup size (64/128/256)")
+    ap.add_argument("--block", type=int, default=None, help="boundary workgroup size (128/256/512)")
     ap.add_argument("--chain", action="store_true", help="also time the 61-layer chained step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-rows", action="store_true", help="time only the headline call")
@@ -173,7 +173,7 @@ def main():
     h = binding.Handle(H, 4, max_rows=128, max_tp=8, top_k=8)
     if args.block:
         h.set_option(binding.MHC_OPT_BOUNDARY_BLOCK, args.block)
-    block = args.block or 64
+    block = args.block or 256
     nb = bytes_boundary(R, H, TP, pre=True, mxfp8=True)
     sets = n_sets(nb)
     base = {k: T(d1[k]) for k in ("x_partials", "residual", "post", "comb", "pre", "norm_weight")}

@@ -22,10 +22,17 @@
  *     synchronization, as HIP reports them.
  *   - rows == 0 is a valid empty call: it returns MHC_OK and touches nothing
  *     (pointers are then not checked).
- *   - A handle owns a small device scratch area (per-row partial sums,
- *     arrival counters, coefficient partials). Calls on one handle must be
- *     serialized, i.e. issued on one stream or ordered by the caller; two
- *     overlapping calls on one handle race on its scratch.
+ *   - A handle owns a small device scratch area (per-row handoff words and
+ *     epochs for the row RMS, an error word, coefficient partials). Calls on
+ *     one handle must be serialized, i.e. issued on one stream or ordered by
+ *     the caller; two overlapping calls on one handle race on its scratch.
+ *   - The boundary kernels with a layer input (pre != NULL) finish each
+ *     row's RMS by a bounded wait between the workgroups of that row, which
+ *     the library keeps co-resident (a launch uses at most a quarter of the
+ *     device's resident-workgroup capacity, in rounds if needed). A wait that
+ *     exceeds the spin limit gives up, counts itself in the handle's error
+ *     word (see mhc_get_errors) and the call's layer input is then wrong;
+ *     nothing hangs.
  *   - The only aliasing allowed is residual_out == residual (in-place update
  *     of the streams); any other overlap of inputs and outputs is undefined.
  *   - Alignment: bf16 tensors 16 bytes; fp32 and int32 tensors 4 bytes;
@@ -64,36 +71,55 @@ const char* mhc_status_string(int status);
  * by the model's hidden size, hc_mult, the largest row count it serves and
  * the MoE top_k, on one device. Here also by the largest number of TP
  * partial slices, max_tp.
- *   hidden   > 0, a multiple of 8 (16-byte vectors)       else MHC_ERR_SHAPE
+ *   hidden   in [8, 32768], a multiple of 8 (16-byte vectors)  else MHC_ERR_SHAPE
  *   hc_mult  == 4                                         else MHC_ERR_UNSUPPORTED
  *   max_rows in [1, 65536], max_tp in [1, 64], top_k in [1, 64]  else MHC_ERR_SHAPE
  *   device   a valid HIP device index                     else MHC_ERR_HIP
  * Allocates the handle's device scratch on `device` (hipMalloc) and zeroes it
- * (synchronously). On failure *out is set to NULL. The sizes are checked
- * before any HIP call.
+ * (synchronously) and picks the boundary block size (256, else 512, else 128:
+ * the first whose row fits half an XCD's resident workgroups and one polling
+ * wave); MHC_ERR_UNSUPPORTED if none does. On failure *out is set to NULL.
+ * The sizes are checked before any HIP call.
  */
 int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int device,
                mhc_handle* out);
 
 /*
- * mhc_set_option -- performance knobs of a handle (results do not depend on them).
- *   MHC_OPT_BOUNDARY_BLOCK: threads per workgroup of the boundary kernels, 64, 128 or
- *   256 (default 64). Each thread owns 8 hidden elements of a row, so a row is split
- *   into ceil(H / (8 * block)) workgroups. Other values: MHC_ERR_SHAPE.
- * Unknown options: MHC_ERR_INVALID_ARG. Takes effect for calls issued afterwards.
+ * mhc_set_option -- knobs of a handle. Results do not depend on them (except
+ * that a spin limit too small to cover the row handoff makes it give up, see
+ * above). Takes effect for calls issued afterwards.
+ *   MHC_OPT_BOUNDARY_BLOCK: threads per workgroup of the boundary kernels, 128, 256 or
+ *     512 (default: see mhc_create). Four threads share 8 hidden elements of a row, so
+ *     a row is split into ceil(H / (2 * block)) workgroups; a size giving more than 64
+ *     of them, or more than half an XCD's resident workgroups, is MHC_ERR_UNSUPPORTED.
+ *     Other values: MHC_ERR_SHAPE.
+ *   MHC_OPT_SPIN_LIMIT: polls (each followed by a short sleep) before a row-handoff
+ *     wait gives up; >= 0, default 2^20. Negative: MHC_ERR_SHAPE.
+ * Unknown options: MHC_ERR_INVALID_ARG.
  */
-enum mhc_option { MHC_OPT_BOUNDARY_BLOCK = 1 };
+enum mhc_option { MHC_OPT_BOUNDARY_BLOCK = 1, MHC_OPT_SPIN_LIMIT = 2 };
 int mhc_set_option(mhc_handle h, int option, int value);
+
+/*
+ * mhc_get_errors -- the number of row-handoff waits that gave up since the
+ * handle was created or last cleared. Enqueues a device-to-host copy of the
+ * error word on `stream` and waits for that stream (so it follows every call
+ * issued before it on `stream`); with clear != 0, then zeroes the word on
+ * `stream`. count must be a host pointer.
+ */
+int mhc_get_errors(mhc_handle h, unsigned* count, int clear, mhc_stream_t stream);
 
 /* Frees the handle and its scratch (synchronizes the device first). NULL is a no-op. */
 int mhc_destroy(mhc_handle h);
 
 /*
- * mhc_reset -- re-zero the handle's arrival counters on `stream`.
+ * mhc_reset -- re-zero the handle's handoff words, epochs and error word on
+ * `stream` (a fill kernel, so it may be captured in a graph).
  *
  * all_reduce page, BoundaryAllReduce.reset: drop what an aborted step left
- * behind. The counters return to zero by themselves after every completed
- * call; this is only needed after a call whose kernels did not complete.
+ * behind. Completed calls leave the handoff state consistent by themselves;
+ * this is only needed after a call whose kernels did not complete or whose
+ * waits gave up.
  */
 int mhc_reset(mhc_handle h, mhc_stream_t stream);
 
@@ -187,7 +213,7 @@ int mhc_collapse_mean(mhc_handle h, const uint16_t* streams, int rows, uint16_t*
  *   comb    = A after sinkhorn_iters rounds of {A <- A / (rowsum + sinkhorn_eps);
  *             A <- A / (colsum + sinkhorn_eps)}, starting from
  *             A[i,j] = exp(l'[2n+n*i+j] - max_j l'[2n+n*i+j])
- *   residual [R, n, H] bf16;  fn [n*H, NC] bf16 row-major
+ *   residual [R, n, H] bf16;  fn [n*H, NC] bf16 row-major (16-byte aligned)
  *   scale [3] fp32;  base [NC] fp32;  sinkhorn_iters in [0, 1000]
  *   pre_out [R, n], post_out [R, n], comb_out [R, n, n], fp32
  */

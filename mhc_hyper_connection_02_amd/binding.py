@@ -21,6 +21,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "mhc.h")
 
 MHC_OK = 0
 MHC_OPT_BOUNDARY_BLOCK = 1
+MHC_OPT_SPIN_LIMIT = 2
 _VALUE_ERRORS = {1, 2, 3, 4, 5}
 
 _lib = None
@@ -33,6 +34,7 @@ _SIGS = {
     "mhc_status_string": ([_i], ctypes.c_char_p),
     "mhc_create": ([_i, _i, _i, _i, _i, _i, ctypes.POINTER(_vp)], _i),
     "mhc_set_option": ([_vp, _i, _i], _i),
+    "mhc_get_errors": ([_vp, ctypes.POINTER(ctypes.c_uint), _i, _vp], _i),
     "mhc_destroy": ([_vp], _i),
     "mhc_reset": ([_vp, _vp], _i),
     "mhc_boundary": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _f, _i, _vp, _vp, _vp, _vp, _vp], _i),
@@ -128,6 +130,13 @@ class Handle:
 
     def set_option(self, option, value):
         _check(load_library().mhc_set_option(self.ptr, option, value), "mhc_set_option")
+
+    def errors(self, clear=False, stream=None):
+        """Row-handoff waits that gave up (``mhc_get_errors``); waits for the stream."""
+        n = ctypes.c_uint(0)
+        _check(load_library().mhc_get_errors(self.ptr, ctypes.byref(n), int(bool(clear)),
+                                             _stream(stream)), "mhc_get_errors")
+        return n.value
 
     def reset(self, stream=None):
         _check(load_library().mhc_reset(self.ptr, _stream(stream)), "mhc_reset")

@@ -15,24 +15,44 @@ constexpr int kMaxRows = 65536;
 constexpr int kMaxTp = 64;
 constexpr int kMaxTopK = 64;
 constexpr int kMaxSinkhornIters = 1000;
-constexpr int kMinBlock = 64;       // smallest boundary workgroup: sizes the partial-sum scratch
-constexpr int kDefaultBlock = 64;
+constexpr int kMinBlock = 128;      // smallest boundary workgroup: the most chunks per row
+constexpr int kDefaultBlock = 256;
+constexpr int kMaxChunks = 64;      // one polling lane per chunk
+constexpr int kMaxHidden = 32768;   // chunks per row at the smallest block stay <= one wave
+constexpr int kDefaultSpinLimit = 1 << 20;
 
 }  // namespace
 
 struct mhc_ctx {
   int hidden, hc_mult, max_rows, max_tp, top_k, device;
-  int part_stride;     // partial sums per row (chunks at the smallest block)
-  int block;           // boundary workgroup size in use
-  size_t pre_floats;   // coefficient-path scratch
-  void* scratch;       // one allocation: ywork | part | pre_part | counters
-  float* ywork;
-  float* part;
+  int slot_stride;         // handoff words per row (chunks at the smallest block)
+  int block;               // boundary workgroup size in use
+  int spin_limit;          // polls before a handoff wait gives up
+  int wgs_per_xcd[3];      // resident boundary workgroups per XCD at block 128 / 256 / 512
+  size_t pre_floats;       // coefficient-path scratch
+  void* scratch;           // one allocation: slots | pre_part | epoch | errors
+  unsigned long long* slots;
   float* pre_part;
-  unsigned* counters;
+  unsigned* epoch;
+  unsigned* errors;
+  size_t zero_words;       // 32-bit words of slots + epoch + errors (cleared by mhc_reset)
 };
 
 namespace {
+
+inline int block_index(int block) {
+  return block == 128 ? 0 : (block == 256 ? 1 : (block == 512 ? 2 : -1));
+}
+
+// Whether a handle may run the boundary at this block size: a row's chunks fit the
+// polling wave and half of an XCD's resident workgroups (a launch then spans rows
+// in rounds of at most a quarter of the XCD, or one row when a row needs more).
+inline bool block_usable(const mhc_ctx* h, int block) {
+  const int i = block_index(block);
+  if (i < 0) return false;
+  const int chunks = mhc::boundary_chunks(h->hidden, block);
+  return chunks <= kMaxChunks && h->wgs_per_xcd[i] / 2 >= chunks;
+}
 
 inline bool aligned(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -84,10 +104,12 @@ void fill_mix(const mhc_ctx* h, mhc::BoundaryLaunch& L, const uint16_t* residual
   L.layer_input_out = layer_input_out;
   L.mx_data_out = mx_data_out;
   L.mx_scale_out = mx_scale_out;
-  L.ywork = h->ywork;
-  L.part = h->part;
-  L.counters = h->counters;
-  L.part_stride = h->part_stride;
+  L.slots = h->slots;
+  L.epoch = h->epoch;
+  L.errors = h->errors;
+  L.slot_stride = h->slot_stride;
+  L.spin_limit = h->spin_limit;
+  L.max_wgs_per_xcd = h->wgs_per_xcd[block_index(h->block)];
   L.block = h->block;
 }
 
@@ -129,7 +151,7 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
                mhc_handle* out) {
   if (!out) return MHC_ERR_INVALID_ARG;
   *out = nullptr;
-  if (hidden <= 0 || hidden % 8 != 0 || hidden > (1 << 24)) return MHC_ERR_SHAPE;
+  if (hidden <= 0 || hidden % 8 != 0 || hidden > kMaxHidden) return MHC_ERR_SHAPE;
   if (max_rows < 1 || max_rows > kMaxRows || max_tp < 1 || max_tp > kMaxTp || top_k < 1 ||
       top_k > kMaxTopK || device < 0)
     return MHC_ERR_SHAPE;
@@ -153,7 +175,30 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   h->top_k = top_k;
   h->device = device;
   h->block = kDefaultBlock;
-  h->part_stride = mhc::boundary_chunks(hidden, kMinBlock);
+  h->spin_limit = kDefaultSpinLimit;
+  h->slot_stride = mhc::boundary_chunks(hidden, kMinBlock);
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      cus < 8) {
+    delete h;
+    (void)hipSetDevice(prev);
+    return MHC_ERR_HIP;
+  }
+  const int blocks[3] = {128, 256, 512};
+  for (int i = 0; i < 3; ++i)
+    h->wgs_per_xcd[i] = mhc::boundary_resident_wgs_per_cu(blocks[i]) * (cus / 8);
+  h->block = 0;
+  for (int b : {kDefaultBlock, 512, 128}) {
+    if (block_usable(h, b)) {
+      h->block = b;
+      break;
+    }
+  }
+  if (h->block == 0) {
+    delete h;
+    (void)hipSetDevice(prev);
+    return MHC_ERR_UNSUPPORTED;
+  }
   size_t pre_floats = 0;
   for (int r = 1; r <= max_rows; r += 16) {  // the split plan changes only every 16 rows
     const size_t f = mhc::pre_scratch_floats_for(r, hidden);
@@ -161,11 +206,11 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   }
   h->pre_floats = pre_floats;
 
-  const size_t y_bytes = round_up((size_t)max_rows * hidden * sizeof(float), 256);
-  const size_t part_bytes = round_up((size_t)max_rows * h->part_stride * sizeof(float), 256);
+  const size_t slot_bytes = round_up((size_t)max_rows * h->slot_stride * 8, 256);
+  const size_t epoch_bytes = round_up((size_t)max_rows * 4, 256);
+  const size_t err_bytes = 256;
   const size_t pre_bytes = round_up(pre_floats * sizeof(float), 256);
-  const size_t cnt_bytes = round_up((size_t)max_rows * sizeof(unsigned), 256);
-  const size_t total = y_bytes + part_bytes + pre_bytes + cnt_bytes;
+  const size_t total = slot_bytes + epoch_bytes + err_bytes + pre_bytes;
   void* base = nullptr;
   if (hipMalloc(&base, total) != hipSuccess) {
     delete h;
@@ -174,10 +219,11 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   }
   char* b = static_cast<char*>(base);
   h->scratch = base;
-  h->ywork = reinterpret_cast<float*>(b);
-  h->part = reinterpret_cast<float*>(b + y_bytes);
-  h->pre_part = reinterpret_cast<float*>(b + y_bytes + part_bytes);
-  h->counters = reinterpret_cast<unsigned*>(b + y_bytes + part_bytes + pre_bytes);
+  h->slots = reinterpret_cast<unsigned long long*>(b);
+  h->epoch = reinterpret_cast<unsigned*>(b + slot_bytes);
+  h->errors = reinterpret_cast<unsigned*>(b + slot_bytes + epoch_bytes);
+  h->pre_part = reinterpret_cast<float*>(b + slot_bytes + epoch_bytes + err_bytes);
+  h->zero_words = (slot_bytes + epoch_bytes + err_bytes) / 4;
   hipError_t e = mhc::launch_fill_u32(reinterpret_cast<unsigned*>(base), total / 4, 0u, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   (void)hipSetDevice(prev);
@@ -194,12 +240,29 @@ int mhc_set_option(mhc_handle h, int option, int value) {
   if (!h) return MHC_ERR_INVALID_ARG;
   switch (option) {
     case MHC_OPT_BOUNDARY_BLOCK:
-      if (value != 64 && value != 128 && value != 256) return MHC_ERR_SHAPE;
+      if (block_index(value) < 0) return MHC_ERR_SHAPE;
+      if (!block_usable(h, value)) return MHC_ERR_UNSUPPORTED;
       h->block = value;
+      return MHC_OK;
+    case MHC_OPT_SPIN_LIMIT:
+      if (value < 0) return MHC_ERR_SHAPE;
+      h->spin_limit = value;
       return MHC_OK;
     default:
       return MHC_ERR_INVALID_ARG;
   }
+}
+
+int mhc_get_errors(mhc_handle h, unsigned* count, int clear, mhc_stream_t stream) {
+  if (!h || !count) return MHC_ERR_INVALID_ARG;
+  int st = check_device(h);
+  if (st != MHC_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(count, h->errors, sizeof(unsigned), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return MHC_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return MHC_ERR_HIP;
+  if (clear) return launch_status(mhc::launch_fill_u32(h->errors, 1, 0u, s));
+  return MHC_OK;
 }
 
 int mhc_destroy(mhc_handle h) {
@@ -219,8 +282,8 @@ int mhc_reset(mhc_handle h, mhc_stream_t stream) {
   if (!h) return MHC_ERR_INVALID_ARG;
   int st = check_device(h);
   if (st != MHC_OK) return st;
-  return launch_status(mhc::launch_fill_u32(h->counters, (size_t)h->max_rows, 0u,
-                                            static_cast<hipStream_t>(stream)));
+  return launch_status(mhc::launch_fill_u32(reinterpret_cast<unsigned*>(h->scratch), h->zero_words,
+                                            0u, static_cast<hipStream_t>(stream)));
 }
 
 int mhc_boundary(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_t* residual,
@@ -311,7 +374,7 @@ int mhc_pre_coeffs(mhc_handle h, const uint16_t* residual, const uint16_t* fn,
   if (rows == 0) return MHC_OK;
   if (!residual || !fn || !scale || !base || !pre_out || !post_out || !comb_out)
     return MHC_ERR_INVALID_ARG;
-  if (!aligned(residual, 16) || !aligned(fn, 2) || !aligned(scale, 4) || !aligned(base, 4) ||
+  if (!aligned(residual, 16) || !aligned(fn, 16) || !aligned(scale, 4) || !aligned(base, 4) ||
       !aligned(pre_out, 4) || !aligned(post_out, 4) || !aligned(comb_out, 4))
     return MHC_ERR_ALIGN;
   int st = check_device(h);

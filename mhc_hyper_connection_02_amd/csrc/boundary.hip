@@ -6,23 +6,42 @@
 // stated in include/mhc.h.
 //
 // Work decomposition. A row (token) is split into `chunks` pieces of
-// 8 * BS bf16 elements; one workgroup of BS threads owns one (row, chunk)
-// and each thread one 16-byte vector of every tensor it touches, so every
-// load and store is a coalesced 16-byte access. All of a thread's loads
-// (tp partial slices, or top_k gathered expert rows plus the shared row, and
-// the hc streams) are issued before the first use.
+// 2 * BS bf16 elements; one workgroup of BS threads owns one (row, chunk).
+// Four consecutive lanes (a quad) own one 16-byte vector (8 elements) of the
+// row: lane q loads stream q and a quarter of the sublayer output (slices or
+// gathered expert rows q, q+4, ...), the quad combines its partial sums and
+// exchanges the streams over DPP quad permutations, and lane q then computes
+// and stores output stream q and two elements of the layer input. Spreading
+// a vector over four lanes gives four times the waves of one lane per vector
+// for the same bytes, which keeps the per-wave arithmetic (it runs after the
+// loads land) short. A lane issues all of its loads before the first use.
+// It stores its stream as soon as it is computed, overlapping the loads of
+// the rest of the row; only the layer input (and its MXFP8 form) waits for
+// the row's RMS.
 //
-// The RMS of a row needs the whole row. Each workgroup writes its fp32
-// collapse chunk y and its partial sum of y^2 to the handle's scratch,
-// releases them, and bumps the row's arrival counter; the last workgroup to
-// arrive for a row sums the partials in chunk order (deterministic, no float
-// atomics), normalizes the whole row, writes the layer input and its MXFP8
-// form, and returns the counter to zero for the next call.
+// The row RMS. The RMS needs the whole row, and a row spans several
+// workgroups. Each workgroup publishes its partial sum of y^2 as ONE 64-bit
+// word (call tag << 32 | fp32 bits) with a relaxed device-scope atomic
+// store; wave 0 of every workgroup of the row then polls the row's words
+// until all carry this call's tag and adds them in chunk order (the same
+// fixed order in every workgroup: deterministic, no float atomics). Because
+// the tag travels in the same word as the value, no fence is needed, so no
+// L2 writeback or invalidate is issued. The tag is the row's epoch + 1,
+// read at the start; chunk 0 advances the epoch once it has seen every
+// word, which is after every workgroup of the row has read it. Epochs live
+// in device memory, so graph replays stay correct.
+//
+// Co-residency. Polling requires all workgroups of a row to be resident at
+// once. The host sizes the grid to at most a quarter of the device's
+// resident-workgroup capacity (or one row per XCD when a row needs more, at
+// most half of it) and, for larger row counts, walks the rows in rounds: in round k, workgroup w handles one (row, chunk) of a block of
+// rows that the grid covers entirely, so every row's chunks are live
+// together. The wait is bounded (spin_limit polls with s_sleep); a timeout
+// is counted in the handle's error word and the workgroup goes on.
 //
 // XCD placement. Consecutive workgroup ids are dealt round-robin to the 8
-// XCDs, so a row's chunks are given ids congruent to the row mod 8: all
-// workgroups of one row share one XCD's L2, where the scratch round trip
-// stays.
+// XCDs, so a row's chunks get ids congruent to the row mod 8: all
+// workgroups of one row share one XCD's L2, where their polling stays.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -49,212 +68,268 @@ struct BoundaryParams {
   const float* pre;         // [rows][4]
   const uint4* norm_w;      // [hv]
   float eps;
-  int rows, hv, hidden, chunks, rows_per_xcd;
+  int rows, hv, hidden, chunks;
   uint4* layer_out;         // [rows][hv]
   uint2* mx_data;           // [rows][hv] (8 E4M3 codes per vector)
   uint8_t* mx_scale;        // [rows][hidden / 32]
-  // scratch
-  float* ywork;             // [rows][hidden]
-  float* part;              // [rows][max_chunks]
-  unsigned* counters;       // [rows]
-  int part_stride;
+  // row-RMS handoff
+  unsigned long long* slots;  // [max_rows][slot_stride]
+  unsigned* epoch;            // [max_rows]
+  unsigned* errors;           // [1]
+  int slot_stride;
+  int rows_per_round;         // rows per XCD per round
+  int rounds;
+  int spin_limit;
 };
+
+// Pick element i (0..3) of four values by a lane-dependent index (register selects).
+__device__ __forceinline__ float pick4(float a0, float a1, float a2, float a3, int i) {
+  return i == 0 ? a0 : (i == 1 ? a1 : (i == 2 ? a2 : a3));
+}
+
+template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8>
+__device__ __forceinline__ void boundary_item(const BoundaryParams& p, int r, int c, float* s_red,
+                                              float* s_inv) {
+  constexpr int kGroups = BS / 4;  // 16-byte vectors (8 elements) per workgroup
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int q = tid & 3;                     // this lane's output stream
+  const int v = c * kGroups + (tid >> 2);    // the quad's 16-byte vector index in the row
+  const bool active = v < p.hv;
+  const int va = active ? v : 0;             // an in-bounds vector for every lane's loads
+
+  // the row's epoch, read first by every lane so that its latency hides under the data
+  // loads (only wave 0 uses it, at the handoff)
+  unsigned epoch_now = 0;
+  if constexpr (HAS_PRE)
+    epoch_now = __hip_atomic_load(p.epoch + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // --- loads, all issued before any use; every address is in bounds, so no load sits
+  //     behind a branch and results of the lanes or slots that do not count are dropped
+  //     by selects afterwards
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  // finalize: this lane's expert slots k = q, q+4, ... first, since the gathers need them
+  int pk[4];
+  float wk[4];
+  if constexpr (FINALIZE) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = 4 * u + q;
+      const bool in = k < p.top_k;
+      pk[u] = in ? p.idx[r * p.top_k + k] : -1;
+      wk[u] = in ? p.ew[r * p.top_k + k] : 0.f;
+    }
+  }
+  const float post_q = p.post[r * kHC + q];
+  float cq[kHC];  // cq[d] = comb[q][q ^ d], the weight of the stream a xor-d quad move brings
+#pragma unroll
+  for (int d = 0; d < kHC; ++d) cq[d] = p.comb[r * kHC * kHC + q * kHC + (q ^ d)];
+  float pre_q = 0.f;
+  if constexpr (HAS_PRE) pre_q = p.pre[r * kHC + q];
+  const uint4 sv = load_nt(p.res_in + ((size_t)r * kHC + q) * p.hv + va);
+  uint32_t wv = 0;
+  if constexpr (HAS_PRE) wv = reinterpret_cast<const uint32_t*>(p.norm_w)[(size_t)va * 4 + q];
+
+  if constexpr (!FINALIZE) {
+    // lane q sums slices t = q, q+4, q+8, ... (ascending)
+    const uint4* src = p.xp + (size_t)r * p.hv + va;
+    const size_t slice = (size_t)p.rows * p.hv;
+    for (int t0 = 0; t0 < p.tp; t0 += 16) {
+      uint4 xv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (t0 + 4 * u < p.tp) {  // uniform: some lane of the quad has slice t0 + 4u + q
+          const int t = t0 + 4 * u + q;
+          xv[u] = load_nt(src + (size_t)(t < p.tp ? t : 0) * slice);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (t0 + 4 * u < p.tp) {
+          const bool in = t0 + 4 * u + q < p.tp;
+          float f[8];
+          unpack8(xv[u], f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] += in ? f[e] : 0.f;
+        }
+      }
+    }
+  } else {
+    // lane q gathers slots k = q, q+4, ... (ascending); lane 3 also adds the shared row
+    const uint4 shv = load_nt(p.shared + (size_t)r * p.hv + va);
+    uint4 gv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (4 * u < p.top_k) {
+        const bool ok = pk[u] >= 0 && pk[u] < p.num_permuted;
+        gv[u] = load_nt(p.g + (size_t)(ok ? pk[u] : 0) * p.hv + va);
+        if (!ok) wk[u] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (4 * u < p.top_k) {
+        float f[8];
+        unpack8(gv[u], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(wk[u], f[e], x[e]);
+      }
+    }
+    // top_k beyond 16: further slots, in the same lane order
+    for (int k0 = 16; k0 < p.top_k; k0 += 4) {
+      const int k = k0 + q;
+      const bool in = k < p.top_k;
+      const int pi = in ? p.idx[r * p.top_k + k] : -1;
+      const bool ok = pi >= 0 && pi < p.num_permuted;
+      const float w = ok ? p.ew[r * p.top_k + k] : 0.f;
+      const uint4 g = load_nt(p.g + (size_t)(ok ? pi : 0) * p.hv + va);
+      float f[8];
+      unpack8(g, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(w, f[e], x[e]);
+    }
+    float f[8];
+    unpack8(shv, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] += (q == 3) ? f[e] : 0.f;
+  }
+
+  // the quad's four partial sums -> the full sum in every lane (a + b == b + a exactly)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] += dpp_f32<kDppQuadXor1>(x[e]);
+    x[e] += dpp_f32<kDppQuadXor2>(x[e]);
+    x[e] = round_bf16(x[e]);  // the reduced output is a bf16 tensor
+  }
+
+  // --- mHC post for stream q: s'_q = post_q x + sum_j comb_qj s_j -------------------
+  uint4 sj[kHC];
+  sj[0] = sv;
+  sj[1] = dpp_u4<kDppQuadXor1>(sv);
+  sj[2] = dpp_u4<kDppQuadXor2>(sv);
+  sj[3] = dpp_u4<kDppQuadXor3>(sv);
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = post_q * x[e];
+#pragma unroll
+  for (int d = 0; d < kHC; ++d) {
+    float f[8];
+    unpack8(sj[d], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(cq[d], f[e], o[e]);
+  }
+  const uint4 so = pack8_round(o);
+  // the new streams do not depend on the RMS: store them now, overlapping the loads of
+  // the rest of the row
+  if (active) p.res_out[((size_t)r * kHC + q) * p.hv + v] = so;
+
+  float y2[2] = {0.f, 0.f};  // this lane's two elements of the collapse: 2q, 2q+1
+  float sq = 0.f;
+  if constexpr (HAS_PRE) {
+    // y = sum_j pre_j s'_j over the quad, on the bf16 streams
+    float f[8], y[8];
+    unpack8(so, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y[e] = pre_q * f[e];
+      y[e] += dpp_f32<kDppQuadXor1>(y[e]);
+      y[e] += dpp_f32<kDppQuadXor2>(y[e]);
+    }
+    y2[0] = pick4(y[0], y[2], y[4], y[6], q);
+    y2[1] = pick4(y[1], y[3], y[5], y[7], q);
+    // lanes past the row's end loaded an in-bounds stand-in vector: they add nothing
+    sq = active ? __builtin_fmaf(y2[0], y2[0], y2[1] * y2[1]) : 0.f;
+
+    // --- the row's sum of squares: workgroup partial, then the handoff ------------
+    sq = wave_sum(sq);
+    if (lane == 0) s_red[wave] = sq;
+    __syncthreads();
+    if (wave == 0) {
+      const unsigned want = epoch_now + 1u;
+      float part = 0.f;
+#pragma unroll
+      for (int w = 0; w < BS / kWave; ++w) part += s_red[w];
+      unsigned long long* row_slots = p.slots + (size_t)r * p.slot_stride;
+      if (lane == 0) {
+        const unsigned long long word = ((unsigned long long)want << 32) | __float_as_uint(part);
+        __hip_atomic_store(row_slots + c, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      float val = 0.f;
+      if (lane < p.chunks) {
+        unsigned long long wd;
+        int spins = 0;
+        for (;;) {
+          wd = __hip_atomic_load(row_slots + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((unsigned)(wd >> 32) == want) break;
+          if (++spins > p.spin_limit) {
+            __hip_atomic_fetch_add(p.errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        val = __uint_as_float((unsigned)wd);
+      }
+      float tot = 0.f;
+      for (int k = 0; k < p.chunks; ++k)  // chunk order
+        tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), k));
+      if (lane == 0) {
+        *s_inv = 1.0f / sqrtf(tot / (float)p.hidden + p.eps);
+        if (c == 0) __hip_atomic_store(p.epoch + r, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+  }
+
+  // --- stores -----------------------------------------------------------------------
+  uint32_t ob = 0;
+  float q2[2] = {0.f, 0.f};
+  if constexpr (HAS_PRE) {
+    const float inv = *s_inv;
+    const float l0 = (y2[0] * inv) * bf16_lo(wv);
+    const float l1 = (y2[1] * inv) * bf16_hi(wv);
+    ob = pack2_bits(f32_to_bf16_bits(l0), f32_to_bf16_bits(l1));
+    q2[0] = bf16_lo(ob);
+    q2[1] = bf16_hi(ob);
+  }
+  float amax = 0.f;
+  if constexpr (MXFP8) {
+    // a 32-element block = 4 vectors = the 16 lanes of one DPP row (hidden % 32 == 0,
+    // so rows are wholly active or inactive)
+    amax = fmaxf(fabsf(q2[0]), fabsf(q2[1]));
+    amax = fmaxf(amax, dpp_f32<kDppQuadXor1>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppRowRor4>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppRowRor8>(amax));
+  }
+  if (!active) return;
+  if constexpr (HAS_PRE) {
+    reinterpret_cast<uint32_t*>(p.layer_out)[((size_t)r * p.hv + v) * 4 + q] = ob;
+    if constexpr (MXFP8) {
+      const int ex = e8m0_exponent(__float_as_uint(amax));
+      const float sc = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-e, exact
+      const uint32_t codes = f32_to_e4m3(q2[0] * sc) | (f32_to_e4m3(q2[1] * sc) << 8);
+      reinterpret_cast<uint16_t*>(p.mx_data)[((size_t)r * p.hv + v) * 4 + q] = (uint16_t)codes;
+      if ((lane & 15) == 0) p.mx_scale[(size_t)r * (p.hidden / 32) + (v >> 2)] = (uint8_t)(ex + 127);
+    }
+  }
+}
 
 template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8>
 __global__ __launch_bounds__(BS) void boundary_kernel(const BoundaryParams p) {
-  // --- (row, chunk) of this workgroup, XCD-aware -------------------------------
+  __shared__ float s_red[BS / kWave];
+  __shared__ float s_inv;
   const int wg = blockIdx.x;
   const int xcd = wg % kXcds;
   const int local = wg / kXcds;
-  const int r = (local / p.chunks) * kXcds + xcd;
   const int c = local % p.chunks;
-  if (r >= p.rows) return;  // padding workgroup (rows not a multiple of 8)
-
-  const int tid = threadIdx.x;
-  const int v = c * BS + tid;  // 16-byte vector index in the row
-  const bool active = v < p.hv;
-
-  // --- coefficients (uniform per workgroup) ------------------------------------
-  float pst[kHC], cmb[kHC * kHC], pr[kHC];
-#pragma unroll
-  for (int i = 0; i < kHC; ++i) pst[i] = p.post[r * kHC + i];
-#pragma unroll
-  for (int i = 0; i < kHC * kHC; ++i) cmb[i] = p.comb[r * kHC * kHC + i];
-  if constexpr (HAS_PRE) {
-#pragma unroll
-    for (int i = 0; i < kHC; ++i) pr[i] = p.pre[r * kHC + i];
-  }
-
-  float y[8];
-  float sq = 0.f;
-  if (active) {
-    // --- loads: the sublayer output and the streams ----------------------------
-    const uint4* res = p.res_in + (size_t)r * kHC * p.hv + v;
-    uint4 sv[kHC];
-#pragma unroll
-    for (int j = 0; j < kHC; ++j) sv[j] = load_nt(res + (size_t)j * p.hv);
-
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    if constexpr (!FINALIZE) {
-      const uint4* src = p.xp + (size_t)r * p.hv + v;
-      const size_t slice = (size_t)p.rows * p.hv;
-      for (int t0 = 0; t0 < p.tp; t0 += 8) {
-        uint4 xv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (t0 + u < p.tp) xv[u] = load_nt(src + (size_t)(t0 + u) * slice);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (t0 + u < p.tp) {
-            float f[8];
-            unpack8(xv[u], f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] += f[e];
-          }
-        }
-      }
-    } else {
-      const uint4 shv = load_nt(p.shared + (size_t)r * p.hv + v);
-      for (int k0 = 0; k0 < p.top_k; k0 += 8) {
-        uint4 gv[8];
-        float wk[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int k = k0 + u;
-          wk[u] = 0.f;
-          if (k < p.top_k) {
-            const int pi = p.idx[r * p.top_k + k];
-            if (pi >= 0 && pi < p.num_permuted) {
-              wk[u] = p.ew[r * p.top_k + k];
-              gv[u] = load_nt(p.g + (size_t)pi * p.hv + v);
-            } else {
-              gv[u] = make_uint4(0u, 0u, 0u, 0u);
-            }
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (k0 + u < p.top_k) {
-            float f[8];
-            unpack8(gv[u], f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(wk[u], f[e], x[e]);
-          }
-        }
-      }
-      float f[8];
-      unpack8(shv, f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] += f[e];
-    }
-    // the reduced output is a bf16 tensor
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = round_bf16(x[e]);
-
-    // --- mHC post: s'_i = sum_j comb_ij s_j + post_i x ---------------------------
-    float s[kHC][8];
-#pragma unroll
-    for (int j = 0; j < kHC; ++j) unpack8(sv[j], s[j]);
-    uint4* out = p.res_out + (size_t)r * kHC * p.hv + v;
-    float sn[kHC][8];
-#pragma unroll
-    for (int i = 0; i < kHC; ++i) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float a = pst[i] * x[e];
-#pragma unroll
-        for (int j = 0; j < kHC; ++j) a = __builtin_fmaf(cmb[i * kHC + j], s[j][e], a);
-        sn[i][e] = a;
-      }
-      const uint4 o = pack8_round(sn[i]);
-      out[(size_t)i * p.hv] = o;
-      if constexpr (HAS_PRE) unpack8(o, sn[i]);  // the collapse reads the bf16 streams
-    }
-
-    // --- pre collapse and the chunk's sum of squares ------------------------------
-    if constexpr (HAS_PRE) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float a = 0.f;
-#pragma unroll
-        for (int j = 0; j < kHC; ++j) a = __builtin_fmaf(pr[j], sn[j][e], a);
-        y[e] = a;
-        sq = __builtin_fmaf(a, a, sq);
-      }
-    }
-  }
-  if constexpr (!HAS_PRE) return;
-
-  // --- publish the chunk: y to scratch, the partial sum of squares ---------------
-  __shared__ float s_red[BS / kWave];
-  __shared__ int s_last;
-  __shared__ float s_inv;
-  float* yrow = p.ywork + (size_t)r * p.hidden;
-  if (active) {
-    float4* dst = reinterpret_cast<float4*>(yrow + (size_t)v * 8);
-    dst[0] = make_float4(y[0], y[1], y[2], y[3]);
-    dst[1] = make_float4(y[4], y[5], y[6], y[7]);
-  }
-  sq = wave_sum(sq);
-  if ((tid & (kWave - 1)) == 0) s_red[tid / kWave] = sq;
-  __syncthreads();
-  if (tid == 0) {
-    float t = 0.f;
-#pragma unroll
-    for (int w = 0; w < BS / kWave; ++w) t += s_red[w];
-    p.part[(size_t)r * p.part_stride + c] = t;
-  }
-  __threadfence();  // release this thread's scratch stores at device scope
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(p.counters + r, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (unsigned)(p.chunks - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-
-  // --- last arriver: normalize the whole row ------------------------------------
-  __threadfence();  // acquire: every chunk's scratch stores are visible
-  if (tid == 0) {
-    float tot = 0.f;
-    for (int k = 0; k < p.chunks; ++k) tot += p.part[(size_t)r * p.part_stride + k];
-    s_inv = 1.0f / sqrtf(tot / (float)p.hidden + p.eps);
-    __hip_atomic_store(p.counters + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  const float inv = s_inv;
-  for (int vv = tid; vv < p.hv; vv += BS) {
-    const float4* src = reinterpret_cast<const float4*>(yrow + (size_t)vv * 8);
-    const float4 a = src[0], b = src[1];
-    float w[8];
-    unpack8(p.norm_w[vv], w);
-    float o[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (o[e] * inv) * w[e];
-    const uint4 ob = pack8_round(o);
-    p.layer_out[(size_t)r * p.hv + vv] = ob;
-    if constexpr (MXFP8) {
-      // 32-element block = the 4 consecutive lanes vv & ~3 .. vv | 3 (hidden % 32 == 0)
-      float q[8];
-      unpack8(ob, q);
-      float amax = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(q[e]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-      amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-      const int ex = e8m0_exponent(__float_as_uint(amax));
-      const float sc = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-e, exact
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) lo |= f32_to_e4m3(q[e] * sc) << (8 * e);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) hi |= f32_to_e4m3(q[4 + e] * sc) << (8 * e);
-      p.mx_data[(size_t)r * p.hv + vv] = make_uint2(lo, hi);
-      if ((vv & 3) == 0) p.mx_scale[(size_t)r * (p.hidden / 32) + (vv >> 2)] = (uint8_t)(ex + 127);
-    }
+  const int jr = local / p.chunks;  // which row of this XCD's block in a round
+  for (int round = 0; round < p.rounds; ++round) {
+    const int r = (round * p.rows_per_round + jr) * kXcds + xcd;
+    if (r >= p.rows) break;  // uniform per workgroup; later rounds only go higher
+    boundary_item<BS, FINALIZE, HAS_PRE, MXFP8>(p, r, c, s_red, &s_inv);
   }
 }
 
@@ -285,7 +360,7 @@ __global__ __launch_bounds__(256) void collapse_mean_kernel(const uint4* __restr
 }
 
 // ---------------------------------------------------------------------------
-// host-side launchers
+// host side
 // ---------------------------------------------------------------------------
 template <int BS, bool FIN, bool PRE, bool MX>
 static hipError_t launch_one(const BoundaryParams& p, int grid, hipStream_t st) {
@@ -306,9 +381,38 @@ static hipError_t launch_bs(const BoundaryParams& p, bool fin, bool pre, bool mx
             : launch_one<BS, true, true, false>(p, grid, st);
 }
 
+template <int BS, bool FIN, bool PRE, bool MX>
+static int occupancy_one() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, boundary_kernel<BS, FIN, PRE, MX>, BS, 0) !=
+      hipSuccess)
+    return 0;
+  return n;
+}
+
+template <int BS>
+static int occupancy_bs() {
+  // the polling variants only; the smallest of them bounds the co-resident grid
+  int n = occupancy_one<BS, false, true, false>();
+  n = min(n, occupancy_one<BS, false, true, true>());
+  n = min(n, occupancy_one<BS, true, true, false>());
+  n = min(n, occupancy_one<BS, true, true, true>());
+  return n;
+}
+
+int boundary_resident_wgs_per_cu(int block) {
+  switch (block) {
+    case 128: return occupancy_bs<128>();
+    case 256: return occupancy_bs<256>();
+    case 512: return occupancy_bs<512>();
+    default: return 0;
+  }
+}
+
 int boundary_chunks(int hidden, int block) {
   const int hv = hidden / 8;
-  return (hv + block - 1) / block;
+  const int groups = block / 4;  // four lanes per 16-byte vector
+  return (hv + groups - 1) / groups;
 }
 
 hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
@@ -335,19 +439,33 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   p.layer_out = reinterpret_cast<uint4*>(L.layer_input_out);
   p.mx_data = reinterpret_cast<uint2*>(L.mx_data_out);
   p.mx_scale = L.mx_scale_out;
-  p.ywork = L.ywork;
-  p.part = L.part;
-  p.counters = L.counters;
-  p.part_stride = L.part_stride;
-  p.rows_per_xcd = (L.rows + kXcds - 1) / kXcds;
-  const int grid = kXcds * p.rows_per_xcd * p.chunks;
+  p.slots = L.slots;
+  p.epoch = L.epoch;
+  p.errors = L.errors;
+  p.slot_stride = L.slot_stride;
+  p.spin_limit = L.spin_limit;
   const bool fin = L.gemm2_permuted != nullptr;
   const bool pre = L.pre != nullptr;
   const bool mx = L.mx_data_out != nullptr;
+  const int row_blocks = (L.rows + kXcds - 1) / kXcds;  // rows per XCD in total
+  if (pre) {
+    // a round may use at most a quarter of the XCD's resident workgroups
+    // (at least one row: a row's chunks fit half an XCD, checked at handle creation)
+    const int per_xcd = L.max_wgs_per_xcd / 4;
+    int rpr = per_xcd / p.chunks;
+    if (rpr < 1) rpr = 1;
+    if (rpr > row_blocks) rpr = row_blocks;
+    p.rows_per_round = rpr;
+    p.rounds = (row_blocks + rpr - 1) / rpr;
+  } else {
+    p.rows_per_round = row_blocks;
+    p.rounds = 1;
+  }
+  const int grid = kXcds * p.rows_per_round * p.chunks;
   switch (L.block) {
-    case 64: return launch_bs<64>(p, fin, pre, mx, grid, stream);
     case 128: return launch_bs<128>(p, fin, pre, mx, grid, stream);
     case 256: return launch_bs<256>(p, fin, pre, mx, grid, stream);
+    case 512: return launch_bs<512>(p, fin, pre, mx, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

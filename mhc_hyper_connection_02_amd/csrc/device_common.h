@@ -87,10 +87,39 @@ __device__ __forceinline__ int e8m0_exponent(uint32_t amax_bits) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// Cross-lane moves on the DPP path (no LDS round trip). Quad permutations act
+// within each group of 4 lanes; row rotations within each row of 16 lanes.
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppQuadXor3 = 0x1B;   // quad_perm [3,2,1,0]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint4 dpp_u4(const uint4& v) {
+  return make_uint4(dpp_u32<CTRL>(v.x), dpp_u32<CTRL>(v.y), dpp_u32<CTRL>(v.z), dpp_u32<CTRL>(v.w));
+}
+
+// Sum over the 64 lanes on the DPP path: within each row of 16 (quad xors, then row
+// rotations), then the four row sums read into scalars. Every lane gets the same value.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppRowRor4>(v);
+  v += dpp_f32<kDppRowRor8>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 }  // namespace mhc

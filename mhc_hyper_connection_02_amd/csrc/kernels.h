@@ -29,10 +29,12 @@ struct BoundaryLaunch {
   uint16_t* layer_input_out;
   uint8_t* mx_data_out;         // NULL: no MXFP8
   uint8_t* mx_scale_out;
-  float* ywork;                 // [max_rows][hidden]
-  float* part;                  // [max_rows][part_stride]
-  unsigned* counters;           // [max_rows], zero between calls
-  int part_stride;
+  unsigned long long* slots;    // [max_rows][slot_stride] row-RMS handoff words
+  unsigned* epoch;              // [max_rows]
+  unsigned* errors;             // [1] handoff timeouts
+  int slot_stride;
+  int spin_limit;
+  int max_wgs_per_xcd;          // resident workgroups of this block size on one XCD
   int block;                    // 64, 128 or 256 threads per workgroup
 };
 
@@ -50,6 +52,7 @@ struct PreLaunch {
 };
 
 int boundary_chunks(int hidden, int block);
+int boundary_resident_wgs_per_cu(int block);
 hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream);
 hipError_t launch_collapse_mean(const uint16_t* streams, int rows, int hidden, uint16_t* out,
                                 hipStream_t stream);

@@ -5,25 +5,30 @@
 // coefficient call's arguments); the arithmetic is stated in include/mhc.h.
 //
 // Kernel 1 (split-K): the projection l[r,c] = sum_k v[r,k] fn[k,c] is a skinny
-// GEMM (M = rows, N = 24 logits, K = n*hidden). Each workgroup owns 16 rows and
-// one contiguous range of 32-wide k steps; its four waves take alternate steps
-// and run v_mfma_f32_16x16x32_bf16 on the raw bf16 operands (bf16 products are
-// exact in fp32, and 1/RMS is applied afterwards, so no normalized copy is
-// rounded). The MFMA's M side is fn^T (logit columns 0..15 and 16..31, the
-// last 8 zero), its N side is the 16 rows. The same pass accumulates the
-// rows' sums of squares. Partials go to scratch [k-split][row][25].
+// GEMM (M = rows, N = 24 logits, K = n*hidden), HBM-bound. Each workgroup owns
+// 16 rows and one contiguous range of 32-wide k steps. It first copies its
+// slice of fn (contiguous in memory: [k range][24]) into LDS with 16-byte
+// loads, transposed to [logit][k] so that each lane's MFMA operand (8
+// consecutive k of one logit column) is one 16-byte LDS read. Its four waves
+// then take alternate k steps and run v_mfma_f32_16x16x32_bf16 on the raw
+// bf16 operands (bf16 products are exact in fp32; 1/RMS is applied
+// afterwards, so no normalized copy is rounded). The MFMA's M side is fn^T
+// (logit columns 0..15 and 16..31, the last 8 zero), its N side the 16 rows.
+// The same pass accumulates the rows' sums of squares. Each workgroup writes
+// its 16 x 25 partials to scratch laid out [row][25][k-split], so that the
+// epilogue reads each (row, logit) range contiguously.
 //
-// Kernel 2: one wave per row sums the k-split partials in a fixed order, then
-// applies 1/RMS, scale/base, the sigmoids and the Sinkhorn iterations, one lane
-// per logit (the 16 comb entries sit in lanes 32..47, row i / column j at lane
-// 32 + 4i + j, so row sums are quad butterflies and column sums use xor 4, 8).
+// Kernel 2: one wave per row. Lanes 0..24 each sum one logit's (or the sum of
+// squares') partials over the k-splits in split order, then the logits get
+// 1/RMS, scale and base; lanes 0..7 write pre and post; lanes 0..3 each hold
+// one row of the 4x4 comb matrix for the Sinkhorn iterations (row sums in
+// registers, column sums over the four lanes).
 #include "device_common.h"
 #include "kernels.h"
 
 namespace mhc {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kN = 4;                      // hc_mult
@@ -32,15 +37,21 @@ constexpr int kPartW = kNC + 1;            // + sum of squares
 constexpr int kRB = 16;                    // rows per workgroup (MFMA N)
 constexpr int kStepK = 32;                 // MFMA K
 constexpr int kPreWaves = 4;
+constexpr int kTargetWgs = 256;
+constexpr int kMaxStepsPerWg = 32;         // LDS: 24 x (32*32 + 8) bf16 = 49.5 KB
+constexpr int kLdsPad = 8;
 
 struct PrePartialParams {
   const uint16_t* res;   // [rows][K] bf16 (the streams, flattened)
   const uint16_t* fn;    // [K][24] bf16
-  float* part;           // [ks][rows_pad][25]
-  int rows, K, ks_count, steps_per_wg, nsteps, rows_pad;
+  float* part;           // [rows_pad][25][ks]
+  int rows, K, ks_count, steps_per_wg, nsteps;
 };
 
 __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const PrePartialParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t fnT[kNC][kMaxStepsPerWg * kStepK + kLdsPad];
+  __shared__ float red[kPreWaves][kRB][kPartW];
+
   const int wg = blockIdx.x;
   const int ks = wg % p.ks_count;  // ks_count % 8 == 0: a k range stays on one XCD
   const int rb = wg / p.ks_count;
@@ -51,25 +62,40 @@ __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const Pr
   const int kg = lane >> 4;  // which 8 of the 32 k
   const int row = rb * kRB + m;
   const bool row_ok = row < p.rows;
-  const bool c1_ok = (16 + m) < kNC;
 
   const int s0 = ks * p.steps_per_wg;
   const int s1 = min(s0 + p.steps_per_wg, p.nsteps);
+  const int kbase = s0 * kStepK;
+  const int kc = max(s1 - s0, 0) * kStepK;  // k values of this workgroup
+
+  // --- fn slice -> LDS, transposed to [logit][k] ---------------------------------
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(p.fn + (size_t)kbase * kNC);
+    const int nvec = kc * kNC / 8;  // 3 vectors per k row
+    for (int i = tid; i < nvec; i += kPreWaves * kWave) {
+      const uint4 w = src[i];
+      const int e = i * 8;
+      const int kk = e / kNC, c0 = e % kNC;  // c0 in {0, 8, 16}
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        fnT[c0 + 2 * q][kk] = (uint16_t)(u[q] & 0xFFFFu);
+        fnT[c0 + 2 * q + 1][kk] = (uint16_t)(u[q] >> 16);
+      }
+    }
+  }
+  __syncthreads();
 
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float sq = 0.f;
   const uint16_t* vrow = p.res + (size_t)(row_ok ? row : 0) * p.K;
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
   for (int s = s0 + wave; s < s1; s += kPreWaves) {
-    const int k0 = s * kStepK + kg * 8;
-    uint4 bv = make_uint4(0u, 0u, 0u, 0u);
-    if (row_ok) bv = load_nt(reinterpret_cast<const uint4*>(vrow + k0));
-    short8_t a0, a1;
-    const uint16_t* f = p.fn + (size_t)k0 * kNC;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      a0[j] = (short)f[j * kNC + m];
-      a1[j] = c1_ok ? (short)f[j * kNC + 16 + m] : (short)0;
-    }
+    const int kl = (s - s0) * kStepK + kg * 8;  // k offset inside the slice
+    uint4 bv = zero;
+    if (row_ok) bv = load_nt(reinterpret_cast<const uint4*>(vrow + kbase + kl));
+    const uint4 a0 = *reinterpret_cast<const uint4*>(&fnT[m][kl]);
+    const uint4 a1 = (16 + m < kNC) ? *reinterpret_cast<const uint4*>(&fnT[16 + m][kl]) : zero;
     const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv);
     acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), b, acc0, 0, 0, 0);
     acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), b, acc1, 0, 0, 0);
@@ -82,7 +108,6 @@ __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const Pr
   sq += __shfl_xor(sq, 16, kWave);
   sq += __shfl_xor(sq, 32, kWave);
 
-  __shared__ float red[kPreWaves][kRB][kPartW];
   // D layout: lane holds D[4*(lane/16) + i][lane % 16]: logit column 4*kg + i (+16), row m
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -96,7 +121,7 @@ __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const Pr
     float t = 0.f;
 #pragma unroll
     for (int w = 0; w < kPreWaves; ++w) t += red[w][rr][cc];
-    p.part[((size_t)ks * p.rows_pad + rb * kRB + rr) * kPartW + cc] = t;
+    p.part[((size_t)(rb * kRB + rr) * kPartW + cc) * p.ks_count + ks] = t;
   }
 }
 
@@ -108,61 +133,77 @@ struct PreEpilogueParams {
   float* post_out;     // [rows][4]
   float* comb_out;     // [rows][16]
   float rms_eps, pre_eps, sk_eps, alpha;
-  int iters, rows, K, ks_count, rows_pad;
+  int iters, rows, K, ks_count;
 };
 
 __global__ __launch_bounds__(kWave) void pre_epilogue_kernel(const PreEpilogueParams p) {
   const int r = blockIdx.x;
   const int L = threadIdx.x;
-  int col = -1;
-  if (L < 2 * kN) col = L;
-  else if (L >= 32 && L < 32 + kN * kN) col = 2 * kN + (L - 32);
-  else if (L == kWave - 1) col = kNC;  // sum of squares
-
+  // lanes 0..23: logits, lane 24: sum of squares; k-split partials are contiguous
   float acc = 0.f;
-  if (col >= 0) {
-    const float* src = p.part + (size_t)r * kPartW + col;
-    const size_t stride = (size_t)p.rows_pad * kPartW;
-    for (int k = 0; k < p.ks_count; ++k) acc += src[(size_t)k * stride];
+  if (L < kPartW) {
+    const float* src = p.part + ((size_t)r * kPartW + L) * p.ks_count;
+    constexpr int kBatch = 16;
+    for (int k0 = 0; k0 < p.ks_count; k0 += kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = (k0 + u < p.ks_count) ? src[k0 + u] : 0.f;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) acc += v[u];  // split order
+    }
   }
-  const float ss = __shfl(acc, kWave - 1, kWave);
+  const float ss = __shfl(acc, kNC, kWave);
   const float inv = 1.0f / sqrtf(ss / (float)p.K + p.rms_eps);
   float lp = 0.f;
-  if (col >= 0 && col < kNC) {
-    const int g = col < kN ? 0 : (col < 2 * kN ? 1 : 2);
-    lp = (acc * inv) * p.scale[g] + p.base[col];
+  if (L < kNC) {
+    const int g = L < kN ? 0 : (L < 2 * kN ? 1 : 2);
+    lp = (acc * inv) * __ldg(p.scale + g) + __ldg(p.base + L);
   }
   if (L < kN) {
     p.pre_out[r * kN + L] = 1.0f / (1.0f + expf(-lp)) + p.pre_eps;
   } else if (L < 2 * kN) {
     p.post_out[r * kN + (L - kN)] = p.alpha * (1.0f / (1.0f + expf(-lp)));
   }
-  // Sinkhorn over lanes 32..47 (every lane runs the shuffles; others carry dummies)
-  float mx = fmaxf(lp, __shfl_xor(lp, 1, kWave));
-  mx = fmaxf(mx, __shfl_xor(mx, 2, kWave));
-  float a = expf(lp - mx);
+  // comb: lane i (< 4) takes row i, columns j = logits 2n + 4i + j
+  float a[kN];
+  const int src_lane = 2 * kN + kN * (L & 3);
+#pragma unroll
+  for (int j = 0; j < kN; ++j) a[j] = __shfl(lp, src_lane + j, kWave);
+  float mx = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+#pragma unroll
+  for (int j = 0; j < kN; ++j) a[j] = expf(a[j] - mx);
   for (int it = 0; it < p.iters; ++it) {
-    float rs = a + __shfl_xor(a, 1, kWave);
-    rs = rs + __shfl_xor(rs, 2, kWave);
-    a = a / (rs + p.sk_eps);
-    float cs = a + __shfl_xor(a, 4, kWave);
-    cs = cs + __shfl_xor(cs, 8, kWave);
-    a = a / (cs + p.sk_eps);
+    const float rs = ((a[0] + a[1]) + a[2]) + a[3] + p.sk_eps;
+#pragma unroll
+    for (int j = 0; j < kN; ++j) a[j] = a[j] / rs;
+    float cs[kN];
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+      const float t = a[j] + __shfl_xor(a[j], 1, kWave);
+      cs[j] = t + __shfl_xor(t, 2, kWave);
+    }
+#pragma unroll
+    for (int j = 0; j < kN; ++j) a[j] = a[j] / (cs[j] + p.sk_eps);
   }
-  if (L >= 32 && L < 32 + kN * kN) p.comb_out[r * kN * kN + (L - 32)] = a;
+  if (L < kN) {
+#pragma unroll
+    for (int j = 0; j < kN; ++j) p.comb_out[r * kN * kN + L * kN + j] = a[j];
+  }
 }
 
 void pre_plan(int rows, int hidden, int* ks_count, int* steps_per_wg, int* rows_pad) {
   const int K = kN * hidden;
   const int nsteps = K / kStepK;
   const int rbn = (rows + kRB - 1) / kRB;
-  int ks = (512 / rbn) / 8 * 8;
-  const int cap = (nsteps / kPreWaves) / 8 * 8;
-  if (ks > cap) ks = cap;
-  if (ks > 256) ks = 256;
+  int ks = (kTargetWgs / rbn) / 8 * 8;
   if (ks < 8) ks = 8;
+  // every workgroup's slice must fit the LDS staging buffer
+  const int min_ks = (nsteps + kMaxStepsPerWg - 1) / kMaxStepsPerWg;
+  if (ks < min_ks) ks = (min_ks + 7) / 8 * 8;
+  int spw = (nsteps + ks - 1) / ks;
+  if (spw < 1) spw = 1;
   *ks_count = ks;
-  *steps_per_wg = (nsteps + ks - 1) / ks;
+  *steps_per_wg = spw;
   *rows_pad = rbn * kRB;
 }
 
@@ -175,6 +216,7 @@ size_t pre_scratch_floats_for(int rows, int hidden) {
 hipError_t launch_pre_coeffs(const PreLaunch& L, hipStream_t stream) {
   int ks, spw, rp;
   pre_plan(L.rows, L.hidden, &ks, &spw, &rp);
+  if (spw > kMaxStepsPerWg) return hipErrorInvalidConfiguration;
   PrePartialParams a;
   a.res = L.residual;
   a.fn = L.fn;
@@ -184,7 +226,6 @@ hipError_t launch_pre_coeffs(const PreLaunch& L, hipStream_t stream) {
   a.ks_count = ks;
   a.steps_per_wg = spw;
   a.nsteps = a.K / kStepK;
-  a.rows_pad = rp;
   const int grid = ks * (rp / kRB);
   hipLaunchKernelGGL(pre_partial_kernel, dim3(grid), dim3(kPreWaves * kWave), 0, stream, a);
   hipError_t e = hipGetLastError();
@@ -204,7 +245,6 @@ hipError_t launch_pre_coeffs(const PreLaunch& L, hipStream_t stream) {
   b.rows = L.rows;
   b.K = a.K;
   b.ks_count = ks;
-  b.rows_pad = rp;
   hipLaunchKernelGGL(pre_epilogue_kernel, dim3(L.rows), dim3(kWave), 0, stream, b);
   return hipGetLastError();
 }

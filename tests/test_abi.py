@@ -18,7 +18,7 @@ def test_header_declares_the_entry_points():
     names = binding.header_functions()
     for want in ("mhc_create", "mhc_destroy", "mhc_reset", "mhc_set_option", "mhc_boundary",
                  "mhc_residual_only", "mhc_finalize", "mhc_collapse_mean", "mhc_pre_coeffs",
-                 "mhc_status_string"):
+                 "mhc_status_string", "mhc_get_errors"):
         assert want in names
 
 
@@ -51,6 +51,7 @@ def test_create_rejects_bad_sizes_before_any_device_call():
         ((0, 4, 32, 8, 8, 0), 2), ((7, 4, 32, 8, 8, 0), 2), ((7168, 4, 0, 8, 8, 0), 2),
         ((7168, 4, 70000, 8, 8, 0), 2), ((7168, 4, 32, 0, 8, 0), 2), ((7168, 4, 32, 65, 8, 0), 2),
         ((7168, 4, 32, 8, 0, 0), 2), ((7168, 4, 32, 8, 8, -1), 2), ((7168, 2, 32, 8, 8, 0), 5),
+        ((32776, 4, 32, 8, 8, 0), 2),
     ]
     for args, want in cases:
         assert lib.mhc_create(*args, ctypes.byref(h)) == want, args
@@ -65,6 +66,7 @@ def test_null_handle_is_invalid_everywhere():
     assert lib.mhc_destroy(z) == 0
     assert lib.mhc_reset(z, z) == 1
     assert lib.mhc_set_option(z, 1, 64) == 1
+    assert lib.mhc_get_errors(z, None, 0, z) == 1
     assert lib.mhc_boundary(z, z, 1, z, z, z, z, z, 0.0, 1, z, z, z, z, z) == 1
     assert lib.mhc_residual_only(z, z, 1, z, z, z, 1, z, z) == 1
     assert lib.mhc_finalize(z, z, 1, z, z, z, z, z, z, z, z, 0.0, 1, z, z, z, z, z) == 1

@@ -96,8 +96,8 @@ def test_config3_pre_coeffs():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("rows,hidden,tp,block", [
-    (1, 512, 1, 64), (5, 1056, 3, 64), (9, 2080, 8, 128), (17, 7168, 8, 256),
-    (13, 3072, 5, 128), (8, 33 * 32, 2, 256), (3, 8 * 40, 4, 64),
+    (1, 512, 1, 128), (5, 1056, 3, 128), (9, 2080, 8, 256), (17, 7168, 8, 512),
+    (13, 3072, 5, 256), (8, 33 * 32, 2, 512), (3, 8 * 40, 4, 128),
 ])
 def test_boundary_ragged(rows, hidden, tp, block):
     mx = hidden % 32 == 0
@@ -108,7 +108,7 @@ def test_boundary_ragged(rows, hidden, tp, block):
 
 
 @pytest.mark.parametrize("rows,hidden,top_k,block", [
-    (1, 512, 1, 64), (7, 1056, 3, 128), (20, 7168, 8, 64), (4, 2048, 12, 256),
+    (1, 512, 1, 128), (7, 1056, 3, 256), (20, 7168, 8, 512), (4, 2048, 12, 256),
 ])
 def test_finalize_ragged(rows, hidden, top_k, block):
     say(f"case: finalize rows={rows} hidden={hidden} top_k={top_k} block={block}")
@@ -134,10 +134,10 @@ def test_pre_coeffs_ragged(rows, hidden, iters):
 
 
 def test_block_sizes_agree():
-    say("case: config 1 at block 64 / 128 / 256")
+    say("case: config 1 at block 128 / 256 / 512")
     d = synth.config(1)
     outs = []
-    for block in (64, 128, 256):
+    for block in (128, 256, 512):
         h = handle_for(7168, 32, tp=8, block=block)
         outs.append(gpu_boundary(h, d))
     for o in outs[1:]:
@@ -314,3 +314,88 @@ def test_reset_then_reuse():
     b = gpu_boundary(h, d)
     for k in a:
         assert np.array_equal(a[k], b[k])
+
+
+# ---------------------------------------------------------------------------
+# The row handoff: rounds, the error word, a bounded wait, graph replays
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,hidden,block", [(400, 7168, 128), (70, 32768, 256), (300, 4096, 512)])
+def test_boundary_in_several_rounds(rows, hidden, block):
+    say(f"case: boundary over several rounds rows={rows} hidden={hidden} block={block}")
+    d = synth.boundary_inputs(400 + rows, rows=rows, hidden=hidden, tp=2, mxfp8=True)
+    h = handle_for(hidden, rows, tp=2, block=block)
+    compare_boundary_outputs(gpu_boundary(h, d), oracle_boundary(d), f"rounds {rows}x{hidden}")
+    assert h.errors() == 0
+
+
+def test_no_handoff_errors_on_normal_calls():
+    say("case: error word after config 1 and config 2 calls")
+    h = handle_for(7168, 64, tp=8, top_k=8)
+    gpu_boundary(h, synth.config(1))
+    gpu_finalize(h, synth.config(2))
+    assert h.errors() == 0
+
+
+def test_zero_spin_limit_returns_and_reset_recovers():
+    """A spin limit of 0 polls once: waits may give up (counted), nothing hangs; after reset and
+    the default limit the results are right again."""
+    say("case: spin limit 0 on config 1, then reset")
+    d = synth.config(1)
+    h = handle_for(7168, 32, tp=8)
+    h.set_option(binding.MHC_OPT_SPIN_LIMIT, 0)
+    gpu_boundary(h, d)
+    n = h.errors(clear=True)
+    say(f"  waits that gave up with limit 0: {n}")
+    assert h.errors() == 0
+    h.set_option(binding.MHC_OPT_SPIN_LIMIT, 1 << 20)
+    h.reset()
+    compare_boundary_outputs(gpu_boundary(h, d), oracle_boundary(d), "after reset")
+    assert h.errors() == 0
+    with pytest.raises(binding.MhcValueError):
+        h.set_option(binding.MHC_OPT_SPIN_LIMIT, -1)
+
+
+def test_graph_replays_match_eager():
+    """One graph with a boundary, a finalize and a coefficient call, replayed three times with
+    eager work and synchronizations between the replays; every replay equals the eager run."""
+    say("case: HIP graph replays of boundary + finalize + pre_coeffs")
+    d1, d2, d3 = synth.config(1), synth.config(2), synth.config(3)
+    h = handle_for(7168, 64, tp=8, top_k=8)
+    a = {k: T(v) for k, v in d1.items() if isinstance(v, np.ndarray)}
+    b = {k: T(v) for k, v in d2.items() if isinstance(v, np.ndarray)}
+    c = {k: T(v) for k, v in d3.items() if isinstance(v, np.ndarray)}
+
+    def step():
+        o1 = binding.boundary(h, a["x_partials"], a["residual"], a["post"], a["comb"], a["pre"],
+                              a["norm_weight"], d1["eps"], mxfp8=True)
+        o2 = binding.finalize(h, b["gemm2_permuted"], b["expert_weights"],
+                              b["expanded_idx_to_permuted_idx"], b["shared_output"], b["residual"],
+                              b["post"], b["comb"], b["pre"], b["norm_weight"], d2["eps"], mxfp8=True)
+        o3 = binding.pre_coeffs(h, c["residual"], c["fn"], c["scale"], c["base"], d3["rms_eps"],
+                                d3["pre_eps"], d3["sinkhorn_eps"], d3["post_alpha"],
+                                d3["sinkhorn_iters"])
+        return [o1["residual"], o1["layer_input"], o1["mx_data"], o1["mx_scale"], o2["residual"],
+                o2["layer_input"], o2["mx_data"], o2["mx_scale"], *o3]
+
+    eager = [N(t) for t in step()]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = step()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (t, e) in enumerate(zip(outs, eager)):
+            assert np.array_equal(N(t), e), f"replay {rep}: output {i} differs from eager"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+    assert h.errors() == 0
