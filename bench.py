@@ -173,7 +173,7 @@ def main():
     h = binding.Handle(H, 4, max_rows=128, max_tp=8, top_k=8)
     if args.block:
         h.set_option(binding.MHC_OPT_BOUNDARY_BLOCK, args.block)
-    block = args.block or 256
+    block = args.block or 128
     nb = bytes_boundary(R, H, TP, pre=True, mxfp8=True)
     sets = n_sets(nb)
     base = {k: T(d1[k]) for k in ("x_partials", "residual", "post", "comb", "pre", "norm_weight")}
@@ -200,6 +200,21 @@ def main():
     del bufs
 
     if not args.no_rows:
+        # the same boundary without the MXFP8 form of the layer input
+        nb16 = bytes_boundary(R, H, TP, pre=True, mxfp8=False)
+        s1 = n_sets(nb16)
+        bufs = [{"x": base["x_partials"].clone(), "s": base["residual"].clone(),
+                 "so": torch.empty_like(base["residual"]),
+                 "li": torch.empty((R, H), dtype=torch.bfloat16, device=dev)} for _ in range(s1)]
+        calls = [(lambda b=b: binding.boundary(h, b["x"], b["s"], base["post"], base["comb"],
+                                               base["pre"], base["norm_weight"], d1["eps"],
+                                               residual_out=b["so"], layer_input_out=b["li"]))
+                 for b in bufs]
+        e, g = time_calls(torch, calls, args.steps, args.warmup)
+        rows["boundary_decode_bf16"] = row_entry("boundary_bf16", nb16, e, g, s1)
+        log(f"  bf16-only {rows['boundary_decode_bf16']}")
+        del bufs, calls
+
         # residual-only at config 1
         nro = bytes_boundary(R, H, TP, pre=False)
         s2 = n_sets(nro)

@@ -71,12 +71,12 @@ const char* mhc_status_string(int status);
  * by the model's hidden size, hc_mult, the largest row count it serves and
  * the MoE top_k, on one device. Here also by the largest number of TP
  * partial slices, max_tp.
- *   hidden   in [8, 32768], a multiple of 8 (16-byte vectors)  else MHC_ERR_SHAPE
+ *   hidden   in [8, 65536], a multiple of 8 (16-byte vectors)  else MHC_ERR_SHAPE
  *   hc_mult  == 4                                         else MHC_ERR_UNSUPPORTED
  *   max_rows in [1, 65536], max_tp in [1, 64], top_k in [1, 64]  else MHC_ERR_SHAPE
  *   device   a valid HIP device index                     else MHC_ERR_HIP
  * Allocates the handle's device scratch on `device` (hipMalloc) and zeroes it
- * (synchronously) and picks the boundary block size (256, else 512, else 128:
+ * (synchronously) and picks the boundary block size (128, else 256, else 512:
  * the first whose row fits half an XCD's resident workgroups and one polling
  * wave); MHC_ERR_UNSUPPORTED if none does. On failure *out is set to NULL.
  * The sizes are checked before any HIP call.
@@ -88,10 +88,12 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
  * mhc_set_option -- knobs of a handle. Results do not depend on them (except
  * that a spin limit too small to cover the row handoff makes it give up, see
  * above). Takes effect for calls issued afterwards.
- *   MHC_OPT_BOUNDARY_BLOCK: threads per workgroup of the boundary kernels, 128, 256 or
- *     512 (default: see mhc_create). Four threads share 8 hidden elements of a row, so
- *     a row is split into ceil(H / (2 * block)) workgroups; a size giving more than 64
- *     of them, or more than half an XCD's resident workgroups, is MHC_ERR_UNSUPPORTED.
+ *   MHC_OPT_BOUNDARY_BLOCK: threads per workgroup of the boundary kernels that write a
+ *     layer input, 128, 256 or 512 (default: see mhc_create). Each thread owns 8 hidden
+ *     elements of a row, so a row is split into ceil(H / (8 * block)) workgroups; a size
+ *     giving more than 64 of them, or more than half an XCD's resident workgroups, is
+ *     MHC_ERR_UNSUPPORTED. (The residual-only kernels use 256 threads, four per 8
+ *     elements.)
  *     Other values: MHC_ERR_SHAPE.
  *   MHC_OPT_SPIN_LIMIT: polls (each followed by a short sleep) before a row-handoff
  *     wait gives up; >= 0, default 2^20. Negative: MHC_ERR_SHAPE.

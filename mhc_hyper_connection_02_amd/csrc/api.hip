@@ -16,9 +16,9 @@ constexpr int kMaxTp = 64;
 constexpr int kMaxTopK = 64;
 constexpr int kMaxSinkhornIters = 1000;
 constexpr int kMinBlock = 128;      // smallest boundary workgroup: the most chunks per row
-constexpr int kDefaultBlock = 256;
+constexpr int kDefaultBlock = 128;
 constexpr int kMaxChunks = 64;      // one polling lane per chunk
-constexpr int kMaxHidden = 32768;   // chunks per row at the smallest block stay <= one wave
+constexpr int kMaxHidden = 65536;   // chunks per row at the largest block stay <= one wave
 constexpr int kDefaultSpinLimit = 1 << 20;
 
 }  // namespace
@@ -28,7 +28,7 @@ struct mhc_ctx {
   int slot_stride;         // handoff words per row (chunks at the smallest block)
   int block;               // boundary workgroup size in use
   int spin_limit;          // polls before a handoff wait gives up
-  int wgs_per_xcd[3];      // resident boundary workgroups per XCD at block 128 / 256 / 512
+  int wgs_per_xcd[3];      // resident layer-input workgroups per XCD at block 128 / 256 / 512
   size_t pre_floats;       // coefficient-path scratch
   void* scratch;           // one allocation: slots | pre_part | epoch | errors
   unsigned long long* slots;
@@ -50,7 +50,7 @@ inline int block_index(int block) {
 inline bool block_usable(const mhc_ctx* h, int block) {
   const int i = block_index(block);
   if (i < 0) return false;
-  const int chunks = mhc::boundary_chunks(h->hidden, block);
+  const int chunks = mhc::boundary_chunks(h->hidden, block, true);
   return chunks <= kMaxChunks && h->wgs_per_xcd[i] / 2 >= chunks;
 }
 
@@ -176,7 +176,7 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   h->device = device;
   h->block = kDefaultBlock;
   h->spin_limit = kDefaultSpinLimit;
-  h->slot_stride = mhc::boundary_chunks(hidden, kMinBlock);
+  h->slot_stride = mhc::boundary_chunks(hidden, kMinBlock, true);  // the most chunks per row
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
       cus < 8) {
@@ -188,7 +188,7 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   for (int i = 0; i < 3; ++i)
     h->wgs_per_xcd[i] = mhc::boundary_resident_wgs_per_cu(blocks[i]) * (cus / 8);
   h->block = 0;
-  for (int b : {kDefaultBlock, 512, 128}) {
+  for (int b : {kDefaultBlock, 256, 512}) {
     if (block_usable(h, b)) {
       h->block = b;
       break;

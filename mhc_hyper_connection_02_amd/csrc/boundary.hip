@@ -49,6 +49,7 @@ namespace mhc {
 
 constexpr int kHC = 4;
 constexpr int kXcds = 8;
+constexpr int kResidualOnlyBlock = 256;
 
 struct BoundaryParams {
   // sublayer output: TP partials ...
@@ -317,8 +318,225 @@ __device__ __forceinline__ void boundary_item(const BoundaryParams& p, int r, in
   }
 }
 
+// One lane per 16-byte vector: lane owns 8 elements of the row and all four streams of
+// them (BS vectors per workgroup). Same dataflow and handoff as the quad layout above.
 template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8>
-__global__ __launch_bounds__(BS) void boundary_kernel(const BoundaryParams p) {
+__device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
+                                                   const float* __restrict__ post,
+                                                   const float* __restrict__ comb,
+                                                   const float* __restrict__ pre,
+                                                   const int* __restrict__ idx,
+                                                   const float* __restrict__ ew, int r, int c,
+                                                   float* s_red, float* s_inv) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int v = c * BS + tid;
+  const bool active = v < p.hv;
+  const int va = active ? v : 0;
+
+  // the row's epoch (wave 0 runs the handoff), read by every wave without a branch, first,
+  // so that its latency hides under the data loads
+  unsigned epoch_now = 0;
+  if constexpr (HAS_PRE)
+    epoch_now = __hip_atomic_load(p.epoch + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  int pk[8];
+  float wk[8];
+  if constexpr (FINALIZE) {
+    // branch-free: slots past top_k re-read the row's last slot and are dropped by selects
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int uu = u < p.top_k ? u : p.top_k - 1;
+      const int pi = idx[r * p.top_k + uu];
+      const float w = ew[r * p.top_k + uu];
+      pk[u] = u < p.top_k ? pi : -1;
+      wk[u] = u < p.top_k ? w : 0.f;
+    }
+  }
+  float pst[kHC], cmb[kHC * kHC], pr[kHC];
+#pragma unroll
+  for (int i = 0; i < kHC; ++i) pst[i] = post[r * kHC + i];
+#pragma unroll
+  for (int i = 0; i < kHC * kHC; ++i) cmb[i] = comb[r * kHC * kHC + i];
+  if constexpr (HAS_PRE) {
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) pr[i] = pre[r * kHC + i];
+  }
+  uint4 sv[kHC];
+#pragma unroll
+  for (int j = 0; j < kHC; ++j) sv[j] = load_nt(p.res_in + ((size_t)r * kHC + j) * p.hv + va);
+  uint4 wv = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (HAS_PRE) wv = p.norm_w[va];
+
+  if constexpr (!FINALIZE) {
+    // t ascending
+    const uint4* src = p.xp + (size_t)r * p.hv + va;
+    const size_t slice = (size_t)p.rows * p.hv;
+    for (int t0 = 0; t0 < p.tp; t0 += 8) {
+      uint4 xv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (t0 + u < p.tp) xv[u] = load_nt(src + (size_t)(t0 + u) * slice);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (t0 + u < p.tp) {
+          float f[8];
+          unpack8(xv[u], f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] += f[e];
+        }
+      }
+    }
+  } else {
+    // k ascending, then the shared row
+    const uint4 shv = load_nt(p.shared + (size_t)r * p.hv + va);
+    uint4 gv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < p.top_k) {
+        const bool ok = pk[u] >= 0 && pk[u] < p.num_permuted;
+        gv[u] = load_nt(p.g + (size_t)(ok ? pk[u] : 0) * p.hv + va);
+        if (!ok) wk[u] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < p.top_k) {
+        float f[8];
+        unpack8(gv[u], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(wk[u], f[e], x[e]);
+      }
+    }
+    for (int k = 8; k < p.top_k; ++k) {  // slots beyond 8, in order
+      const int pi = idx[r * p.top_k + k];
+      const bool ok = pi >= 0 && pi < p.num_permuted;
+      const float w = ok ? ew[r * p.top_k + k] : 0.f;
+      const uint4 g = load_nt(p.g + (size_t)(ok ? pi : 0) * p.hv + va);
+      float f[8];
+      unpack8(g, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(w, f[e], x[e]);
+    }
+    float f[8];
+    unpack8(shv, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] += f[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = round_bf16(x[e]);
+
+  float s[kHC][8];
+#pragma unroll
+  for (int j = 0; j < kHC; ++j) unpack8(sv[j], s[j]);
+  float sn[kHC][8];
+  uint4* out = p.res_out + (size_t)r * kHC * p.hv + v;
+#pragma unroll
+  for (int i = 0; i < kHC; ++i) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = pst[i] * x[e];
+#pragma unroll
+      for (int j = 0; j < kHC; ++j) a = __builtin_fmaf(cmb[i * kHC + j], s[j][e], a);
+      sn[i][e] = a;
+    }
+    const uint4 o = pack8_round(sn[i]);
+    if (active) out[(size_t)i * p.hv] = o;  // the streams do not wait for the RMS
+    if constexpr (HAS_PRE) unpack8(o, sn[i]);
+  }
+  if constexpr (!HAS_PRE) return;
+
+  float y[8];
+  float sq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) a = __builtin_fmaf(pr[j], sn[j][e], a);
+    y[e] = a;
+    sq = __builtin_fmaf(a, a, sq);
+  }
+  if (!active) sq = 0.f;
+  sq = wave_sum(sq);
+  if (lane == 0) s_red[wave] = sq;
+  __syncthreads();
+  if (wave == 0) {
+    const unsigned want = epoch_now + 1u;
+    float part = 0.f;
+#pragma unroll
+    for (int w = 0; w < BS / kWave; ++w) part += s_red[w];
+    unsigned long long* row_slots = p.slots + (size_t)r * p.slot_stride;
+    if (lane == 0) {
+      const unsigned long long word = ((unsigned long long)want << 32) | __float_as_uint(part);
+      __hip_atomic_store(row_slots + c, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float val = 0.f;
+    if (lane < p.chunks) {
+      unsigned long long wd;
+      int spins = 0;
+      for (;;) {
+        wd = __hip_atomic_load(row_slots + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((unsigned)(wd >> 32) == want) break;
+        if (++spins > p.spin_limit) {
+          __hip_atomic_fetch_add(p.errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      val = __uint_as_float((unsigned)wd);
+    }
+    float tot = 0.f;
+    for (int k = 0; k < p.chunks; ++k)  // chunk order
+      tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), k));
+    if (lane == 0) {
+      *s_inv = 1.0f / sqrtf(tot / (float)p.hidden + p.eps);
+      if (c == 0) __hip_atomic_store(p.epoch + r, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+  const float inv = *s_inv;
+  float w[8], o[8];
+  unpack8(wv, w);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (y[e] * inv) * w[e];
+  const uint4 ob = pack8_round(o);
+  p.layer_out[(size_t)r * p.hv + v] = ob;
+  if constexpr (MXFP8) {
+    // 32-element block = the quad of lanes holding vectors v & ~3 .. v | 3
+    float q[8];
+    unpack8(ob, q);
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(q[e]));
+    amax = fmaxf(amax, dpp_f32<kDppQuadXor1>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
+    const int ex = e8m0_exponent(__float_as_uint(amax));
+    const float sc = __uint_as_float((uint32_t)(127 - ex) << 23);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lo |= f32_to_e4m3(q[e] * sc) << (8 * e);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hi |= f32_to_e4m3(q[4 + e] * sc) << (8 * e);
+    p.mx_data[(size_t)r * p.hv + v] = make_uint2(lo, hi);
+    if ((v & 3) == 0) p.mx_scale[(size_t)r * (p.hidden / 32) + (v >> 2)] = (uint8_t)(ex + 127);
+  }
+}
+
+template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8>
+__global__ __launch_bounds__(BS) void boundary_kernel(const BoundaryParams p,
+                                                      const float* __restrict__ post,
+                                                      const float* __restrict__ comb,
+                                                      const float* __restrict__ pre,
+                                                      const int* __restrict__ idx,
+                                                      const float* __restrict__ ew) {
+  // the layer-input kernels (with the row handoff) run one lane per vector; the
+  // residual-only kernels run four lanes per vector
+  constexpr bool QUAD = !HAS_PRE;
   __shared__ float s_red[BS / kWave];
   __shared__ float s_inv;
   const int wg = blockIdx.x;
@@ -329,7 +547,11 @@ __global__ __launch_bounds__(BS) void boundary_kernel(const BoundaryParams p) {
   for (int round = 0; round < p.rounds; ++round) {
     const int r = (round * p.rows_per_round + jr) * kXcds + xcd;
     if (r >= p.rows) break;  // uniform per workgroup; later rounds only go higher
-    boundary_item<BS, FINALIZE, HAS_PRE, MXFP8>(p, r, c, s_red, &s_inv);
+    if constexpr (QUAD)
+      boundary_item<BS, FINALIZE, HAS_PRE, MXFP8>(p, r, c, s_red, &s_inv);
+    else
+      boundary_item_lane<BS, FINALIZE, HAS_PRE, MXFP8>(p, post, comb, pre, idx, ew, r, c, s_red,
+                                                       &s_inv);
   }
 }
 
@@ -364,7 +586,8 @@ __global__ __launch_bounds__(256) void collapse_mean_kernel(const uint4* __restr
 // ---------------------------------------------------------------------------
 template <int BS, bool FIN, bool PRE, bool MX>
 static hipError_t launch_one(const BoundaryParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((boundary_kernel<BS, FIN, PRE, MX>), dim3(grid), dim3(BS), 0, st, p);
+  hipLaunchKernelGGL((boundary_kernel<BS, FIN, PRE, MX>), dim3(grid), dim3(BS), 0, st, p, p.post,
+                     p.comb, p.pre, p.idx, p.ew);
   return hipGetLastError();
 }
 
@@ -409,10 +632,10 @@ int boundary_resident_wgs_per_cu(int block) {
   }
 }
 
-int boundary_chunks(int hidden, int block) {
+int boundary_chunks(int hidden, int block, bool has_pre) {
   const int hv = hidden / 8;
-  const int groups = block / 4;  // four lanes per 16-byte vector
-  return (hv + groups - 1) / groups;
+  const int per_wg = has_pre ? block : block / 4;  // 16-byte vectors per workgroup
+  return (hv + per_wg - 1) / per_wg;
 }
 
 hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
@@ -435,7 +658,9 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   p.rows = L.rows;
   p.hidden = L.hidden;
   p.hv = L.hidden / 8;
-  p.chunks = boundary_chunks(L.hidden, L.block);
+  const bool pre = L.pre != nullptr;
+  const int block = pre ? L.block : kResidualOnlyBlock;
+  p.chunks = boundary_chunks(L.hidden, block, pre);
   p.layer_out = reinterpret_cast<uint4*>(L.layer_input_out);
   p.mx_data = reinterpret_cast<uint2*>(L.mx_data_out);
   p.mx_scale = L.mx_scale_out;
@@ -445,7 +670,6 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   p.slot_stride = L.slot_stride;
   p.spin_limit = L.spin_limit;
   const bool fin = L.gemm2_permuted != nullptr;
-  const bool pre = L.pre != nullptr;
   const bool mx = L.mx_data_out != nullptr;
   const int row_blocks = (L.rows + kXcds - 1) / kXcds;  // rows per XCD in total
   if (pre) {
@@ -462,7 +686,7 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
     p.rounds = 1;
   }
   const int grid = kXcds * p.rows_per_round * p.chunks;
-  switch (L.block) {
+  switch (block) {
     case 128: return launch_bs<128>(p, fin, pre, mx, grid, stream);
     case 256: return launch_bs<256>(p, fin, pre, mx, grid, stream);
     case 512: return launch_bs<512>(p, fin, pre, mx, grid, stream);

@@ -35,7 +35,7 @@ struct BoundaryLaunch {
   int slot_stride;
   int spin_limit;
   int max_wgs_per_xcd;          // resident workgroups of this block size on one XCD
-  int block;                    // 64, 128 or 256 threads per workgroup
+  int block;                    // 128, 256 or 512 threads per workgroup (layer-input kernels)
 };
 
 struct PreLaunch {
@@ -51,7 +51,7 @@ struct PreLaunch {
   float* part;                  // pre_scratch_floats(max_rows, hidden) floats
 };
 
-int boundary_chunks(int hidden, int block);
+int boundary_chunks(int hidden, int block, bool has_pre);
 int boundary_resident_wgs_per_cu(int block);
 hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream);
 hipError_t launch_collapse_mean(const uint16_t* streams, int rows, int hidden, uint16_t* out,

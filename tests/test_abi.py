@@ -51,7 +51,7 @@ def test_create_rejects_bad_sizes_before_any_device_call():
         ((0, 4, 32, 8, 8, 0), 2), ((7, 4, 32, 8, 8, 0), 2), ((7168, 4, 0, 8, 8, 0), 2),
         ((7168, 4, 70000, 8, 8, 0), 2), ((7168, 4, 32, 0, 8, 0), 2), ((7168, 4, 32, 65, 8, 0), 2),
         ((7168, 4, 32, 8, 0, 0), 2), ((7168, 4, 32, 8, 8, -1), 2), ((7168, 2, 32, 8, 8, 0), 5),
-        ((32776, 4, 32, 8, 8, 0), 2),
+        ((65544, 4, 32, 8, 8, 0), 2),
     ]
     for args, want in cases:
         assert lib.mhc_create(*args, ctypes.byref(h)) == want, args
