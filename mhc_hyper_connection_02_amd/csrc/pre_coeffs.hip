@@ -20,9 +20,10 @@
 //
 // Kernel 2: one wave per row. Lanes 0..24 each sum one logit's (or the sum of
 // squares') partials over the k-splits in split order, then the logits get
-// 1/RMS, scale and base; lanes 0..7 write pre and post; lanes 0..3 each hold
-// one row of the 4x4 comb matrix for the Sinkhorn iterations (row sums in
-// registers, column sums over the four lanes).
+// 1/RMS, scale and base; lanes 0..7 write pre and post; the 16 comb entries
+// run the Sinkhorn iterations in one 16-lane DPP row (row sums over quads,
+// column sums over row rotations, each normalization one reciprocal and a
+// multiply).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -51,6 +52,8 @@ struct PrePartialParams {
 __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const PrePartialParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t fnT[kNC][kMaxStepsPerWg * kStepK + kLdsPad];
   __shared__ float red[kPreWaves][kRB][kPartW];
+  constexpr int kMaxWaveSteps = kMaxStepsPerWg / kPreWaves;                  // 8
+  constexpr int kMaxFnVecs = kMaxStepsPerWg * kStepK * kNC / 8 / (kPreWaves * kWave);  // 12
 
   const int wg = blockIdx.x;
   const int ks = wg % p.ks_count;  // ks_count % 8 == 0: a k range stays on one XCD
@@ -67,16 +70,32 @@ __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const Pr
   const int s1 = min(s0 + p.steps_per_wg, p.nsteps);
   const int kbase = s0 * kStepK;
   const int kc = max(s1 - s0, 0) * kStepK;  // k values of this workgroup
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
 
-  // --- fn slice -> LDS, transposed to [logit][k] ---------------------------------
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(p.fn + (size_t)kbase * kNC);
-    const int nvec = kc * kNC / 8;  // 3 vectors per k row
-    for (int i = tid; i < nvec; i += kPreWaves * kWave) {
-      const uint4 w = src[i];
+  // --- every load first: this wave's row vectors (steps s0 + wave + 4i), then the fn slice
+  const uint16_t* vrow = p.res + (size_t)(row_ok ? row : 0) * p.K + kbase + kg * 8;
+  uint4 bv[kMaxWaveSteps];
+#pragma unroll
+  for (int i = 0; i < kMaxWaveSteps; ++i) {
+    const int sl = wave + kPreWaves * i;  // step inside the slice
+    if (s0 + sl < s1) bv[i] = row_ok ? load_nt(reinterpret_cast<const uint4*>(vrow + sl * kStepK)) : zero;
+  }
+  const uint4* src = reinterpret_cast<const uint4*>(p.fn + (size_t)kbase * kNC);
+  const int nvec = kc * kNC / 8;  // 3 vectors per k row
+  uint4 fv[kMaxFnVecs];
+#pragma unroll
+  for (int j = 0; j < kMaxFnVecs; ++j) {
+    const int i = tid + j * kPreWaves * kWave;
+    if (i < nvec) fv[j] = src[i];
+  }
+  // --- fn slice -> LDS, transposed to [logit][k]
+#pragma unroll
+  for (int j = 0; j < kMaxFnVecs; ++j) {
+    const int i = tid + j * kPreWaves * kWave;
+    if (i < nvec) {
       const int e = i * 8;
       const int kk = e / kNC, c0 = e % kNC;  // c0 in {0, 8, 16}
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+      const uint32_t u[4] = {fv[j].x, fv[j].y, fv[j].z, fv[j].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         fnT[c0 + 2 * q][kk] = (uint16_t)(u[q] & 0xFFFFu);
@@ -88,21 +107,21 @@ __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const Pr
 
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float sq = 0.f;
-  const uint16_t* vrow = p.res + (size_t)(row_ok ? row : 0) * p.K;
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-  for (int s = s0 + wave; s < s1; s += kPreWaves) {
-    const int kl = (s - s0) * kStepK + kg * 8;  // k offset inside the slice
-    uint4 bv = zero;
-    if (row_ok) bv = load_nt(reinterpret_cast<const uint4*>(vrow + kbase + kl));
-    const uint4 a0 = *reinterpret_cast<const uint4*>(&fnT[m][kl]);
-    const uint4 a1 = (16 + m < kNC) ? *reinterpret_cast<const uint4*>(&fnT[16 + m][kl]) : zero;
-    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), b, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), b, acc1, 0, 0, 0);
-    float x[8];
-    unpack8(bv, x);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sq = __builtin_fmaf(x[e], x[e], sq);
+  for (int i = 0; i < kMaxWaveSteps; ++i) {
+    const int sl = wave + kPreWaves * i;
+    if (s0 + sl < s1) {
+      const int kl = sl * kStepK + kg * 8;  // k offset inside the slice
+      const uint4 a0 = *reinterpret_cast<const uint4*>(&fnT[m][kl]);
+      const uint4 a1 = (16 + m < kNC) ? *reinterpret_cast<const uint4*>(&fnT[16 + m][kl]) : zero;
+      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv[i]);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), b, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), b, acc1, 0, 0, 0);
+      float x[8];
+      unpack8(bv[i], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq = __builtin_fmaf(x[e], x[e], sq);
+    }
   }
   // the four k groups of a row -> lanes m
   sq += __shfl_xor(sq, 16, kWave);
@@ -139,17 +158,20 @@ struct PreEpilogueParams {
 __global__ __launch_bounds__(kWave) void pre_epilogue_kernel(const PreEpilogueParams p) {
   const int r = blockIdx.x;
   const int L = threadIdx.x;
-  // lanes 0..23: logits, lane 24: sum of squares; k-split partials are contiguous
+  // lanes 0..23: logits, lane 24: sum of squares; k-split partials are contiguous, and a
+  // lane fetches a whole batch of them before adding them in split order
   float acc = 0.f;
   if (L < kPartW) {
-    const float* src = p.part + ((size_t)r * kPartW + L) * p.ks_count;
-    constexpr int kBatch = 16;
-    for (int k0 = 0; k0 < p.ks_count; k0 += kBatch) {
-      float v[kBatch];
+    const float4* src = reinterpret_cast<const float4*>(p.part + ((size_t)r * kPartW + L) * p.ks_count);
+    constexpr int kBatch = 16;  // float4 per batch: 64 splits
+    for (int b0 = 0; b0 < p.ks_count / 4; b0 += kBatch) {
+      float4 v[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) v[u] = (k0 + u < p.ks_count) ? src[k0 + u] : 0.f;
+      for (int u = 0; u < kBatch; ++u)
+        if (b0 + u < p.ks_count / 4) v[u] = src[b0 + u];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) acc += v[u];  // split order
+      for (int u = 0; u < kBatch; ++u)
+        if (b0 + u < p.ks_count / 4) acc = (((acc + v[u].x) + v[u].y) + v[u].z) + v[u].w;
     }
   }
   const float ss = __shfl(acc, kNC, kWave);
@@ -164,31 +186,23 @@ __global__ __launch_bounds__(kWave) void pre_epilogue_kernel(const PreEpiloguePa
   } else if (L < 2 * kN) {
     p.post_out[r * kN + (L - kN)] = p.alpha * (1.0f / (1.0f + expf(-lp)));
   }
-  // comb: lane i (< 4) takes row i, columns j = logits 2n + 4i + j
-  float a[kN];
-  const int src_lane = 2 * kN + kN * (L & 3);
-#pragma unroll
-  for (int j = 0; j < kN; ++j) a[j] = __shfl(lp, src_lane + j, kWave);
-  float mx = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
-#pragma unroll
-  for (int j = 0; j < kN; ++j) a[j] = expf(a[j] - mx);
+  // comb: the 16 entries sit in lanes 32..47 (one DPP row), entry (i, j) at lane 32 + 4i + j,
+  // so a row sum is two quad steps and a column sum two row rotations. Every lane runs the
+  // same instructions (lanes outside the row carry dummies).
+  const int ce = L - 32;  // entry index for lanes 32..47
+  float a = __shfl(lp, 2 * kN + (ce & 15), kWave);
+  float mx = fmaxf(a, dpp_f32<kDppQuadXor1>(a));
+  mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
+  a = expf(a - mx);
   for (int it = 0; it < p.iters; ++it) {
-    const float rs = ((a[0] + a[1]) + a[2]) + a[3] + p.sk_eps;
-#pragma unroll
-    for (int j = 0; j < kN; ++j) a[j] = a[j] / rs;
-    float cs[kN];
-#pragma unroll
-    for (int j = 0; j < kN; ++j) {
-      const float t = a[j] + __shfl_xor(a[j], 1, kWave);
-      cs[j] = t + __shfl_xor(t, 2, kWave);
-    }
-#pragma unroll
-    for (int j = 0; j < kN; ++j) a[j] = a[j] / (cs[j] + p.sk_eps);
+    float rs = a + dpp_f32<kDppQuadXor1>(a);
+    rs = rs + dpp_f32<kDppQuadXor2>(rs);
+    a = a * __builtin_amdgcn_rcpf(rs + p.sk_eps);
+    float cs = a + dpp_f32<kDppRowRor4>(a);
+    cs = cs + dpp_f32<kDppRowRor8>(cs);
+    a = a * __builtin_amdgcn_rcpf(cs + p.sk_eps);
   }
-  if (L < kN) {
-#pragma unroll
-    for (int j = 0; j < kN; ++j) p.comb_out[r * kN * kN + L * kN + j] = a[j];
-  }
+  if (ce >= 0 && ce < kN * kN) p.comb_out[r * kN * kN + ce] = a;
 }
 
 void pre_plan(int rows, int hidden, int* ks_count, int* steps_per_wg, int* rows_pad) {
