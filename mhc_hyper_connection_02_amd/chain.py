@@ -1,0 +1,147 @@
+"""One decode step's boundaries over all layers, on the library's entry points.
+
+decode page, ``SpecializedDecode.run``: the first layer enters through
+``Boundaries.first`` (the embedding broadcast to the hc streams, whose identity
+pre-mix selects stream zero); then each sublayer's output is reduced at the
+next boundary (``Boundaries.sublayer``: the fused kernel, then the coefficient
+call on the new streams), and after the last sublayer ``Boundaries.post_only``
+reduces it residual-only, followed by the streams' mean (the final collapse).
+
+The pre-mix is delayed (boundary page, ``Boundaries.sublayer`` and
+``BoundaryState``): a boundary collapses its new streams with the ``pre`` that
+the coefficient call returned at the previous boundary; the call on the new
+streams returns the post/comb of the sublayer about to run and the pre of the
+next collapse. One coefficient buffer set therefore suffices: each boundary
+reads it before the following coefficient call rewrites it, in stream order.
+
+The streams are updated in place. Every buffer is allocated up front, so
+``run`` allocates nothing and can be captured in a HIP graph. The embedding
+broadcast is a plain device copy, as it is on the pages. The sublayers'
+outputs (attention partials, unfinalized MoE outputs) are inputs here: the
+step covers the boundaries only.
+"""
+
+import torch
+
+from . import binding, synth
+
+
+class DecodeChain:
+    def __init__(self, handle, embedding, sublayers, params, device):
+        """embedding: [R,H] bf16 tensor; sublayers: list of dicts of device tensors as built by
+        :meth:`from_synth`; params: rms_eps, hc_eps, post_alpha, sinkhorn_iters, norm_eps."""
+        self.h = handle
+        self.emb = embedding
+        self.subs = sublayers
+        self.p = params
+        R, H = embedding.shape
+        self.rows, self.hidden = R, H
+        n = handle.hc_mult
+        self.streams = torch.empty((R, n, H), dtype=torch.bfloat16, device=device)
+        self.pre = torch.empty((R, n), dtype=torch.float32, device=device)
+        self.post = torch.empty((R, n), dtype=torch.float32, device=device)
+        self.comb = torch.empty((R, n, n), dtype=torch.float32, device=device)
+        self.layer_input = torch.empty((R, H), dtype=torch.bfloat16, device=device)
+        self.mx_data = torch.empty((R, H), dtype=torch.uint8, device=device)
+        self.mx_scale = torch.empty((R, H // 32), dtype=torch.uint8, device=device)
+        self.mean = torch.empty((R, H), dtype=torch.bfloat16, device=device)
+        # optional callback(index, stage, chain) around every boundary: stage "before", "after"
+        # (the boundary's outputs), "coeffs" (the coefficient call that follows it)
+        self.record = None
+
+    @classmethod
+    def from_synth(cls, device, layers=synth.CHAIN_LAYERS, rows=synth.CHAIN_ROWS,
+                   hidden=synth.CHAIN_HIDDEN, tp=synth.CHAIN_TP, top_k=synth.CHAIN_TOP_K,
+                   handle=None):
+        """The chained step on the seeded synthetic inputs (see ``synth.chain_sublayer``)."""
+        T = lambda a: synth.to_torch(a, device)  # noqa: E731
+        if handle is None:
+            handle = binding.Handle(hidden, 4, max_rows=rows, max_tp=tp, top_k=top_k,
+                                    device=device.index)
+        emb = T(synth.chain_embedding(rows, hidden))
+        subs = []
+        for layer in range(layers):
+            for ffn in (False, True):
+                d = synth.chain_sublayer(layer, ffn, rows=rows, hidden=hidden, tp=tp, top_k=top_k)
+                t = {k: T(d[k]) for k in ("fn", "scale", "base", "norm_w")}
+                t["mxfp8"] = d["mxfp8"]
+                if "partials" in d["output"]:
+                    t["partials"] = T(d["output"]["partials"])
+                else:
+                    g, w, idx, sh = d["output"]["finalize"]
+                    t["finalize"] = (T(g), T(w), T(idx), T(sh))
+                subs.append(t)
+        return cls(handle, emb, subs, synth.chain_params(), device)
+
+    def input_bytes(self):
+        tot = self.emb.numel() * 2
+        for s in self.subs:
+            for k, v in s.items():
+                if isinstance(v, torch.Tensor):
+                    tot += v.numel() * v.element_size()
+                elif isinstance(v, tuple):
+                    tot += sum(x.numel() * x.element_size() for x in v)
+        return tot
+
+    def algorithmic_bytes(self):
+        """Bytes the step must move: every boundary's and coefficient call's read-once inputs
+        and written outputs, plus the broadcast (R*n*H written, R*H read) and the mean."""
+        R, H, n = self.rows, self.hidden, self.h.hc_mult
+        nc = 2 * n + n * n
+        coef = R * (n + n + n * n) * 4
+        tot = R * H * 2 + R * n * H * 2                      # broadcast
+        pre_call = R * n * H * 2 + n * H * nc * 2 + (3 + nc) * 4 + coef
+        tot += pre_call                                       # first coefficients
+        for i, s in enumerate(self.subs):
+            last = i + 1 == len(self.subs)
+            nxt = None if last else self.subs[i + 1]
+            b = 2 * R * n * H * 2 + coef                      # streams in/out + mixes
+            if "partials" in s:
+                b += s["partials"].numel() * 2
+            else:
+                g, w, idx, sh = s["finalize"]
+                b += R * self.h.top_k * (H * 2 + 8) + R * H * 2
+            if not last:
+                b += H * 2 + R * H * 2                        # norm weight, layer input
+                if nxt["mxfp8"]:
+                    b += R * H + R * H // 32
+                b += pre_call
+            tot += b
+        tot += R * n * H * 2 + R * H * 2                      # mean-collapse
+        return tot
+
+    def run(self):
+        """One decode step: broadcast, coefficients, 122 boundaries, final reduction, mean."""
+        h, p = self.h, self.p
+        self.streams.copy_(self.emb.unsqueeze(1).expand_as(self.streams))
+        first = self.subs[0]
+        binding.pre_coeffs(h, self.streams, first["fn"], first["scale"], first["base"],
+                           p["rms_eps"], p["hc_eps"], p["hc_eps"], p["post_alpha"],
+                           p["sinkhorn_iters"], out=(self.pre, self.post, self.comb))
+        for i, s in enumerate(self.subs):
+            last = i + 1 == len(self.subs)
+            nxt = None if last else self.subs[i + 1]
+            kw = {}
+            if not last:
+                kw = dict(pre=self.pre, norm_weight=nxt["norm_w"], eps=p["norm_eps"],
+                          mxfp8=nxt["mxfp8"], layer_input_out=self.layer_input,
+                          mx_out=(self.mx_data, self.mx_scale) if nxt["mxfp8"] else None)
+            if self.record is not None:
+                self.record(i, "before", self)
+            if "partials" in s:
+                binding.boundary(h, s["partials"], self.streams, self.post, self.comb,
+                                 residual_out=self.streams, **kw)
+            else:
+                g, w, idx, sh = s["finalize"]
+                binding.finalize(h, g, w, idx, sh, self.streams, self.post, self.comb,
+                                 residual_out=self.streams, **kw)
+            if self.record is not None:
+                self.record(i, "after", self)
+            if not last:
+                binding.pre_coeffs(h, self.streams, nxt["fn"], nxt["scale"], nxt["base"],
+                                   p["rms_eps"], p["hc_eps"], p["hc_eps"], p["post_alpha"],
+                                   p["sinkhorn_iters"], out=(self.pre, self.post, self.comb))
+                if self.record is not None:
+                    self.record(i, "coeffs", self)
+        binding.collapse_mean(h, self.streams, out=self.mean)
+        return self.mean
