@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused mHC boundary µs/call + achieved HBM GB/s (rows=32, hidden=7168, hc=4)"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
+COPY_CALIBRATION_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "boundary_decode_r32_h7168_traffic.json")
 KERNEL_SOURCES = ["boundary.hip", "device_common.h"]
 
@@ -43,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-rows", action="store_true", help="time only the headline call")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 256 MiB, --steps times (to scale "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     return ap.parse_args()
 
 
@@ -163,6 +167,17 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     T = lambda a: synth.to_torch(a, dev)  # noqa: E731
+
+    if args.copy_calibration:
+        n = COPY_CALIBRATION_BYTES
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": args.steps}), flush=True)
+        return
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)

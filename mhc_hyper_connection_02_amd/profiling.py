@@ -1,0 +1,97 @@
+"""Summaries of rocprofv3 output (CSV format) for the kernels of this library.
+
+  python -m mhc_hyper_connection_02_amd.profiling stats <trace_dir> --cmd "<command>"
+      per-kernel dispatch count and duration from a ``--kernel-trace --stats`` run
+  python -m mhc_hyper_connection_02_amd.profiling traffic --fetch <dir> --write <dir>
+      --cal-fetch <dir> --cal-write <dir> --cal-bytes N --kernel <substring>
+      --block B --source-hash H --cmd "<commands>" --out <json>
+      HBM bytes per launch of one kernel from two ``--pmc`` runs (FETCH_SIZE, then
+      WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a
+      plain device copy of cal-bytes bytes.
+
+Nothing here touches the GPU; it only reads the CSV files rocprofv3 wrote.
+"""
+
+import argparse
+import collections
+import csv
+import glob
+import json
+import os
+import sys
+
+
+def _find(d, suffix):
+    hits = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def kernel_stats(trace_dir):
+    """[(name, calls, avg_ns, min_ns, max_ns)] from the kernel trace, longest total first."""
+    rows = list(csv.DictReader(open(_find(trace_dir, "kernel_trace.csv"))))
+    agg = collections.defaultdict(list)
+    for r in rows:
+        agg[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = [(k, len(v), sum(v) / len(v), min(v), max(v)) for k, v in agg.items()]
+    return sorted(out, key=lambda t: -t[1] * t[2])
+
+
+def counter_mean(pmc_dir, counter, kernel_substring):
+    """Mean per-dispatch value of a counter over the dispatches of kernels matching."""
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(_find(pmc_dir, "counter_collection.csv")))
+            if r["Counter_Name"] == counter and kernel_substring in r["Kernel_Name"]]
+    if not vals:
+        raise ValueError(f"no {counter} samples for kernels matching {kernel_substring!r}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("trace_dir")
+    s.add_argument("--cmd", required=True)
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "cal_fetch", "cal_write", "kernel", "source_hash", "cmd", "out"):
+        t.add_argument("--" + k.replace("_", "-"), required=True)
+    t.add_argument("--cal-bytes", type=int, required=True)
+    t.add_argument("--block", type=int, required=True)
+    a = ap.parse_args(argv)
+
+    if a.what == "stats":
+        print(f"# rocprofv3 kernel trace: per-dispatch duration\n# command: {a.cmd}\n")
+        print(f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}  kernel")
+        for name, n, avg, mn, mx in kernel_stats(a.trace_dir):
+            print(f"{n:6d} {avg / 1e3:9.3f} {mn / 1e3:9.3f} {mx / 1e3:9.3f}  {name}")
+        return 0
+
+    fk, nf = counter_mean(a.fetch, "FETCH_SIZE", a.kernel)
+    wk, nw = counter_mean(a.write, "WRITE_SIZE", a.kernel)
+    cf, _ = counter_mean(a.cal_fetch, "FETCH_SIZE", "copyBuffer")
+    cw, _ = counter_mean(a.cal_write, "WRITE_SIZE", "copyBuffer")
+    sf = a.cal_bytes / (cf * 1024.0)
+    sw = a.cal_bytes / (cw * 1024.0)
+    res = {
+        "kernel": a.kernel, "block": a.block, "source_hash": a.source_hash,
+        "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+        "dispatches": [nf, nw],
+        "copy_calibration": {"bytes": a.cal_bytes, "fetch_kib": round(cf, 1),
+                             "write_kib": round(cw, 1), "fetch_scale": round(sf, 4),
+                             "write_scale": round(sw, 4)},
+        "hbm_read_bytes_per_launch": int(fk * 1024 * sf),
+        "hbm_write_bytes_per_launch": int(wk * 1024 * sw),
+        "hbm_bytes_per_launch": int(fk * 1024 * sf + wk * 1024 * sw),
+        "commands": a.cmd,
+    }
+    with open(a.out, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    json.dump(res, sys.stdout, indent=1)
+    print()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
