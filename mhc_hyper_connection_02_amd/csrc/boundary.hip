@@ -5,19 +5,21 @@
 // (BoundaryAllReduce.__call__ / finalize). The arithmetic of each step is
 // stated in include/mhc.h.
 //
-// Work decomposition. A row (token) is split into `chunks` pieces of
-// 2 * BS bf16 elements; one workgroup of BS threads owns one (row, chunk).
-// Four consecutive lanes (a quad) own one 16-byte vector (8 elements) of the
-// row: lane q loads stream q and a quarter of the sublayer output (slices or
-// gathered expert rows q, q+4, ...), the quad combines its partial sums and
-// exchanges the streams over DPP quad permutations, and lane q then computes
-// and stores output stream q and two elements of the layer input. Spreading
-// a vector over four lanes gives four times the waves of one lane per vector
-// for the same bytes, which keeps the per-wave arithmetic (it runs after the
-// loads land) short. A lane issues all of its loads before the first use.
-// It stores its stream as soon as it is computed, overlapping the loads of
-// the rest of the row; only the layer input (and its MXFP8 form) waits for
-// the row's RMS.
+// Work decomposition. A row (token) is split into `chunks` pieces; one
+// workgroup of BS threads owns one (row, chunk). Two layouts:
+//  - kernels that write a layer input: one lane per 16-byte vector (8 hidden
+//    elements). The lane loads the vector's partial slices (or gathered expert
+//    rows), its four streams and its norm weights, computes the four new
+//    streams, the collapse and its share of the row's sum of squares; BS
+//    vectors per workgroup.
+//  - residual-only kernels: four lanes (a quad) per vector. Lane q loads stream
+//    q and a quarter of the sublayer output, the quad combines its partial sums
+//    and exchanges the streams over DPP quad permutations, and lane q computes
+//    and stores stream q; BS / 4 vectors per workgroup, so four times the waves
+//    for the same bytes and a quarter of the per-lane arithmetic.
+// A lane issues all of its loads before the first use and stores its new
+// streams as soon as they are computed; only the layer input (and its MXFP8
+// form) waits for the row's RMS.
 //
 // The row RMS. The RMS needs the whole row, and a row spans several
 // workgroups. Each workgroup publishes its partial sum of y^2 as ONE 64-bit
@@ -83,28 +85,18 @@ struct BoundaryParams {
   int spin_limit;
 };
 
-// Pick element i (0..3) of four values by a lane-dependent index (register selects).
-__device__ __forceinline__ float pick4(float a0, float a1, float a2, float a3, int i) {
-  return i == 0 ? a0 : (i == 1 ? a1 : (i == 2 ? a2 : a3));
-}
-
-template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8>
-__device__ __forceinline__ void boundary_item(const BoundaryParams& p, int r, int c, float* s_red,
-                                              float* s_inv) {
+// Residual-only, four lanes per 16-byte vector: lane q loads stream q and a quarter
+// of the sublayer output (slices or expert slots q, q+4, ...), the quad combines its
+// partial sums and exchanges the streams over DPP quad permutations, and lane q
+// computes and stores output stream q (BS / 4 vectors per workgroup).
+template <int BS, bool FINALIZE>
+__device__ __forceinline__ void boundary_item_quad(const BoundaryParams& p, int r, int c) {
   constexpr int kGroups = BS / 4;  // 16-byte vectors (8 elements) per workgroup
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
   const int q = tid & 3;                     // this lane's output stream
   const int v = c * kGroups + (tid >> 2);    // the quad's 16-byte vector index in the row
   const bool active = v < p.hv;
   const int va = active ? v : 0;             // an in-bounds vector for every lane's loads
-
-  // the row's epoch, read first by every lane so that its latency hides under the data
-  // loads (only wave 0 uses it, at the handoff)
-  unsigned epoch_now = 0;
-  if constexpr (HAS_PRE)
-    epoch_now = __hip_atomic_load(p.epoch + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // --- loads, all issued before any use; every address is in bounds, so no load sits
   //     behind a branch and results of the lanes or slots that do not count are dropped
@@ -124,15 +116,13 @@ __device__ __forceinline__ void boundary_item(const BoundaryParams& p, int r, in
       wk[u] = in ? p.ew[r * p.top_k + k] : 0.f;
     }
   }
+  // this lane's mixes: post_q and cq[d] = comb[q][q ^ d], the weight of the stream
+  // that a xor-d quad move brings
   const float post_q = p.post[r * kHC + q];
-  float cq[kHC];  // cq[d] = comb[q][q ^ d], the weight of the stream a xor-d quad move brings
+  float cq[kHC];
 #pragma unroll
-  for (int d = 0; d < kHC; ++d) cq[d] = p.comb[r * kHC * kHC + q * kHC + (q ^ d)];
-  float pre_q = 0.f;
-  if constexpr (HAS_PRE) pre_q = p.pre[r * kHC + q];
+  for (int d = 0; d < kHC; ++d) cq[d] = p.comb[(r * kHC + q) * kHC + (q ^ d)];
   const uint4 sv = load_nt(p.res_in + ((size_t)r * kHC + q) * p.hv + va);
-  uint32_t wv = 0;
-  if constexpr (HAS_PRE) wv = reinterpret_cast<const uint32_t*>(p.norm_w)[(size_t)va * 4 + q];
 
   if constexpr (!FINALIZE) {
     // lane q sums slices t = q, q+4, q+8, ... (ascending)
@@ -203,8 +193,8 @@ __device__ __forceinline__ void boundary_item(const BoundaryParams& p, int r, in
   for (int e = 0; e < 8; ++e) {
     x[e] += dpp_f32<kDppQuadXor1>(x[e]);
     x[e] += dpp_f32<kDppQuadXor2>(x[e]);
-    x[e] = round_bf16(x[e]);  // the reduced output is a bf16 tensor
   }
+  round8_bf16(x);  // the reduced output is a bf16 tensor
 
   // --- mHC post for stream q: s'_q = post_q x + sum_j comb_qj s_j -------------------
   uint4 sj[kHC];
@@ -222,100 +212,7 @@ __device__ __forceinline__ void boundary_item(const BoundaryParams& p, int r, in
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(cq[d], f[e], o[e]);
   }
-  const uint4 so = pack8_round(o);
-  // the new streams do not depend on the RMS: store them now, overlapping the loads of
-  // the rest of the row
-  if (active) p.res_out[((size_t)r * kHC + q) * p.hv + v] = so;
-
-  float y2[2] = {0.f, 0.f};  // this lane's two elements of the collapse: 2q, 2q+1
-  float sq = 0.f;
-  if constexpr (HAS_PRE) {
-    // y = sum_j pre_j s'_j over the quad, on the bf16 streams
-    float f[8], y[8];
-    unpack8(so, f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      y[e] = pre_q * f[e];
-      y[e] += dpp_f32<kDppQuadXor1>(y[e]);
-      y[e] += dpp_f32<kDppQuadXor2>(y[e]);
-    }
-    y2[0] = pick4(y[0], y[2], y[4], y[6], q);
-    y2[1] = pick4(y[1], y[3], y[5], y[7], q);
-    // lanes past the row's end loaded an in-bounds stand-in vector: they add nothing
-    sq = active ? __builtin_fmaf(y2[0], y2[0], y2[1] * y2[1]) : 0.f;
-
-    // --- the row's sum of squares: workgroup partial, then the handoff ------------
-    sq = wave_sum(sq);
-    if (lane == 0) s_red[wave] = sq;
-    __syncthreads();
-    if (wave == 0) {
-      const unsigned want = epoch_now + 1u;
-      float part = 0.f;
-#pragma unroll
-      for (int w = 0; w < BS / kWave; ++w) part += s_red[w];
-      unsigned long long* row_slots = p.slots + (size_t)r * p.slot_stride;
-      if (lane == 0) {
-        const unsigned long long word = ((unsigned long long)want << 32) | __float_as_uint(part);
-        __hip_atomic_store(row_slots + c, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      float val = 0.f;
-      if (lane < p.chunks) {
-        unsigned long long wd;
-        int spins = 0;
-        for (;;) {
-          wd = __hip_atomic_load(row_slots + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if ((unsigned)(wd >> 32) == want) break;
-          if (++spins > p.spin_limit) {
-            __hip_atomic_fetch_add(p.errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        val = __uint_as_float((unsigned)wd);
-      }
-      float tot = 0.f;
-      for (int k = 0; k < p.chunks; ++k)  // chunk order
-        tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), k));
-      if (lane == 0) {
-        *s_inv = 1.0f / sqrtf(tot / (float)p.hidden + p.eps);
-        if (c == 0) __hip_atomic_store(p.epoch + r, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
-  }
-
-  // --- stores -----------------------------------------------------------------------
-  uint32_t ob = 0;
-  float q2[2] = {0.f, 0.f};
-  if constexpr (HAS_PRE) {
-    const float inv = *s_inv;
-    const float l0 = (y2[0] * inv) * bf16_lo(wv);
-    const float l1 = (y2[1] * inv) * bf16_hi(wv);
-    ob = pack2_bits(f32_to_bf16_bits(l0), f32_to_bf16_bits(l1));
-    q2[0] = bf16_lo(ob);
-    q2[1] = bf16_hi(ob);
-  }
-  float amax = 0.f;
-  if constexpr (MXFP8) {
-    // a 32-element block = 4 vectors = the 16 lanes of one DPP row (hidden % 32 == 0,
-    // so rows are wholly active or inactive)
-    amax = fmaxf(fabsf(q2[0]), fabsf(q2[1]));
-    amax = fmaxf(amax, dpp_f32<kDppQuadXor1>(amax));
-    amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
-    amax = fmaxf(amax, dpp_f32<kDppRowRor4>(amax));
-    amax = fmaxf(amax, dpp_f32<kDppRowRor8>(amax));
-  }
-  if (!active) return;
-  if constexpr (HAS_PRE) {
-    reinterpret_cast<uint32_t*>(p.layer_out)[((size_t)r * p.hv + v) * 4 + q] = ob;
-    if constexpr (MXFP8) {
-      const int ex = e8m0_exponent(__float_as_uint(amax));
-      const float sc = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-e, exact
-      const uint32_t codes = f32_to_e4m3(q2[0] * sc) | (f32_to_e4m3(q2[1] * sc) << 8);
-      reinterpret_cast<uint16_t*>(p.mx_data)[((size_t)r * p.hv + v) * 4 + q] = (uint16_t)codes;
-      if ((lane & 15) == 0) p.mx_scale[(size_t)r * (p.hidden / 32) + (v >> 2)] = (uint8_t)(ex + 127);
-    }
-  }
+  if (active) p.res_out[((size_t)r * kHC + q) * p.hv + v] = pack8_round(o);
 }
 
 // One lane per 16-byte vector: lane owns 8 elements of the row and all four streams of
@@ -427,8 +324,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] += f[e];
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = round_bf16(x[e]);
+  round8_bf16(x);  // the reduced output is a bf16 tensor
 
   float s[kHC][8];
 #pragma unroll
@@ -517,11 +413,9 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
     const int ex = e8m0_exponent(__float_as_uint(amax));
     const float sc = __uint_as_float((uint32_t)(127 - ex) << 23);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) lo |= f32_to_e4m3(q[e] * sc) << (8 * e);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) hi |= f32_to_e4m3(q[4 + e] * sc) << (8 * e);
+    // |q| * 2^-e <= 448 by the choice of e: in range, exact scaling
+    const uint32_t lo = cvt_pk4_e4m3(q[0] * sc, q[1] * sc, q[2] * sc, q[3] * sc);
+    const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
     p.mx_data[(size_t)r * p.hv + v] = make_uint2(lo, hi);
     if ((v & 3) == 0) p.mx_scale[(size_t)r * (p.hidden / 32) + (v >> 2)] = (uint8_t)(ex + 127);
   }
@@ -536,7 +430,6 @@ __global__ __launch_bounds__(BS) void boundary_kernel(const BoundaryParams p,
                                                       const float* __restrict__ ew) {
   // the layer-input kernels (with the row handoff) run one lane per vector; the
   // residual-only kernels run four lanes per vector
-  constexpr bool QUAD = !HAS_PRE;
   __shared__ float s_red[BS / kWave];
   __shared__ float s_inv;
   const int wg = blockIdx.x;
@@ -547,8 +440,8 @@ __global__ __launch_bounds__(BS) void boundary_kernel(const BoundaryParams p,
   for (int round = 0; round < p.rounds; ++round) {
     const int r = (round * p.rows_per_round + jr) * kXcds + xcd;
     if (r >= p.rows) break;  // uniform per workgroup; later rounds only go higher
-    if constexpr (QUAD)
-      boundary_item<BS, FINALIZE, HAS_PRE, MXFP8>(p, r, c, s_red, &s_inv);
+    if constexpr (!HAS_PRE)
+      boundary_item_quad<BS, FINALIZE>(p, r, c);
     else
       boundary_item_lane<BS, FINALIZE, HAS_PRE, MXFP8>(p, post, comb, pre, idx, ew, r, c, s_red,
                                                        &s_inv);

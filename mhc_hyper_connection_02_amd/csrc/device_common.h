@@ -1,7 +1,8 @@
 // Device helpers shared by the gfx950 kernels: bf16 / E4M3 / E8M0 conversions
-// and wave-level reductions. All conversions are exact bit manipulations of
-// the format definitions (bf16: 8 significant bits in fp32's exponent range;
-// OCP E4M3 "FN": bias 7, 3 fraction bits, max 448, subnormal step 2^-9).
+// and wave-level reductions. Narrowing to bf16 (8 significant bits in fp32's
+// exponent range) and to OCP E4M3 "FN" (bias 7, 3 fraction bits, max 448,
+// subnormal step 2^-9) runs on gfx950's packed conversion instructions, round
+// to nearest even; widening and the E8M0 exponent are bit manipulations.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,19 +23,6 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest, ties to even. Inputs are finite by
-// construction; a NaN is kept quiet.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ __forceinline__ float round_bf16(float f) {
-  return __uint_as_float(f32_to_bf16_bits(f) << 16);
-}
-
 // Eight bf16 values packed in a 16-byte vector <-> eight floats.
 __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
   f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
@@ -43,37 +31,38 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
   f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
-__device__ __forceinline__ uint32_t pack2_bits(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (lo in bits 0..15), round to nearest even, in one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 // Round eight floats to bf16 and pack them.
 __device__ __forceinline__ uint4 pack8_round(const float (&f)[8]) {
   uint4 v;
-  v.x = pack2_bits(f32_to_bf16_bits(f[0]), f32_to_bf16_bits(f[1]));
-  v.y = pack2_bits(f32_to_bf16_bits(f[2]), f32_to_bf16_bits(f[3]));
-  v.z = pack2_bits(f32_to_bf16_bits(f[4]), f32_to_bf16_bits(f[5]));
-  v.w = pack2_bits(f32_to_bf16_bits(f[6]), f32_to_bf16_bits(f[7]));
+  v.x = cvt_pk_bf16(f[0], f[1]);
+  v.y = cvt_pk_bf16(f[2], f[3]);
+  v.z = cvt_pk_bf16(f[4], f[5]);
+  v.w = cvt_pk_bf16(f[6], f[7]);
   return v;
 }
 
-// E4M3 (FN) code of a finite float, nearest-even; |f| >= 448 saturates to 0x7E.
-// Below 2^-6 the code is the subnormal count round(|f| * 2^9) (8 is the
-// smallest normal); above, the fp32 fraction is rounded to 3 bits and the
-// exponent re-biased from 127 to 7.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x43E00000u) {            // 448.0
-    code = 0x7Eu;
-  } else if (a < 0x3C800000u) {      // 2^-6
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);  // exact scaling, RNE
-  } else {
-    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;     // exponent:3-bit fraction, RNE
-    code = r - ((127u - 7u) << 3);
-    if (code > 0x7Eu) code = 0x7Eu;
-  }
-  return code | sign;
+// Round eight floats to bf16 precision in place (they stay floats).
+__device__ __forceinline__ void round8_bf16(float (&f)[8]) {
+  unpack8(pack8_round(f), f);
+}
+
+// Four floats -> four OCP E4M3 (FN) codes (byte i = f[i]), round to nearest even,
+// in two v_cvt_pk_fp8_f32. Inputs must be finite with |f| <= 448 (the E8M0 scale
+// guarantees it), where no saturation or NaN case arises; below 2^-6 the codes are
+// the subnormals.
+__device__ __forceinline__ uint32_t cvt_pk4_e4m3(float f0, float f1, float f2, float f3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, lo, true);
 }
 
 // E8M0 block exponent e of a non-negative finite amax given as fp32 bits:
