@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--no-chain", action="store_true", help="skip the 61-layer chained step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-rows", action="store_true", help="time only the headline call")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="skip the eager timing loops (profiled runs: dispatches are then the "
+                         "graph replays that the reported numbers time)")
+    ap.add_argument("--chain-only", action="store_true",
+                    help="run only the chained decode step and print its row")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 256 MiB, --steps times (to scale "
@@ -86,20 +91,26 @@ def bytes_mean(rows, hidden, n=4):
 # timing
 # ---------------------------------------------------------------------------
 
+GRAPH_ONLY = False
+
+
 def time_calls(torch, calls, steps, warmup):
-    """calls: list of zero-argument launchers, one per buffer set; call i uses set i % len."""
+    """calls: list of zero-argument launchers, one per buffer set; call i uses set i % len.
+    Returns (eager, graph) microseconds per call; eager is None under --graph-only."""
     nset = len(calls)
     for i in range(warmup):
         calls[i % nset]()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(steps):
-        calls[i % nset]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1)
+    eager_ms = None
+    if not GRAPH_ONLY:
+        e0.record(stream)
+        for i in range(steps):
+            calls[i % nset]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1)
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -114,7 +125,8 @@ def time_calls(torch, calls, steps, warmup):
     torch.cuda.synchronize()
     graph_ms = e0.elapsed_time(e1)
     del g
-    return eager_ms / steps * 1e3, graph_ms / steps * 1e3  # us per call
+    eager_us = None if eager_ms is None else eager_ms / steps * 1e3
+    return eager_us, graph_ms / steps * 1e3  # us per call
 
 
 def n_sets(bytes_per_set):
@@ -124,7 +136,8 @@ def n_sets(bytes_per_set):
 def row_entry(name, nbytes, us_eager, us_graph, sets):
     us = us_graph
     gbs = nbytes / (us * 1e-6) / 1e9
-    return {"us_per_call": round(us, 3), "us_per_call_eager": round(us_eager, 3),
+    return {"us_per_call": round(us, 3),
+            "us_per_call_eager": None if us_eager is None else round(us_eager, 3),
             "algorithmic_bytes": int(nbytes), "gb_per_s": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "buffer_sets": sets}
 
@@ -179,8 +192,29 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": args.steps}), flush=True)
         return
 
+    global GRAPH_ONLY
+    GRAPH_ONLY = args.graph_only
+
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
+
+    def chain_row():
+        from mhc_hyper_connection_02_amd import chain as chain_mod
+        log("chain: generating 122 sublayers of synthetic inputs")
+        t0 = time.time()
+        step = chain_mod.DecodeChain.from_synth(dev)
+        log(f"  inputs ready in {time.time() - t0:.1f} s ({step.input_bytes() / 1e9:.2f} GB)")
+        us_e, us_g = time_calls(torch, [step.run], max(3, args.steps // 40), 2)
+        row = {"us_per_step": round(us_g, 1),
+               "us_per_step_eager": None if us_e is None else round(us_e, 1),
+               "algorithmic_bytes": int(step.algorithmic_bytes()),
+               "gb_per_s": round(step.algorithmic_bytes() / us_g / 1e3, 1)}
+        log(f"  chain {row}")
+        return row
+
+    if args.chain_only:
+        print(json.dumps({"rows": {"chain_decode_step": chain_row()}}), flush=True)
+        return
 
     # --- headline: config 1, decode boundary + MXFP8 --------------------------------
     R, H, TP = 32, 7168, 8
@@ -296,18 +330,7 @@ def main():
         del bufs, calls
 
     if not args.no_chain and not args.no_rows:
-        from mhc_hyper_connection_02_amd import chain as chain_mod
-        log("chain: generating 122 sublayers of synthetic inputs")
-        t0 = time.time()
-        step = chain_mod.DecodeChain.from_synth(dev)
-        log(f"  inputs ready in {time.time() - t0:.1f} s ({step.input_bytes() / 1e9:.2f} GB)")
-        us_e, us_g = time_calls(torch, [step.run], max(3, args.steps // 40), 2)
-        rows["chain_decode_step"] = {"us_per_step": round(us_g, 1),
-                                     "us_per_step_eager": round(us_e, 1),
-                                     "algorithmic_bytes": int(step.algorithmic_bytes()),
-                                     "gb_per_s": round(step.algorithmic_bytes() / us_g / 1e3, 1)}
-        log(f"  chain {rows['chain_decode_step']}")
-        del step
+        rows["chain_decode_step"] = chain_row()
 
     head = rows["boundary_decode_mxfp8"]
     us = head["us_per_call"]

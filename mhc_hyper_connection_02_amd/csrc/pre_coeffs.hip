@@ -158,6 +158,10 @@ struct PreEpilogueParams {
 __global__ __launch_bounds__(kWave) void pre_epilogue_kernel(const PreEpilogueParams p) {
   const int r = blockIdx.x;
   const int L = threadIdx.x;
+  // this lane's scale and base first, so that they arrive with the partials
+  const int Lc = L < kNC ? L : kNC - 1;
+  const float sc_l = p.scale[Lc < kN ? 0 : (Lc < 2 * kN ? 1 : 2)];
+  const float base_l = p.base[Lc];
   // lanes 0..23: logits, lane 24: sum of squares; k-split partials are contiguous, and a
   // lane fetches a whole batch of them before adding them in split order
   float acc = 0.f;
@@ -177,10 +181,7 @@ __global__ __launch_bounds__(kWave) void pre_epilogue_kernel(const PreEpiloguePa
   const float ss = __shfl(acc, kNC, kWave);
   const float inv = 1.0f / sqrtf(ss / (float)p.K + p.rms_eps);
   float lp = 0.f;
-  if (L < kNC) {
-    const int g = L < kN ? 0 : (L < 2 * kN ? 1 : 2);
-    lp = (acc * inv) * __ldg(p.scale + g) + __ldg(p.base + L);
-  }
+  if (L < kNC) lp = (acc * inv) * sc_l + base_l;
   if (L < kN) {
     p.pre_out[r * kN + L] = 1.0f / (1.0f + expf(-lp)) + p.pre_eps;
   } else if (L < 2 * kN) {

@@ -29,12 +29,17 @@ def _find(d, suffix):
 
 
 def kernel_stats(trace_dir):
-    """[(name, calls, avg_ns, min_ns, max_ns)] from the kernel trace, longest total first."""
+    """[(name, calls, avg_ns, median_ns, min_ns, max_ns)] from the kernel trace, longest
+    total first."""
     rows = list(csv.DictReader(open(_find(trace_dir, "kernel_trace.csv"))))
     agg = collections.defaultdict(list)
     for r in rows:
         agg[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    out = [(k, len(v), sum(v) / len(v), min(v), max(v)) for k, v in agg.items()]
+    out = []
+    for k, v in agg.items():
+        v = sorted(v)
+        med = v[len(v) // 2] if len(v) % 2 else (v[len(v) // 2 - 1] + v[len(v) // 2]) / 2
+        out.append((k, len(v), sum(v) / len(v), med, v[0], v[-1]))
     return sorted(out, key=lambda t: -t[1] * t[2])
 
 
@@ -62,9 +67,9 @@ def main(argv=None):
 
     if a.what == "stats":
         print(f"# rocprofv3 kernel trace: per-dispatch duration\n# command: {a.cmd}\n")
-        print(f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}  kernel")
-        for name, n, avg, mn, mx in kernel_stats(a.trace_dir):
-            print(f"{n:6d} {avg / 1e3:9.3f} {mn / 1e3:9.3f} {mx / 1e3:9.3f}  {name}")
+        print(f"{'calls':>6} {'avg_us':>9} {'median_us':>9} {'min_us':>9} {'max_us':>9}  kernel")
+        for name, n, avg, med, mn, mx in kernel_stats(a.trace_dir):
+            print(f"{n:6d} {avg / 1e3:9.3f} {med / 1e3:9.3f} {mn / 1e3:9.3f} {mx / 1e3:9.3f}  {name}")
         return 0
 
     fk, nf = counter_mean(a.fetch, "FETCH_SIZE", a.kernel)

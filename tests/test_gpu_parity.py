@@ -136,6 +136,51 @@ def test_pre_coeffs_ragged(rows, hidden, iters):
         assert_f32_close(N(a), b, f"{name} rows={rows} hidden={hidden}")
 
 
+def _pre_call(h, d, iters=None):
+    it = d["sinkhorn_iters"] if iters is None else iters
+    got = binding.pre_coeffs(h, T(d["residual"]), T(d["fn"]), T(d["scale"]), T(d["base"]),
+                             d["rms_eps"], d["pre_eps"], d["sinkhorn_eps"], d["post_alpha"], it)
+    torch.cuda.synchronize()
+    return [N(a) for a in got]
+
+
+def _pre_oracle(d, iters=None):
+    it = d["sinkhorn_iters"] if iters is None else iters
+    return oracle.pre_coeffs(d["residual"], d["fn"], d["scale"], d["base"], d["rms_eps"],
+                             d["pre_eps"], d["sinkhorn_eps"], d["post_alpha"], it)
+
+
+def test_pre_coeffs_row_counts_change_between_calls():
+    """One handle, calls whose split layouts differ (16-row tiles x k-splits: 4x64, 8x32,
+    1x256, 19x8) in one scratch area; a repeated call is bit-identical."""
+    say("case: pre_coeffs rows 64, 128, 5, 300, 64 on one handle, hidden=7168")
+    h = handle_for(7168, 300)
+    first = None
+    for rows in (64, 128, 5, 300, 64):
+        d = synth.pre_inputs(500 + rows, rows=rows, hidden=7168)
+        d["sinkhorn_iters"] = 20
+        got = _pre_call(h, d)
+        for name, a, b in zip(("pre", "post", "comb"), got, _pre_oracle(d)):
+            assert_f32_close(a, b, f"{name} rows={rows}")
+        if rows == 64:
+            if first is None:
+                first = got
+            else:  # the same call again: bit-identical (fixed split order)
+                for a, b in zip(got, first):
+                    assert np.array_equal(a, b)
+    assert h.errors() == 0
+
+
+@pytest.mark.parametrize("rows,hidden", [(4096, 512), (1000, 7168)])
+def test_pre_coeffs_large_row_counts(rows, hidden):
+    say(f"case: pre_coeffs rows={rows} hidden={hidden}")
+    d = synth.pre_inputs(600 + rows, rows=rows, hidden=hidden)
+    h = handle_for(hidden, rows)
+    for name, a, b in zip(("pre", "post", "comb"), _pre_call(h, d, 20), _pre_oracle(d, 20)):
+        assert_f32_close(a, b, f"{name} rows={rows} hidden={hidden}")
+    assert h.errors() == 0
+
+
 def test_block_sizes_agree():
     say("case: config 1 at block 128 / 256 / 512")
     d = synth.config(1)
@@ -312,11 +357,17 @@ def test_reset_then_reuse():
     say("case: mhc_reset between calls")
     d = synth.config(0)
     h = handle_for(1024, 4, tp=2)
+    d3 = synth.pre_inputs(7, rows=4, hidden=1024)
+    d3["sinkhorn_iters"] = 20
     a = gpu_boundary(h, d)
+    pa = _pre_call(h, d3)
     h.reset()
     b = gpu_boundary(h, d)
+    pb = _pre_call(h, d3)
     for k in a:
         assert np.array_equal(a[k], b[k])
+    for x, y in zip(pa, pb):
+        assert np.array_equal(x, y)
 
 
 # ---------------------------------------------------------------------------
@@ -337,6 +388,7 @@ def test_no_handoff_errors_on_normal_calls():
     h = handle_for(7168, 64, tp=8, top_k=8)
     gpu_boundary(h, synth.config(1))
     gpu_finalize(h, synth.config(2))
+    _pre_call(h, synth.config(3))
     assert h.errors() == 0
 
 
