@@ -263,11 +263,13 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
 #pragma unroll
     for (int i = 0; i < kHC; ++i) pr[i] = pre[r * kHC + i];
   }
+  // the norm weight first: it is shared by every row, so it mostly hits in L2, and issued
+  // ahead of the streaming loads it is back before them (measured: 0.2 us per call)
+  uint4 wv = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (HAS_PRE) wv = p.norm_w[va];
   uint4 sv[kHC];
 #pragma unroll
   for (int j = 0; j < kHC; ++j) sv[j] = load_nt(p.res_in + ((size_t)r * kHC + j) * p.hv + va);
-  uint4 wv = make_uint4(0u, 0u, 0u, 0u);
-  if constexpr (HAS_PRE) wv = p.norm_w[va];
 
   if constexpr (!FINALIZE) {
     // t ascending
