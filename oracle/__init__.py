@@ -41,6 +41,8 @@ from .mhc import (  # noqa: F401
     finalize,
     residual_only,
     collapse_mean,
+    first,
+    collapse_norm,
     sinkhorn,
     pre_coeffs,
     decode_chain,

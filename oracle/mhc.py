@@ -171,6 +171,43 @@ def collapse_mean(streams_bits):
     return f64_to_bf16_bits(s.mean(axis=1))
 
 
+def _with_mxfp8(out, mxfp8):
+    if mxfp8:
+        out["mx_data"], out["mx_scale"] = mxfp8_quantize(out["layer_input"])
+    return out
+
+
+def first(x_bits, norm_weight_bits, eps, hc_mult=4, mxfp8=False):
+    """The first layer's entry: the embedding broadcast to the hc streams, and the first
+    sublayer's input.
+
+    boundary page, ``Boundaries.first``: the residual is the embedding x repeated over the
+    hc streams, and the identity pre-mix selects stream zero, so the collapse is x itself
+    and the layer input is x RMS-normalized with the sublayer's norm (``Boundaries._pre``
+    receives x and the attention norm). Returns {"residual": [R,n,H] bf16 bits,
+    "layer_input": [R,H] bf16 bits} (and "mx_data", "mx_scale" with ``mxfp8``).
+    """
+    x = np.asarray(x_bits, dtype=np.uint16)
+    out = {"residual": np.repeat(x[:, None, :], hc_mult, axis=1),
+           "layer_input": rms_norm(bf16_bits_to_f64(x), norm_weight_bits, eps)}
+    return _with_mxfp8(out, mxfp8)
+
+
+def collapse_norm(streams_bits, pre, norm_weight_bits, eps, mxfp8=False):
+    """The head after the layers: the streams collapsed with the last pre-mix, then the
+    final norm.
+
+    decode page, ``_head`` (after ``Boundaries.post_only``): the hc streams are collapsed
+    with ``state.pre`` into one hidden state, which the backbone's final norm normalizes.
+    Reading: there the collapse is its own op and materializes a bf16 tensor, so y is
+    rounded to bf16 once before the norm (inside the fused boundary, y goes straight into
+    the norm). Returns {"layer_input": [R,H] bf16 bits} (and the MXFP8 pair with
+    ``mxfp8``).
+    """
+    y = bf16_bits_to_f64(f64_to_bf16_bits(collapse(streams_bits, pre)))
+    return _with_mxfp8({"layer_input": rms_norm(y, norm_weight_bits, eps)}, mxfp8)
+
+
 # ----------------------------------------------------------------------------
 # mhc_pre: the next coefficients
 # ----------------------------------------------------------------------------

@@ -196,6 +196,74 @@ def test_layer_input_scale_invariance_of_premix():
     assert np.array_equal(a["layer_input"], b["layer_input"])
 
 
+# ---------------------------------------------------------------------------
+# The first layer's entry and the head
+# ---------------------------------------------------------------------------
+
+def test_first_broadcasts_and_normalizes_the_embedding():
+    """Streams: x in every stream, bit for bit. Layer input: closed forms of RMSNorm(x)
+    (rows of +-c normalize to +-1 without eps, whatever c), equal to the boundary's layer
+    input with comb = I, post = 0, pre = e0 on those streams, and MXFP8 of it."""
+    R, H = 3, 64
+    alt = np.where(np.arange(H) % 2 == 0, 1.0, -1.0)
+    x = bf(np.stack([2.5 * alt, -0.125 * alt, 96.0 * alt]))
+    w = bf(np.ones(H))
+    out = oracle.first(x, w, 0.0, mxfp8=True)
+    assert out["residual"].shape == (R, 4, H)
+    for i in range(4):
+        assert np.array_equal(out["residual"][:, i], x)
+    assert np.array_equal(dec(out["layer_input"]), np.stack([alt, -alt, alt]))
+    codes, scales = codecs.mxfp8_quantize(out["layer_input"])
+    assert np.array_equal(out["mx_data"], codes) and np.array_equal(out["mx_scale"], scales)
+    rng = np.random.default_rng(5)
+    x = bf(rng.normal(0, 1, (R, H)))
+    w = bf(rng.normal(1, 0.1, H))
+    eye = np.broadcast_to(np.eye(4, dtype=np.float32), (R, 4, 4)).copy()
+    pre = np.zeros((R, 4), np.float32)
+    pre[:, 0] = 1.0
+    b = oracle.boundary(bf(np.zeros((1, R, H))), np.repeat(x[:, None, :], 4, axis=1),
+                        np.zeros((R, 4), np.float32), eye, pre, w, 1e-6)
+    assert np.array_equal(oracle.first(x, w, 1e-6)["layer_input"], b["layer_input"])
+
+
+def test_collapse_norm_closed_forms_and_invariances():
+    """Constant streams c_j: y = sum_j pre_j c_j per row, normalized to sign(y) * w without
+    eps; a power-of-two scale of every stream changes nothing (eps = 0); pre = e0 reduces
+    the head to the first layer's normalization of stream 0."""
+    R, H = 2, 32
+    c = np.array([[1.0, -2.0, 0.5, 4.0], [-3.0, 1.0, 1.0, -1.0]])
+    s = bf(np.repeat(c[:, :, None], H, axis=2))
+    pre = np.array([[0.25, 0.5, 1.0, 0.125], [1.0, 0.5, 0.5, 2.0]], np.float32)
+    w = bf(np.linspace(0.5, 1.5, H))
+    y = (pre.astype(np.float64) * c).sum(axis=1)          # 0.25, -4.0
+    got = dec(oracle.collapse_norm(s, pre, w, 0.0)["layer_input"])
+    assert np.array_equal(got, np.sign(y)[:, None] * dec(w)[None, :])
+    rng = np.random.default_rng(6)
+    s = bf(rng.normal(0, 1, (3, 4, H)))
+    pre = rng.uniform(0.1, 1.0, (3, 4)).astype(np.float32)
+    a = oracle.collapse_norm(s, pre, w, 0.0, mxfp8=True)
+    b = oracle.collapse_norm(bf(dec(s) * 2.0 ** -7), pre, w, 0.0, mxfp8=True)
+    for k in a:
+        assert np.array_equal(a[k], b[k])
+    e0 = np.zeros((3, 4), np.float32)
+    e0[:, 0] = 1.0
+    assert np.array_equal(oracle.collapse_norm(s, e0, w, 1e-6)["layer_input"],
+                          oracle.first(s[:, 0], w, 1e-6)["layer_input"])
+
+
+def test_collapse_norm_rounds_the_collapse_once_before_the_norm():
+    """y = [1.453125 + 2^-9, 0.90625] is not a bf16 number; the head normalizes its bf16
+    rounding [1.453125, 0.90625] (ties to even), which decides the second output: 0.75,
+    where normalizing the unrounded y would give 0.74609375 (worked out by hand: mean(y^2)
+    = (1.453125^2 + 0.90625^2) / 2 = 1.4664306640625, and 0.90625 / sqrt of that
+    = 0.74836..., which rounds to 0.75; with the unrounded y it is 0.74772... -> 0.74609375)."""
+    s = bf(np.array([[[1.453125, 0.90625], [2.0 ** -9, 0.0], [0.0, 0.0], [0.0, 0.0]]]))
+    pre = np.array([[1.0, 1.0, 0.0, 0.0]], np.float32)
+    w = bf(np.ones(2))
+    got = dec(oracle.collapse_norm(s, pre, w, 0.0)["layer_input"])
+    assert np.array_equal(got, np.array([[1.203125, 0.75]]))
+
+
 def test_residual_only_streams_equal_full_boundary_streams():
     d = _tiny_boundary()
     full = oracle.boundary(d["x_partials"], d["residual"], d["post"], d["comb"], d["pre"],
