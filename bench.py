@@ -87,6 +87,17 @@ def bytes_mean(rows, hidden, n=4):
     return rows * n * hidden * 2 + rows * hidden * 2
 
 
+def bytes_first(rows, hidden, n=4, mxfp8=False):
+    """Embedding read, norm weight, n streams and the layer input written (+ MXFP8)."""
+    b = rows * hidden * 2 + hidden * 2 + rows * n * hidden * 2 + rows * hidden * 2
+    return b + (rows * hidden + rows * hidden // 32 if mxfp8 else 0)
+
+
+def bytes_collapse_norm(rows, hidden, n=4):
+    """Streams and pre read, norm weight, the normalized collapse written."""
+    return rows * n * hidden * 2 + rows * n * 4 + hidden * 2 + rows * hidden * 2
+
+
 # ---------------------------------------------------------------------------
 # timing
 # ---------------------------------------------------------------------------
@@ -315,6 +326,37 @@ def main():
         e, g = time_calls(torch, calls, args.steps, args.warmup)
         rows["pre_coeffs"] = row_entry("pre_coeffs", npb, e, g, s4)
         log(f"  pre_coeffs {rows['pre_coeffs']}")
+        del bufs, calls
+
+        # the first layer's entry at the decode boundary's 32 rows, with MXFP8
+        nfi = bytes_first(R, H, mxfp8=True)
+        s6 = n_sets(nfi)
+        emb = T(synth.chain_embedding(R, H))
+        bufs = [{"x": emb.clone(), "so": torch.empty((R, 4, H), dtype=torch.bfloat16, device=dev),
+                 "li": torch.empty((R, H), dtype=torch.bfloat16, device=dev),
+                 "md": torch.empty((R, H), dtype=torch.uint8, device=dev),
+                 "ms": torch.empty((R, H // 32), dtype=torch.uint8, device=dev)}
+                for _ in range(s6)]
+        calls = [(lambda b=b: binding.first(h, b["x"], base["norm_weight"], d1["eps"], mxfp8=True,
+                                            residual_out=b["so"], layer_input_out=b["li"],
+                                            mx_out=(b["md"], b["ms"]))) for b in bufs]
+        e, g = time_calls(torch, calls, args.steps, args.warmup)
+        rows["first_decode_mxfp8"] = row_entry("first", nfi, e, g, s6)
+        log(f"  first {rows['first_decode_mxfp8']}")
+        del bufs, calls
+
+        # the head (collapse with the last pre-mix + final norm) at the chained step's 128 rows
+        nhd = bytes_collapse_norm(128, H)
+        s7 = n_sets(nhd)
+        dh = synth.boundary_inputs(7, rows=128, hidden=H, tp=1)
+        sh, ph, wh = T(dh["residual"]), T(dh["pre"]), T(dh["norm_weight"])
+        bufs = [{"s": sh.clone(), "o": torch.empty((128, H), dtype=torch.bfloat16, device=dev)}
+                for _ in range(s7)]
+        calls = [(lambda b=b: binding.collapse_norm(h, b["s"], ph, wh, dh["eps"], out=b["o"]))
+                 for b in bufs]
+        e, g = time_calls(torch, calls, args.steps, args.warmup)
+        rows["collapse_norm_r128"] = row_entry("collapse_norm", nhd, e, g, s7)
+        log(f"  collapse_norm {rows['collapse_norm_r128']}")
         del bufs, calls
 
         # mean-collapse at the chained step's 128 rows

@@ -26,10 +26,11 @@
  *     epochs for the row RMS, an error word, coefficient partials). Calls on
  *     one handle must be serialized, i.e. issued on one stream or ordered by
  *     the caller; two overlapping calls on one handle race on its scratch.
- *   - The boundary kernels with a layer input (pre != NULL) finish each
- *     row's RMS by a bounded wait between the workgroups of that row, which
- *     the library keeps co-resident (a launch uses at most a quarter of the
- *     device's resident-workgroup capacity, in rounds if needed). A wait that
+ *   - The kernels that write a layer input (mhc_boundary and mhc_finalize with
+ *     pre, mhc_first, mhc_collapse_norm) finish each row's RMS by a bounded
+ *     wait between the workgroups of that row, which the library keeps
+ *     co-resident (a launch uses at most half of the device's
+ *     resident-workgroup capacity, in rounds if needed). A wait that
  *     exceeds the spin limit gives up, counts itself in the handle's error
  *     word (see mhc_get_errors) and the call's layer input is then wrong;
  *     nothing hangs.
@@ -201,6 +202,41 @@ int mhc_finalize(mhc_handle h, const uint16_t* gemm2_permuted, int num_permuted,
  */
 int mhc_collapse_mean(mhc_handle h, const uint16_t* streams, int rows, uint16_t* out,
                       mhc_stream_t stream);
+
+/*
+ * mhc_first -- the first layer's entry: the embedding broadcast to the hc
+ * streams and the first sublayer's input.
+ *
+ * boundary page, Boundaries.first: the residual streams are the embedding x
+ * repeated over the hc streams, and the identity pre-mix selects stream zero,
+ * so the layer input is x normalized with the sublayer's norm:
+ *   residual_out[r, i, :] = x[r, :]                     (bit for bit, every i)
+ *   layer[r, h] = bf16( x[r,h] * (mean_h x[r]^2 + eps)^(-1/2) * w[h] )
+ * and the optional MXFP8 form as for mhc_boundary. The coefficients of the
+ * first sublayer come from mhc_pre_coeffs on residual_out.
+ *   x [R, H] bf16;  norm_weight [H] bf16;  eps >= 0
+ *   residual_out [R, n, H] bf16 (must not overlap x);  layer_input_out [R, H] bf16
+ *   mx_data_out, mx_scale_out: both NULL or both set (hidden % 32 == 0)
+ */
+int mhc_first(mhc_handle h, const uint16_t* x, const uint16_t* norm_weight, float eps, int rows,
+              uint16_t* residual_out, uint16_t* layer_input_out, uint8_t* mx_data_out,
+              uint8_t* mx_scale_out, mhc_stream_t stream);
+
+/*
+ * mhc_collapse_norm -- the head after the layers: the streams collapsed with
+ * the last pre-mix, then the final norm.
+ *
+ * decode page, _head (after Boundaries.post_only): the collapse is its own op
+ * there, so it is rounded to bf16 once before the norm:
+ *   y[r, h]   = bf16( sum_j pre[r, j] * s[r, j, h] )
+ *   out[r, h] = bf16( y * (mean_h y^2 + eps)^(-1/2) * w[h] )
+ * and the optional MXFP8 form as for mhc_boundary.
+ *   residual [R, n, H] bf16 (read only);  pre [R, n] fp32;  norm_weight [H] bf16
+ *   out [R, H] bf16;  mx_data_out, mx_scale_out: both NULL or both set
+ */
+int mhc_collapse_norm(mhc_handle h, const uint16_t* residual, const float* pre,
+                      const uint16_t* norm_weight, float eps, int rows, uint16_t* out,
+                      uint8_t* mx_data_out, uint8_t* mx_scale_out, mhc_stream_t stream);
 
 /*
  * mhc_pre_coeffs -- the next sublayer's mHC coefficients from the streams.

@@ -42,6 +42,8 @@ _SIGS = {
     "mhc_finalize": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _i, _vp, _vp,
                       _vp, _vp, _vp], _i),
     "mhc_collapse_mean": ([_vp, _vp, _i, _vp, _vp], _i),
+    "mhc_first": ([_vp, _vp, _vp, _f, _i, _vp, _vp, _vp, _vp, _vp], _i),
+    "mhc_collapse_norm": ([_vp, _vp, _vp, _vp, _f, _i, _vp, _vp, _vp, _vp], _i),
     "mhc_pre_coeffs": ([_vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f, _i, _i, _vp, _vp, _vp, _vp], _i),
 }
 
@@ -276,6 +278,68 @@ def collapse_mean(h, streams, out=None, stream=None):
     _check(load_library().mhc_collapse_mean(h.ptr, _ptr(streams), rows, _ptr(out), _stream(stream)),
            "mhc_collapse_mean")
     return out
+
+
+def _layer_outputs(h, rows, dev, mxfp8, layer_input_out, mx_out):
+    hidden = h.hidden
+    if layer_input_out is None:
+        layer_input_out = torch.empty((rows, hidden), dtype=torch.bfloat16, device=dev)
+    _need(layer_input_out, "layer_input_out", torch.bfloat16, (rows, hidden), dev)
+    mx_data = mx_scale = None
+    if mxfp8:
+        if mx_out is None:
+            mx_out = (torch.empty((rows, hidden), dtype=torch.uint8, device=dev),
+                      torch.empty((rows, hidden // 32), dtype=torch.uint8, device=dev))
+        mx_data, mx_scale = mx_out
+        _need(mx_data, "mx_data_out", torch.uint8, (rows, hidden), dev)
+        _need(mx_scale, "mx_scale_out", torch.uint8, (rows, hidden // 32), dev)
+    elif mx_out is not None:
+        raise ValueError("mx_out given without mxfp8=True")
+    return layer_input_out, mx_data, mx_scale
+
+
+def first(h, x, norm_weight, eps, mxfp8=False, residual_out=None, layer_input_out=None,
+          mx_out=None, stream=None):
+    """``mhc_first``: embedding [rows, hidden] -> dict(residual [rows, n, hidden] (x in every
+    stream), layer_input, mx_data?, mx_scale?)."""
+    if x.dim() != 2 or x.shape[1] != h.hidden:
+        raise ValueError(f"x must be [rows, {h.hidden}]")
+    rows, dev = x.shape[0], x.device
+    _need(x, "x", torch.bfloat16, (rows, h.hidden), dev)
+    _need(norm_weight, "norm_weight", torch.bfloat16, (h.hidden,), dev)
+    if residual_out is None:
+        residual_out = torch.empty((rows, h.hc_mult, h.hidden), dtype=torch.bfloat16, device=dev)
+    _need(residual_out, "residual_out", torch.bfloat16, (rows, h.hc_mult, h.hidden), dev)
+    li, md, ms = _layer_outputs(h, rows, dev, mxfp8, layer_input_out, mx_out)
+    st = load_library().mhc_first(h.ptr, _ptr(x), _ptr(norm_weight), float(eps), rows,
+                                  _ptr(residual_out), _ptr(li), _ptr(md), _ptr(ms),
+                                  _stream(stream))
+    _check(st, "mhc_first")
+    return _result(residual_out, li, md, ms)
+
+
+def collapse_norm(h, residual, pre, norm_weight, eps, mxfp8=False, out=None, mx_out=None,
+                  stream=None):
+    """``mhc_collapse_norm``: streams [rows, n, hidden] and pre [rows, n] -> dict(layer_input
+    [rows, hidden], mx_data?, mx_scale?)."""
+    if residual.dim() != 3:
+        raise ValueError("residual must be [rows, hc_mult, hidden]")
+    rows, n, hidden = residual.shape
+    dev = residual.device
+    if n != h.hc_mult or hidden != h.hidden:
+        raise ValueError("residual does not fit the handle")
+    _need(residual, "residual", torch.bfloat16, (rows, n, hidden), dev)
+    _need(pre, "pre", torch.float32, (rows, n), dev)
+    _need(norm_weight, "norm_weight", torch.bfloat16, (hidden,), dev)
+    li, md, ms = _layer_outputs(h, rows, dev, mxfp8, out, mx_out)
+    st = load_library().mhc_collapse_norm(h.ptr, _ptr(residual), _ptr(pre), _ptr(norm_weight),
+                                          float(eps), rows, _ptr(li), _ptr(md), _ptr(ms),
+                                          _stream(stream))
+    _check(st, "mhc_collapse_norm")
+    res = {"layer_input": li}
+    if md is not None:
+        res["mx_data"], res["mx_scale"] = md, ms
+    return res
 
 
 def pre_coeffs(h, residual, fn, scale, base, rms_eps, pre_eps, sinkhorn_eps, post_alpha,

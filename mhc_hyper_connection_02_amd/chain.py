@@ -1,8 +1,9 @@
 """One decode step's boundaries over all layers, on the library's entry points.
 
 decode page, ``SpecializedDecode.run``: the first layer enters through
-``Boundaries.first`` (the embedding broadcast to the hc streams, whose identity
-pre-mix selects stream zero); then each sublayer's output is reduced at the
+``Boundaries.first`` (``mhc_first``: the embedding broadcast to the hc streams, whose
+identity pre-mix selects stream zero, and the first sublayer's normalized input, then
+the coefficient call on the broadcast streams); then each sublayer's output is reduced at the
 next boundary (``Boundaries.sublayer``: the fused kernel, then the coefficient
 call on the new streams), and after the last sublayer ``Boundaries.post_only``
 reduces it residual-only, followed by the streams' mean (the final collapse).
@@ -15,8 +16,7 @@ next collapse. One coefficient buffer set therefore suffices: each boundary
 reads it before the following coefficient call rewrites it, in stream order.
 
 The streams are updated in place. Every buffer is allocated up front, so
-``run`` allocates nothing and can be captured in a HIP graph. The embedding
-broadcast is a plain device copy, as it is on the pages. The sublayers'
+``run`` allocates nothing and can be captured in a HIP graph. The sublayers'
 outputs (attention partials, unfinalized MoE outputs) are inputs here: the
 step covers the boundaries only.
 """
@@ -46,7 +46,8 @@ class DecodeChain:
         self.mx_scale = torch.empty((R, H // 32), dtype=torch.uint8, device=device)
         self.mean = torch.empty((R, H), dtype=torch.bfloat16, device=device)
         # optional callback(index, stage, chain) around every boundary: stage "before", "after"
-        # (the boundary's outputs), "coeffs" (the coefficient call that follows it)
+        # (the boundary's outputs), "coeffs" (the coefficient call that follows it); and once
+        # with index -1, stage "first", after the first layer's entry
         self.record = None
 
     @classmethod
@@ -89,7 +90,9 @@ class DecodeChain:
         R, H, n = self.rows, self.hidden, self.h.hc_mult
         nc = 2 * n + n * n
         coef = R * (n + n + n * n) * 4
-        tot = R * H * 2 + R * n * H * 2                      # broadcast
+        tot = R * H * 2 + R * n * H * 2 + H * 2 + R * H * 2   # first: broadcast, layer input
+        if self.subs[0]["mxfp8"]:
+            tot += R * H + R * H // 32
         pre_call = R * n * H * 2 + n * H * nc * 2 + (3 + nc) * 4 + coef
         tot += pre_call                                       # first coefficients
         for i, s in enumerate(self.subs):
@@ -111,10 +114,15 @@ class DecodeChain:
         return tot
 
     def run(self):
-        """One decode step: broadcast, coefficients, 122 boundaries, final reduction, mean."""
+        """One decode step: the first layer's entry, coefficients, 122 boundaries, final
+        reduction, mean."""
         h, p = self.h, self.p
-        self.streams.copy_(self.emb.unsqueeze(1).expand_as(self.streams))
         first = self.subs[0]
+        binding.first(h, self.emb, first["norm_w"], p["norm_eps"], mxfp8=first["mxfp8"],
+                      residual_out=self.streams, layer_input_out=self.layer_input,
+                      mx_out=(self.mx_data, self.mx_scale) if first["mxfp8"] else None)
+        if self.record is not None:
+            self.record(-1, "first", self)
         binding.pre_coeffs(h, self.streams, first["fn"], first["scale"], first["base"],
                            p["rms_eps"], p["hc_eps"], p["hc_eps"], p["post_alpha"],
                            p["sinkhorn_iters"], out=(self.pre, self.post, self.comb))

@@ -48,7 +48,7 @@ inline int block_index(int block) {
 
 // Whether a handle may run the boundary at this block size: a row's chunks fit the
 // polling wave and half of an XCD's resident workgroups (a launch then spans rows
-// in rounds of at most a quarter of the XCD, or one row when a row needs more).
+// in rounds of at most half of the XCD).
 inline bool block_usable(const mhc_ctx* h, int block) {
   const int i = block_index(block);
   if (i < 0) return false;
@@ -352,6 +352,54 @@ int mhc_finalize(mhc_handle h, const uint16_t* gemm2_permuted, int num_permuted,
   L.top_k = h->top_k;
   fill_mix(h, L, true, residual, post, comb, pre, norm_weight, norm_eps, rows, residual_out,
            layer_input_out, mx_data_out, mx_scale_out);
+  return launch_status(mhc::launch_boundary(L, static_cast<hipStream_t>(stream)));
+}
+
+int mhc_first(mhc_handle h, const uint16_t* x, const uint16_t* norm_weight, float norm_eps,
+              int rows, uint16_t* residual_out, uint16_t* layer_input_out, uint8_t* mx_data_out,
+              uint8_t* mx_scale_out, mhc_stream_t stream) {
+  if (!h) return MHC_ERR_INVALID_ARG;
+  if (rows < 0) return MHC_ERR_SHAPE;
+  if (rows > h->max_rows) return MHC_ERR_LIMIT;
+  if (rows == 0) return MHC_OK;
+  if (!x || !norm_weight || !residual_out || !layer_input_out) return MHC_ERR_INVALID_ARG;
+  if ((mx_data_out == nullptr) != (mx_scale_out == nullptr)) return MHC_ERR_INVALID_ARG;
+  if (mx_data_out && (h->hidden % 32) != 0) return MHC_ERR_UNSUPPORTED;
+  if (!(norm_eps >= 0.0f)) return MHC_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(norm_weight, 16) || !aligned(residual_out, 16) ||
+      !aligned(layer_input_out, 16) || (mx_data_out && !aligned(mx_data_out, 8)))
+    return MHC_ERR_ALIGN;
+  int st = check_device(h);
+  if (st != MHC_OK) return st;
+  mhc::BoundaryLaunch L = {};
+  fill_mix(h, L, false, nullptr, nullptr, nullptr, nullptr, norm_weight, norm_eps, rows,
+           residual_out, layer_input_out, mx_data_out, mx_scale_out);
+  L.x_partials = x;
+  L.tp = 1;
+  L.mode = mhc::kBoundaryFirst;
+  return launch_status(mhc::launch_boundary(L, static_cast<hipStream_t>(stream)));
+}
+
+int mhc_collapse_norm(mhc_handle h, const uint16_t* residual, const float* pre,
+                      const uint16_t* norm_weight, float norm_eps, int rows, uint16_t* out,
+                      uint8_t* mx_data_out, uint8_t* mx_scale_out, mhc_stream_t stream) {
+  if (!h) return MHC_ERR_INVALID_ARG;
+  if (rows < 0) return MHC_ERR_SHAPE;
+  if (rows > h->max_rows) return MHC_ERR_LIMIT;
+  if (rows == 0) return MHC_OK;
+  if (!residual || !pre || !norm_weight || !out) return MHC_ERR_INVALID_ARG;
+  if ((mx_data_out == nullptr) != (mx_scale_out == nullptr)) return MHC_ERR_INVALID_ARG;
+  if (mx_data_out && (h->hidden % 32) != 0) return MHC_ERR_UNSUPPORTED;
+  if (!(norm_eps >= 0.0f)) return MHC_ERR_SHAPE;
+  if (!aligned(residual, 16) || !aligned(pre, 4) || !aligned(norm_weight, 16) ||
+      !aligned(out, 16) || (mx_data_out && !aligned(mx_data_out, 8)))
+    return MHC_ERR_ALIGN;
+  int st = check_device(h);
+  if (st != MHC_OK) return st;
+  mhc::BoundaryLaunch L = {};
+  fill_mix(h, L, false, residual, nullptr, nullptr, pre, norm_weight, norm_eps, rows, nullptr,
+           out, mx_data_out, mx_scale_out);
+  L.mode = mhc::kBoundaryHead;
   return launch_status(mhc::launch_boundary(L, static_cast<hipStream_t>(stream)));
 }
 

@@ -34,12 +34,13 @@
 // in device memory, so graph replays stay correct.
 //
 // Co-residency. Polling requires all workgroups of a row to be resident at
-// once. The host sizes the grid to at most a quarter of the device's
-// resident-workgroup capacity (or one row per XCD when a row needs more, at
-// most half of it) and, for larger row counts, walks the rows in rounds: in round k, workgroup w handles one (row, chunk) of a block of
-// rows that the grid covers entirely, so every row's chunks are live
-// together. The wait is bounded (spin_limit polls with s_sleep); a timeout
-// is counted in the handle's error word and the workgroup goes on.
+// once. The host sizes the grid to at most half of the device's
+// resident-workgroup capacity (the other half stays free for other streams'
+// kernels) and, for larger row counts, walks the rows in rounds: in round k,
+// workgroup w handles one (row, chunk) of a block of rows that the grid covers
+// entirely, so every row's chunks are live together. The wait is bounded
+// (spin_limit polls with s_sleep); a timeout is counted in the handle's error
+// word and the workgroup goes on.
 //
 // XCD placement. Consecutive workgroup ids are dealt round-robin to the 8
 // XCDs, so a row's chunks get ids congruent to the row mod 8: all
@@ -217,7 +218,7 @@ __device__ __forceinline__ void boundary_item_quad(const BoundaryParams& p, int 
 
 // One lane per 16-byte vector: lane owns 8 elements of the row and all four streams of
 // them (BS vectors per workgroup). Same dataflow and handoff as the quad layout above.
-template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8>
+template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8, int MODE>
 __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
                                                    const float* __restrict__ post,
                                                    const float* __restrict__ comb,
@@ -255,11 +256,13 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     }
   }
   float pst[kHC], cmb[kHC * kHC], pr[kHC];
+  if constexpr (MODE == kBoundaryMix) {
 #pragma unroll
-  for (int i = 0; i < kHC; ++i) pst[i] = post[r * kHC + i];
+    for (int i = 0; i < kHC; ++i) pst[i] = post[r * kHC + i];
 #pragma unroll
-  for (int i = 0; i < kHC * kHC; ++i) cmb[i] = comb[r * kHC * kHC + i];
-  if constexpr (HAS_PRE) {
+    for (int i = 0; i < kHC * kHC; ++i) cmb[i] = comb[r * kHC * kHC + i];
+  }
+  if constexpr (HAS_PRE && MODE != kBoundaryFirst) {
 #pragma unroll
     for (int i = 0; i < kHC; ++i) pr[i] = pre[r * kHC + i];
   }
@@ -268,10 +271,18 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   uint4 wv = make_uint4(0u, 0u, 0u, 0u);
   if constexpr (HAS_PRE) wv = p.norm_w[va];
   uint4 sv[kHC];
+  if constexpr (MODE != kBoundaryFirst) {
 #pragma unroll
-  for (int j = 0; j < kHC; ++j) sv[j] = load_nt(p.res_in + ((size_t)r * kHC + j) * p.hv + va);
+    for (int j = 0; j < kHC; ++j) sv[j] = load_nt(p.res_in + ((size_t)r * kHC + j) * p.hv + va);
+  }
+  uint4 xr = make_uint4(0u, 0u, 0u, 0u);  // first: the embedding vector itself
 
-  if constexpr (!FINALIZE) {
+  if constexpr (MODE == kBoundaryFirst) {
+    xr = load_nt(p.xp + (size_t)r * p.hv + va);
+    unpack8(xr, x);
+  } else if constexpr (MODE == kBoundaryHead) {
+    // no sublayer output
+  } else if constexpr (!FINALIZE) {
     // t ascending
     const uint4* src = p.xp + (size_t)r * p.hv + va;
     const size_t slice = (size_t)p.rows * p.hv;
@@ -326,38 +337,57 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] += f[e];
   }
-  round8_bf16(x);  // the reduced output is a bf16 tensor
+  if constexpr (MODE == kBoundaryMix) round8_bf16(x);  // the reduced output is a bf16 tensor
 
-  float s[kHC][8];
-#pragma unroll
-  for (int j = 0; j < kHC; ++j) unpack8(sv[j], s[j]);
   float sn[kHC][8];
-  uint4* out = p.res_out + (size_t)r * kHC * p.hv + v;
+  if constexpr (MODE == kBoundaryFirst) {
+    // every stream is the embedding, bit for bit
+    uint4* out = p.res_out + (size_t)r * kHC * p.hv + v;
 #pragma unroll
-  for (int i = 0; i < kHC; ++i) {
+    for (int i = 0; i < kHC; ++i)
+      if (active) out[(size_t)i * p.hv] = xr;
+  } else if constexpr (MODE == kBoundaryHead) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float a = pst[i] * x[e];
+    for (int j = 0; j < kHC; ++j) unpack8(sv[j], sn[j]);
+  } else {
+    uint4* out = p.res_out + (size_t)r * kHC * p.hv + v;
+    float s[kHC][8];
 #pragma unroll
-      for (int j = 0; j < kHC; ++j) a = __builtin_fmaf(cmb[i * kHC + j], s[j][e], a);
-      sn[i][e] = a;
+    for (int j = 0; j < kHC; ++j) unpack8(sv[j], s[j]);
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float a = pst[i] * x[e];
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) a = __builtin_fmaf(cmb[i * kHC + j], s[j][e], a);
+        sn[i][e] = a;
+      }
+      const uint4 o = pack8_round(sn[i]);
+      if (active) out[(size_t)i * p.hv] = o;  // the streams do not wait for the RMS
+      if constexpr (HAS_PRE) unpack8(o, sn[i]);
     }
-    const uint4 o = pack8_round(sn[i]);
-    if (active) out[(size_t)i * p.hv] = o;  // the streams do not wait for the RMS
-    if constexpr (HAS_PRE) unpack8(o, sn[i]);
   }
   if constexpr (!HAS_PRE) return;
 
   float y[8];
   float sq = 0.f;
+  if constexpr (MODE == kBoundaryFirst) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float a = 0.f;
+    for (int e = 0; e < 8; ++e) y[e] = x[e];  // the identity pre-mix
+  } else {
 #pragma unroll
-    for (int j = 0; j < kHC; ++j) a = __builtin_fmaf(pr[j], sn[j][e], a);
-    y[e] = a;
-    sq = __builtin_fmaf(a, a, sq);
+    for (int e = 0; e < 8; ++e) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < kHC; ++j) a = __builtin_fmaf(pr[j], sn[j][e], a);
+      y[e] = a;
+    }
+    // the head's collapse is a bf16 tensor of its own before the norm
+    if constexpr (MODE == kBoundaryHead) round8_bf16(y);
   }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sq = __builtin_fmaf(y[e], y[e], sq);
   if (!active) sq = 0.f;
   sq = wave_sum(sq);
   if (lane == 0) s_red[wave] = sq;
@@ -423,7 +453,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   }
 }
 
-template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8>
+template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8, int MODE>
 __global__ __launch_bounds__(BS) void boundary_kernel(const BoundaryParams p,
                                                       const float* __restrict__ post,
                                                       const float* __restrict__ comb,
@@ -445,8 +475,8 @@ __global__ __launch_bounds__(BS) void boundary_kernel(const BoundaryParams p,
     if constexpr (!HAS_PRE)
       boundary_item_quad<BS, FINALIZE>(p, r, c);
     else
-      boundary_item_lane<BS, FINALIZE, HAS_PRE, MXFP8>(p, post, comb, pre, idx, ew, r, c, s_red,
-                                                       &s_inv);
+      boundary_item_lane<BS, FINALIZE, HAS_PRE, MXFP8, MODE>(p, post, comb, pre, idx, ew, r, c,
+                                                             s_red, &s_inv);
   }
 }
 
@@ -479,16 +509,22 @@ __global__ __launch_bounds__(256) void collapse_mean_kernel(const uint4* __restr
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-template <int BS, bool FIN, bool PRE, bool MX>
+template <int BS, bool FIN, bool PRE, bool MX, int MODE = kBoundaryMix>
 static hipError_t launch_one(const BoundaryParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((boundary_kernel<BS, FIN, PRE, MX>), dim3(grid), dim3(BS), 0, st, p, p.post,
-                     p.comb, p.pre, p.idx, p.ew);
+  hipLaunchKernelGGL((boundary_kernel<BS, FIN, PRE, MX, MODE>), dim3(grid), dim3(BS), 0, st, p,
+                     p.post, p.comb, p.pre, p.idx, p.ew);
   return hipGetLastError();
 }
 
 template <int BS>
-static hipError_t launch_bs(const BoundaryParams& p, bool fin, bool pre, bool mx, int grid,
-                            hipStream_t st) {
+static hipError_t launch_bs(const BoundaryParams& p, bool fin, bool pre, bool mx, int mode,
+                            int grid, hipStream_t st) {
+  if (mode == kBoundaryFirst)
+    return mx ? launch_one<BS, false, true, true, kBoundaryFirst>(p, grid, st)
+              : launch_one<BS, false, true, false, kBoundaryFirst>(p, grid, st);
+  if (mode == kBoundaryHead)
+    return mx ? launch_one<BS, false, true, true, kBoundaryHead>(p, grid, st)
+              : launch_one<BS, false, true, false, kBoundaryHead>(p, grid, st);
   if (!fin) {
     if (!pre) return launch_one<BS, false, false, false>(p, grid, st);
     return mx ? launch_one<BS, false, true, true>(p, grid, st)
@@ -499,11 +535,11 @@ static hipError_t launch_bs(const BoundaryParams& p, bool fin, bool pre, bool mx
             : launch_one<BS, true, true, false>(p, grid, st);
 }
 
-template <int BS, bool FIN, bool PRE, bool MX>
+template <int BS, bool FIN, bool PRE, bool MX, int MODE = kBoundaryMix>
 static int occupancy_one() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, boundary_kernel<BS, FIN, PRE, MX>, BS, 0) !=
-      hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, boundary_kernel<BS, FIN, PRE, MX, MODE>, BS,
+                                                   0) != hipSuccess)
     return 0;
   return n;
 }
@@ -515,6 +551,8 @@ static int occupancy_bs() {
   n = min(n, occupancy_one<BS, false, true, true>());
   n = min(n, occupancy_one<BS, true, true, false>());
   n = min(n, occupancy_one<BS, true, true, true>());
+  n = min(n, occupancy_one<BS, false, true, true, kBoundaryFirst>());
+  n = min(n, occupancy_one<BS, false, true, true, kBoundaryHead>());
   return n;
 }
 
@@ -553,7 +591,7 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   p.rows = L.rows;
   p.hidden = L.hidden;
   p.hv = L.hidden / 8;
-  const bool pre = L.pre != nullptr;
+  const bool pre = L.pre != nullptr || L.mode == kBoundaryFirst;  // a layer input is written
   const int block = pre ? L.block : kResidualOnlyBlock;
   p.chunks = boundary_chunks(L.hidden, block, pre);
   p.layer_out = reinterpret_cast<uint4*>(L.layer_input_out);
@@ -568,9 +606,9 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   const bool mx = L.mx_data_out != nullptr;
   const int row_blocks = (L.rows + kXcds - 1) / kXcds;  // rows per XCD in total
   if (pre) {
-    // a round may use at most a quarter of the XCD's resident workgroups
+    // a round may use at most half of the XCD's resident workgroups
     // (at least one row: a row's chunks fit half an XCD, checked at handle creation)
-    const int per_xcd = L.max_wgs_per_xcd / 4;
+    const int per_xcd = L.max_wgs_per_xcd / 2;
     int rpr = per_xcd / p.chunks;
     if (rpr < 1) rpr = 1;
     if (rpr > row_blocks) rpr = row_blocks;
@@ -582,9 +620,9 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   }
   const int grid = kXcds * p.rows_per_round * p.chunks;
   switch (block) {
-    case 128: return launch_bs<128>(p, fin, pre, mx, grid, stream);
-    case 256: return launch_bs<256>(p, fin, pre, mx, grid, stream);
-    case 512: return launch_bs<512>(p, fin, pre, mx, grid, stream);
+    case 128: return launch_bs<128>(p, fin, pre, mx, L.mode, grid, stream);
+    case 256: return launch_bs<256>(p, fin, pre, mx, L.mode, grid, stream);
+    case 512: return launch_bs<512>(p, fin, pre, mx, L.mode, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

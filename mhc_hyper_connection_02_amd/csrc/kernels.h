@@ -36,7 +36,19 @@ struct BoundaryLaunch {
   int spin_limit;
   int max_wgs_per_xcd;          // resident workgroups of this block size on one XCD
   int block;                    // 128, 256 or 512 threads per workgroup (layer-input kernels)
+  int mode;                     // kBoundaryMix, kBoundaryFirst or kBoundaryHead
 };
+
+// What the layer-input kernel computes (the layer input is always RMSNorm(y) * w):
+//  mix:   x from the sublayer output, new streams s' = post x + comb s (stored),
+//         y = sum_j pre_j s'_j
+//  first: x = the one slice x_partials[0] (the embedding), every stream := x (stored),
+//         y = x (the identity pre-mix); no streams read, no post/comb/pre
+//  head:  no x; y = bf16(sum_j pre_j s_j) on the given streams; nothing stored but the
+//         layer input (and its MXFP8 form)
+constexpr int kBoundaryMix = 0;
+constexpr int kBoundaryFirst = 1;
+constexpr int kBoundaryHead = 2;
 
 struct PreLaunch {
   const uint16_t* residual;

@@ -293,19 +293,21 @@ def decode_chain(embedding_bits, sublayers, rms_eps, hc_eps, post_alpha, sinkhor
     each with the coefficient weights "fn", "scale", "base", the norm weight
     "norm_w", a flag "mxfp8" for its layer input, and "output": the sublayer's
     output as {"partials": [T,R,H]} or {"finalize": (g, w, idx, shared)}.
-    The first sublayer's layer input (the normalized embedding) feeds nothing
-    here and is not computed. Coefficients pass between steps as fp32, as they
-    do between the library's calls. Returns the final streams and their mean;
-    with ``record`` (a list), appends the first coefficients and then each
-    boundary's outputs.
+    The first entry (:func:`first`) also yields the first sublayer's input, the
+    normalized embedding. Coefficients pass between steps as fp32, as they do
+    between the library's calls. Returns the final streams and their mean; with
+    ``record`` (a list), appends the first entry's outputs with the first
+    coefficients, and then each boundary's outputs.
     """
     emb = np.asarray(embedding_bits, dtype=np.uint16)
-    streams = np.repeat(emb[:, None, :], hc_mult, axis=1)
-    first = sublayers[0]
-    pre, post, comb = pre_coeffs(streams, first["fn"], first["scale"], first["base"],
+    head = sublayers[0]
+    entry = first(emb, head["norm_w"], norm_eps, hc_mult, mxfp8=bool(head["mxfp8"]))
+    streams = entry["residual"]
+    pre, post, comb = pre_coeffs(streams, head["fn"], head["scale"], head["base"],
                                  rms_eps, hc_eps, hc_eps, post_alpha, sinkhorn_iters)
     if record is not None:
-        record.append({"pre": pre, "post": post, "comb": comb})
+        entry.update({"pre": pre, "post": post, "comb": comb})
+        record.append(entry)
     for idx in range(len(sublayers)):
         out = sublayers[idx]["output"]
         last = idx + 1 == len(sublayers)

@@ -25,6 +25,11 @@ def _teacher_forced_checks(step, check):
     host = {}
 
     def record(i, stage, c):
+        if stage == "first":
+            torch.cuda.synchronize()
+            snaps["first"] = {"residual": N(c.streams), "layer_input": N(c.layer_input),
+                              "mx_data": N(c.mx_data), "mx_scale": N(c.mx_scale)}
+            return
         if i not in check:
             return
         torch.cuda.synchronize()
@@ -42,6 +47,12 @@ def _teacher_forced_checks(step, check):
     step.run()
     torch.cuda.synchronize()
     step.record = None
+    # the first layer's entry: streams = the embedding, layer input = its normalized form
+    s0 = step.subs[0]
+    want = oracle.first(N(step.emb), N(s0["norm_w"]), p["norm_eps"], mxfp8=s0["mxfp8"])
+    got = {k: v for k, v in snaps["first"].items() if k in want}
+    assert np.array_equal(got["residual"], want["residual"]), "first: streams"
+    compare_boundary_outputs(got, want, "chain entry")
     for i in sorted(check):
         sn = snaps[i]
         s = step.subs[i]
