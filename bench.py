@@ -209,22 +209,39 @@ def main():
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
 
-    def chain_row():
+    def chain_rows():
+        """The chained step, then the same step with a stand-in sublayer (one bf16 GEMM of the
+        layer input per sublayer), coefficient calls inline and on a side stream."""
         from mhc_hyper_connection_02_amd import chain as chain_mod
         log("chain: generating 122 sublayers of synthetic inputs")
         t0 = time.time()
         step = chain_mod.DecodeChain.from_synth(dev)
         log(f"  inputs ready in {time.time() - t0:.1f} s ({step.input_bytes() / 1e9:.2f} GB)")
-        us_e, us_g = time_calls(torch, [step.run], max(3, args.steps // 40), 2)
-        row = {"us_per_step": round(us_g, 1),
-               "us_per_step_eager": None if us_e is None else round(us_e, 1),
-               "algorithmic_bytes": int(step.algorithmic_bytes()),
-               "gb_per_s": round(step.algorithmic_bytes() / us_g / 1e3, 1)}
-        log(f"  chain {row}")
-        return row
+        k = max(3, args.steps // 40)
+        us_e, us_g = time_calls(torch, [step.run], k, 2)
+        out = {"chain_decode_step": {
+            "us_per_step": round(us_g, 1),
+            "us_per_step_eager": None if us_e is None else round(us_e, 1),
+            "algorithmic_bytes": int(step.algorithmic_bytes()),
+            "gb_per_s": round(step.algorithmic_bytes() / us_g / 1e3, 1)}}
+        log(f"  chain {out['chain_decode_step']}")
+        for side in (False, True):
+            s2 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, standin=True,
+                                       side_stream=side)
+            e2, g2 = time_calls(torch, [s2.run], k, 2)
+            name = "chain_standin_side_stream" if side else "chain_standin_inline"
+            out[name] = {"us_per_step": round(g2, 1),
+                         "us_per_step_eager": None if e2 is None else round(e2, 1),
+                         "note": "boundaries + one [R,H]x[H,H] bf16 GEMM per sublayer as a "
+                                 "stand-in; coefficient calls " + ("on a side stream, joined "
+                                 "before the next boundary" if side else "inline")}
+            log(f"  {name} {out[name]}")
+            del s2
+        del step
+        return out
 
     if args.chain_only:
-        print(json.dumps({"rows": {"chain_decode_step": chain_row()}}), flush=True)
+        print(json.dumps({"rows": chain_rows()}), flush=True)
         return
 
     # --- headline: config 1, decode boundary + MXFP8 --------------------------------
@@ -372,7 +389,7 @@ def main():
         del bufs, calls
 
     if not args.no_chain and not args.no_rows:
-        rows["chain_decode_step"] = chain_row()
+        rows.update(chain_rows())
 
     head = rows["boundary_decode_mxfp8"]
     us = head["us_per_call"]

@@ -19,6 +19,13 @@ The streams are updated in place. Every buffer is allocated up front, so
 ``run`` allocates nothing and can be captured in a HIP graph. The sublayers'
 outputs (attention partials, unfinalized MoE outputs) are inputs here: the
 step covers the boundaries only.
+
+Side stream (boundary page, ``Boundaries.sublayer`` and ``Boundaries.join``): the
+coefficient call after a boundary may run on a second stream while the sublayer
+computes on the layer input, joined before the next boundary. With
+``standin=True`` each sublayer is stood in for by one bf16 GEMM of the layer input
+([R, H] x [H, H], a projection's worth of work, outside the hot path and its
+result unused), so that the overlap has something to hide under.
 """
 
 import torch
@@ -27,7 +34,8 @@ from . import binding, synth
 
 
 class DecodeChain:
-    def __init__(self, handle, embedding, sublayers, params, device):
+    def __init__(self, handle, embedding, sublayers, params, device, standin=False,
+                 side_stream=False):
         """embedding: [R,H] bf16 tensor; sublayers: list of dicts of device tensors as built by
         :meth:`from_synth`; params: rms_eps, hc_eps, post_alpha, sinkhorn_iters, norm_eps."""
         self.h = handle
@@ -45,6 +53,14 @@ class DecodeChain:
         self.mx_data = torch.empty((R, H), dtype=torch.uint8, device=device)
         self.mx_scale = torch.empty((R, H // 32), dtype=torch.uint8, device=device)
         self.mean = torch.empty((R, H), dtype=torch.bfloat16, device=device)
+        self.side = torch.cuda.Stream(device=device) if side_stream else None
+        self.standin_w = self.standin_out = None
+        if standin:
+            g = torch.Generator(device=device)
+            g.manual_seed(1234)
+            self.standin_w = (torch.randn((H, H), generator=g, device=device) * H ** -0.5
+                              ).to(torch.bfloat16)
+            self.standin_out = torch.empty((R, H), dtype=torch.bfloat16, device=device)
         # optional callback(index, stage, chain) around every boundary: stage "before", "after"
         # (the boundary's outputs), "coeffs" (the coefficient call that follows it); and once
         # with index -1, stage "first", after the first layer's entry
@@ -53,7 +69,7 @@ class DecodeChain:
     @classmethod
     def from_synth(cls, device, layers=synth.CHAIN_LAYERS, rows=synth.CHAIN_ROWS,
                    hidden=synth.CHAIN_HIDDEN, tp=synth.CHAIN_TP, top_k=synth.CHAIN_TOP_K,
-                   handle=None):
+                   handle=None, standin=False, side_stream=False):
         """The chained step on the seeded synthetic inputs (see ``synth.chain_sublayer``)."""
         T = lambda a: synth.to_torch(a, device)  # noqa: E731
         if handle is None:
@@ -72,7 +88,8 @@ class DecodeChain:
                     g, w, idx, sh = d["output"]["finalize"]
                     t["finalize"] = (T(g), T(w), T(idx), T(sh))
                 subs.append(t)
-        return cls(handle, emb, subs, synth.chain_params(), device)
+        return cls(handle, emb, subs, synth.chain_params(), device, standin=standin,
+                   side_stream=side_stream)
 
     def input_bytes(self):
         tot = self.emb.numel() * 2
@@ -146,9 +163,22 @@ class DecodeChain:
             if self.record is not None:
                 self.record(i, "after", self)
             if not last:
+                main = torch.cuda.current_stream()
+                if self.side is not None:
+                    # the coefficients of the next sublayer beside it, joined before the
+                    # next boundary (which reads them)
+                    self.side.wait_stream(main)
+                    cs = self.side
+                else:
+                    cs = main
                 binding.pre_coeffs(h, self.streams, nxt["fn"], nxt["scale"], nxt["base"],
                                    p["rms_eps"], p["hc_eps"], p["hc_eps"], p["post_alpha"],
-                                   p["sinkhorn_iters"], out=(self.pre, self.post, self.comb))
+                                   p["sinkhorn_iters"], out=(self.pre, self.post, self.comb),
+                                   stream=cs)
+                if self.standin_w is not None:
+                    torch.matmul(self.layer_input, self.standin_w, out=self.standin_out)
+                if self.side is not None:
+                    main.wait_stream(self.side)
                 if self.record is not None:
                     self.record(i, "coeffs", self)
         binding.collapse_mean(h, self.streams, out=self.mean)

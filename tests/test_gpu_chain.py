@@ -111,3 +111,37 @@ def test_chain_full_61_layers_sampled_steps():
     torch.cuda.synchronize()
     assert np.all(np.isfinite(mean.view(np.uint16).astype(np.float64)))
     assert step.h.errors() == 0
+
+
+def test_side_stream_and_standin_leave_the_boundaries_unchanged():
+    """The coefficient calls on a side stream beside a stand-in sublayer GEMM, joined before
+    each boundary: the step's streams and mean equal the plain step's bit for bit, in eager
+    runs and in graph replays."""
+    say("case: chained step, 3 layers: side-stream coefficients + stand-in sublayer")
+    plain = chain.DecodeChain.from_synth(DEV, layers=3)
+    want_mean = N(plain.run())
+    want_streams = N(plain.streams)
+    side = chain.DecodeChain(plain.h, plain.emb, plain.subs, plain.p, DEV, standin=True,
+                             side_stream=True)
+    got = N(side.run())
+    torch.cuda.synchronize()
+    assert np.array_equal(got, want_mean)
+    assert np.array_equal(N(side.streams), want_streams)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        side.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        out = side.run()
+    for rep in range(2):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(N(out), want_mean), f"replay {rep}"
+        plain.run()  # eager work between replays
+        torch.cuda.synchronize()
+    assert plain.h.errors() == 0
+
