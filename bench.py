@@ -225,6 +225,15 @@ def main():
             "algorithmic_bytes": int(step.algorithmic_bytes()),
             "gb_per_s": round(step.algorithmic_bytes() / us_g / 1e3, 1)}}
         log(f"  chain {out['chain_decode_step']}")
+        s3 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, deferred=True)
+        e3, g3 = time_calls(torch, [s3.run], k, 2)
+        out["chain_decode_step_deferred"] = {
+            "us_per_step": round(g3, 1), "us_per_step_eager": None if e3 is None else round(e3, 1),
+            "gb_per_s": round(step.algorithmic_bytes() / g3 / 1e3, 1),
+            "note": "coefficient calls deferred: each boundary finishes the coefficients it "
+                    "consumes (no epilogue launch)"}
+        log(f"  chain deferred {out['chain_decode_step_deferred']}")
+        del s3
         for side in (False, True):
             s2 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, standin=True,
                                        side_stream=side)

@@ -262,6 +262,33 @@ int mhc_pre_coeffs(mhc_handle h, const uint16_t* residual, const uint16_t* fn,
                    float sinkhorn_eps, float post_alpha, int sinkhorn_iters, int rows,
                    float* pre_out, float* post_out, float* comb_out, mhc_stream_t stream);
 
+/*
+ * mhc_pre_coeffs_deferred -- mhc_pre_coeffs (same arguments, same results, bit for bit)
+ * with its last step left to the call that consumes it.
+ *
+ * Runs the split-K projection now and records the call as pending on the handle. The
+ * next mhc_boundary, mhc_finalize or mhc_residual_only on the handle whose post and
+ * comb are this call's post_out and comb_out (and whose pre, if any, is pre_out), with
+ * the same rows, finishes the coefficients inside its own kernel (while its loads are
+ * in flight) and writes pre_out, post_out and comb_out as well. Any other call on the
+ * handle, a mhc_pre_coeffs or mhc_pre_coeffs_deferred call included, first enqueues the
+ * pending epilogue as mhc_pre_coeffs would have. Until then the outputs are not
+ * written: a caller that reads them otherwise calls mhc_pre_coeffs_flush first.
+ * Errors: as mhc_pre_coeffs (a failing call records nothing).
+ */
+int mhc_pre_coeffs_deferred(mhc_handle h, const uint16_t* residual, const uint16_t* fn,
+                            const float* scale, const float* base, float rms_eps, float pre_eps,
+                            float sinkhorn_eps, float post_alpha, int sinkhorn_iters, int rows,
+                            float* pre_out, float* post_out, float* comb_out,
+                            mhc_stream_t stream);
+
+/*
+ * mhc_pre_coeffs_flush -- enqueue the epilogue of a pending deferred coefficient call on
+ * `stream` (nothing if none is pending), after which its outputs are complete in stream
+ * order. MHC_ERR_INVALID_ARG for a NULL handle.
+ */
+int mhc_pre_coeffs_flush(mhc_handle h, mhc_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,6 +45,9 @@ _SIGS = {
     "mhc_first": ([_vp, _vp, _vp, _f, _i, _vp, _vp, _vp, _vp, _vp], _i),
     "mhc_collapse_norm": ([_vp, _vp, _vp, _vp, _f, _i, _vp, _vp, _vp, _vp], _i),
     "mhc_pre_coeffs": ([_vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f, _i, _i, _vp, _vp, _vp, _vp], _i),
+    "mhc_pre_coeffs_deferred": ([_vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f, _i, _i, _vp, _vp, _vp,
+                                 _vp], _i),
+    "mhc_pre_coeffs_flush": ([_vp, _vp], _i),
 }
 
 
@@ -343,8 +346,10 @@ def collapse_norm(h, residual, pre, norm_weight, eps, mxfp8=False, out=None, mx_
 
 
 def pre_coeffs(h, residual, fn, scale, base, rms_eps, pre_eps, sinkhorn_eps, post_alpha,
-               sinkhorn_iters, out=None, stream=None):
-    """``mhc_pre_coeffs``: streams [rows, n, hidden] -> (pre [rows,n], post [rows,n], comb [rows,n,n])."""
+               sinkhorn_iters, out=None, stream=None, deferred=False):
+    """``mhc_pre_coeffs``: streams [rows, n, hidden] -> (pre [rows,n], post [rows,n], comb [rows,n,n]).
+    With ``deferred``, ``mhc_pre_coeffs_deferred``: the outputs are written by the boundary
+    call that consumes them, or by :func:`pre_coeffs_flush`."""
     if residual.dim() != 3:
         raise ValueError("residual must be [rows, hc_mult, hidden]")
     rows, n, hidden = residual.shape
@@ -364,9 +369,15 @@ def pre_coeffs(h, residual, fn, scale, base, rms_eps, pre_eps, sinkhorn_eps, pos
     _need(pre, "pre_out", torch.float32, (rows, n), dev)
     _need(post, "post_out", torch.float32, (rows, n), dev)
     _need(comb, "comb_out", torch.float32, (rows, n, n), dev)
-    st = load_library().mhc_pre_coeffs(h.ptr, _ptr(residual), _ptr(fn), _ptr(scale), _ptr(base),
+    name = "mhc_pre_coeffs_deferred" if deferred else "mhc_pre_coeffs"
+    st = getattr(load_library(), name)(h.ptr, _ptr(residual), _ptr(fn), _ptr(scale), _ptr(base),
                                        float(rms_eps), float(pre_eps), float(sinkhorn_eps),
                                        float(post_alpha), int(sinkhorn_iters), rows, _ptr(pre),
                                        _ptr(post), _ptr(comb), _stream(stream))
-    _check(st, "mhc_pre_coeffs")
+    _check(st, name)
     return pre, post, comb
+
+
+def pre_coeffs_flush(h, stream=None):
+    """``mhc_pre_coeffs_flush``: complete a pending deferred coefficient call."""
+    _check(load_library().mhc_pre_coeffs_flush(h.ptr, _stream(stream)), "mhc_pre_coeffs_flush")

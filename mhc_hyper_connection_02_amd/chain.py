@@ -35,7 +35,7 @@ from . import binding, synth
 
 class DecodeChain:
     def __init__(self, handle, embedding, sublayers, params, device, standin=False,
-                 side_stream=False):
+                 side_stream=False, deferred=False):
         """embedding: [R,H] bf16 tensor; sublayers: list of dicts of device tensors as built by
         :meth:`from_synth`; params: rms_eps, hc_eps, post_alpha, sinkhorn_iters, norm_eps."""
         self.h = handle
@@ -53,6 +53,8 @@ class DecodeChain:
         self.mx_data = torch.empty((R, H), dtype=torch.uint8, device=device)
         self.mx_scale = torch.empty((R, H // 32), dtype=torch.uint8, device=device)
         self.mean = torch.empty((R, H), dtype=torch.bfloat16, device=device)
+        # deferred coefficient calls: each boundary finishes the coefficients it consumes
+        self.deferred = deferred
         self.side = torch.cuda.Stream(device=device) if side_stream else None
         self.standin_w = self.standin_out = None
         if standin:
@@ -69,7 +71,7 @@ class DecodeChain:
     @classmethod
     def from_synth(cls, device, layers=synth.CHAIN_LAYERS, rows=synth.CHAIN_ROWS,
                    hidden=synth.CHAIN_HIDDEN, tp=synth.CHAIN_TP, top_k=synth.CHAIN_TOP_K,
-                   handle=None, standin=False, side_stream=False):
+                   handle=None, standin=False, side_stream=False, deferred=False):
         """The chained step on the seeded synthetic inputs (see ``synth.chain_sublayer``)."""
         T = lambda a: synth.to_torch(a, device)  # noqa: E731
         if handle is None:
@@ -89,7 +91,7 @@ class DecodeChain:
                     t["finalize"] = (T(g), T(w), T(idx), T(sh))
                 subs.append(t)
         return cls(handle, emb, subs, synth.chain_params(), device, standin=standin,
-                   side_stream=side_stream)
+                   side_stream=side_stream, deferred=deferred)
 
     def input_bytes(self):
         tot = self.emb.numel() * 2
@@ -142,7 +144,8 @@ class DecodeChain:
             self.record(-1, "first", self)
         binding.pre_coeffs(h, self.streams, first["fn"], first["scale"], first["base"],
                            p["rms_eps"], p["hc_eps"], p["hc_eps"], p["post_alpha"],
-                           p["sinkhorn_iters"], out=(self.pre, self.post, self.comb))
+                           p["sinkhorn_iters"], out=(self.pre, self.post, self.comb),
+                           deferred=self.deferred)
         for i, s in enumerate(self.subs):
             last = i + 1 == len(self.subs)
             nxt = None if last else self.subs[i + 1]
@@ -174,7 +177,7 @@ class DecodeChain:
                 binding.pre_coeffs(h, self.streams, nxt["fn"], nxt["scale"], nxt["base"],
                                    p["rms_eps"], p["hc_eps"], p["hc_eps"], p["post_alpha"],
                                    p["sinkhorn_iters"], out=(self.pre, self.post, self.comb),
-                                   stream=cs)
+                                   stream=cs, deferred=self.deferred)
                 if self.standin_w is not None:
                     torch.matmul(self.layer_input, self.standin_w, out=self.standin_out)
                 if self.side is not None:

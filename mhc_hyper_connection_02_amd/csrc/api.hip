@@ -38,6 +38,9 @@ struct mhc_ctx {
   unsigned* epoch;
   unsigned* errors;
   size_t zero_words;       // 32-bit words of slots + epoch + errors (cleared by mhc_reset)
+  // a deferred coefficient call whose epilogue has not been enqueued yet
+  bool pending;
+  mhc::PreLaunch pend;
 };
 
 namespace {
@@ -116,6 +119,28 @@ void fill_mix(const mhc_ctx* h, mhc::BoundaryLaunch& L, bool finalize, const uin
   L.block = block;
 }
 
+// Enqueue the epilogue of a pending deferred coefficient call, if any.
+int flush_pending(mhc_ctx* h, hipStream_t stream) {
+  if (!h->pending) return MHC_OK;
+  h->pending = false;
+  return launch_status(mhc::launch_pre_epilogue(h->pend, stream));
+}
+
+// A boundary call that consumes the pending call's outputs finishes its epilogue in the
+// kernel; any other boundary call enqueues the epilogue first.
+int take_pending(mhc_ctx* h, mhc::BoundaryLaunch& L, const float* post, const float* comb,
+                 const float* pre, int rows, hipStream_t stream) {
+  if (!h->pending) return MHC_OK;
+  const bool match = post == h->pend.post_out && comb == h->pend.comb_out &&
+                     (pre == nullptr || pre == h->pend.pre_out) && rows == h->pend.rows;
+  if (!match) return flush_pending(h, stream);
+  h->pending = false;
+  L.defer = true;
+  L.coef = mhc::pre_epilogue_args(h->pend);
+  L.pre_pending = h->pend.pre_out;
+  return MHC_OK;
+}
+
 }  // namespace
 
 namespace mhc {
@@ -179,6 +204,7 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   h->device = device;
   h->block = kDefaultBlock;
   h->spin_limit = kDefaultSpinLimit;
+  h->pending = false;
   h->slot_stride = mhc::boundary_chunks(hidden, kMinBlock, true);  // the most chunks per row
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
@@ -313,6 +339,8 @@ int mhc_boundary(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_
   L.tp = tp;
   fill_mix(h, L, false, residual, post, comb, pre, norm_weight, norm_eps, rows, residual_out,
            layer_input_out, mx_data_out, mx_scale_out);
+  st = take_pending(h, L, post, comb, pre, rows, static_cast<hipStream_t>(stream));
+  if (st != MHC_OK) return st;
   return launch_status(mhc::launch_boundary(L, static_cast<hipStream_t>(stream)));
 }
 
@@ -352,6 +380,8 @@ int mhc_finalize(mhc_handle h, const uint16_t* gemm2_permuted, int num_permuted,
   L.top_k = h->top_k;
   fill_mix(h, L, true, residual, post, comb, pre, norm_weight, norm_eps, rows, residual_out,
            layer_input_out, mx_data_out, mx_scale_out);
+  st = take_pending(h, L, post, comb, pre, rows, static_cast<hipStream_t>(stream));
+  if (st != MHC_OK) return st;
   return launch_status(mhc::launch_boundary(L, static_cast<hipStream_t>(stream)));
 }
 
@@ -372,6 +402,8 @@ int mhc_first(mhc_handle h, const uint16_t* x, const uint16_t* norm_weight, floa
   int st = check_device(h);
   if (st != MHC_OK) return st;
   mhc::BoundaryLaunch L = {};
+  st = flush_pending(h, static_cast<hipStream_t>(stream));
+  if (st != MHC_OK) return st;
   fill_mix(h, L, false, nullptr, nullptr, nullptr, nullptr, norm_weight, norm_eps, rows,
            residual_out, layer_input_out, mx_data_out, mx_scale_out);
   L.x_partials = x;
@@ -397,6 +429,8 @@ int mhc_collapse_norm(mhc_handle h, const uint16_t* residual, const float* pre,
   int st = check_device(h);
   if (st != MHC_OK) return st;
   mhc::BoundaryLaunch L = {};
+  st = flush_pending(h, static_cast<hipStream_t>(stream));
+  if (st != MHC_OK) return st;
   fill_mix(h, L, false, residual, nullptr, nullptr, pre, norm_weight, norm_eps, rows, nullptr,
            out, mx_data_out, mx_scale_out);
   L.mode = mhc::kBoundaryHead;
@@ -413,14 +447,19 @@ int mhc_collapse_mean(mhc_handle h, const uint16_t* streams, int rows, uint16_t*
   if (!aligned(streams, 16) || !aligned(out, 16)) return MHC_ERR_ALIGN;
   int st = check_device(h);
   if (st != MHC_OK) return st;
+  st = flush_pending(h, static_cast<hipStream_t>(stream));
+  if (st != MHC_OK) return st;
   return launch_status(
       mhc::launch_collapse_mean(streams, rows, h->hidden, out, static_cast<hipStream_t>(stream)));
 }
 
-int mhc_pre_coeffs(mhc_handle h, const uint16_t* residual, const uint16_t* fn,
-                   const float* scale, const float* base, float rms_eps, float pre_eps,
-                   float sinkhorn_eps, float post_alpha, int sinkhorn_iters, int rows,
-                   float* pre_out, float* post_out, float* comb_out, mhc_stream_t stream) {
+namespace {
+
+int pre_coeffs_common(mhc_handle h, const uint16_t* residual, const uint16_t* fn,
+                      const float* scale, const float* base, float rms_eps, float pre_eps,
+                      float sinkhorn_eps, float post_alpha, int sinkhorn_iters, int rows,
+                      float* pre_out, float* post_out, float* comb_out, mhc_stream_t stream,
+                      bool deferred) {
   if (!h) return MHC_ERR_INVALID_ARG;
   if (rows < 0 || sinkhorn_iters < 0 || sinkhorn_iters > kMaxSinkhornIters) return MHC_ERR_SHAPE;
   if (!(rms_eps >= 0.0f) || !(sinkhorn_eps >= 0.0f)) return MHC_ERR_SHAPE;
@@ -449,7 +488,44 @@ int mhc_pre_coeffs(mhc_handle h, const uint16_t* residual, const uint16_t* fn,
   L.post_out = post_out;
   L.comb_out = comb_out;
   L.part = h->pre_part;
-  return launch_status(mhc::launch_pre_coeffs(L, static_cast<hipStream_t>(stream)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = flush_pending(h, s);  // its partials are about to be overwritten
+  if (st != MHC_OK) return st;
+  if (!deferred) return launch_status(mhc::launch_pre_coeffs(L, s));
+  st = launch_status(mhc::launch_pre_partial(L, s));
+  if (st != MHC_OK) return st;
+  h->pending = true;
+  h->pend = L;
+  return MHC_OK;
+}
+
+}  // namespace
+
+int mhc_pre_coeffs(mhc_handle h, const uint16_t* residual, const uint16_t* fn,
+                   const float* scale, const float* base, float rms_eps, float pre_eps,
+                   float sinkhorn_eps, float post_alpha, int sinkhorn_iters, int rows,
+                   float* pre_out, float* post_out, float* comb_out, mhc_stream_t stream) {
+  return pre_coeffs_common(h, residual, fn, scale, base, rms_eps, pre_eps, sinkhorn_eps,
+                           post_alpha, sinkhorn_iters, rows, pre_out, post_out, comb_out, stream,
+                           false);
+}
+
+int mhc_pre_coeffs_deferred(mhc_handle h, const uint16_t* residual, const uint16_t* fn,
+                            const float* scale, const float* base, float rms_eps, float pre_eps,
+                            float sinkhorn_eps, float post_alpha, int sinkhorn_iters, int rows,
+                            float* pre_out, float* post_out, float* comb_out,
+                            mhc_stream_t stream) {
+  return pre_coeffs_common(h, residual, fn, scale, base, rms_eps, pre_eps, sinkhorn_eps,
+                           post_alpha, sinkhorn_iters, rows, pre_out, post_out, comb_out, stream,
+                           true);
+}
+
+int mhc_pre_coeffs_flush(mhc_handle h, mhc_stream_t stream) {
+  if (!h) return MHC_ERR_INVALID_ARG;
+  if (!h->pending) return MHC_OK;
+  int st = check_device(h);
+  if (st != MHC_OK) return st;
+  return flush_pending(h, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -45,6 +45,9 @@
 // XCD placement. Consecutive workgroup ids are dealt round-robin to the 8
 // XCDs, so a row's chunks get ids congruent to the row mod 8: all
 // workgroups of one row share one XCD's L2, where their polling stays.
+#include <type_traits>
+
+#include "coeff_epilogue.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -86,12 +89,50 @@ struct BoundaryParams {
   int spin_limit;
 };
 
+// Deferred coefficients: post, comb and pre come from a pending coefficient call's
+// split-K partials, finished in the kernel; each row's first workgroup writes them out.
+// A kernel argument of the deferred variants only (the others take an empty one, so
+// that their argument block stays small).
+struct DeferParams {
+  CoeffEpilogue coef;
+  float* def_pre;
+  float* def_post;
+  float* def_comb;
+};
+struct NoDefer {};
+constexpr int kBoundaryPrefetch = 8;  // float4 of a row's partials fetched ahead per lane
+template <bool DEFER>
+using DeferArg = typename std::conditional<DEFER, DeferParams, NoDefer>::type;
+
+// Deferred coefficients, wave 0 of the workgroup: finish row r's coefficient epilogue
+// from the prefetched partials into s_coef (pre | post | comb, as coeff_row's slots); the
+// row's first workgroup also writes them to the pending call's outputs. The workgroup
+// reads s_coef after the next barrier.
+__device__ __forceinline__ void deferred_finish(const DeferParams& d, int r, int c,
+                                                const CoeffPrefetch<kBoundaryPrefetch>& f,
+                                                float sc_l,
+                                                float base_l, float* s_coef) {
+  const int L = threadIdx.x;
+  int slot;
+  const float v = coeff_row_finish<true>(d.coef, r, L, f, sc_l, base_l, &slot);
+  if (slot >= 0) {
+    s_coef[slot] = v;
+    if (c == 0) {
+      if (slot < kHC) d.def_pre[r * kHC + slot] = v;
+      else if (slot < 2 * kHC) d.def_post[r * kHC + slot - kHC] = v;
+      else d.def_comb[r * kHC * kHC + slot - 2 * kHC] = v;
+    }
+  }
+}
+
 // Residual-only, four lanes per 16-byte vector: lane q loads stream q and a quarter
 // of the sublayer output (slices or expert slots q, q+4, ...), the quad combines its
 // partial sums and exchanges the streams over DPP quad permutations, and lane q
 // computes and stores output stream q (BS / 4 vectors per workgroup).
-template <int BS, bool FINALIZE>
-__device__ __forceinline__ void boundary_item_quad(const BoundaryParams& p, int r, int c) {
+template <int BS, bool FINALIZE, bool DEFER>
+__device__ __forceinline__ void boundary_item_quad(const BoundaryParams& p,
+                                                   const DeferArg<DEFER>& dp, int r, int c,
+                                                   float* s_coef, float sc_l, float base_l) {
   constexpr int kGroups = BS / 4;  // 16-byte vectors (8 elements) per workgroup
   const int tid = threadIdx.x;
   const int q = tid & 3;                     // this lane's output stream
@@ -118,12 +159,18 @@ __device__ __forceinline__ void boundary_item_quad(const BoundaryParams& p, int 
     }
   }
   // this lane's mixes: post_q and cq[d] = comb[q][q ^ d], the weight of the stream
-  // that a xor-d quad move brings
-  const float post_q = p.post[r * kHC + q];
+  // that a xor-d quad move brings (deferred: from LDS once wave 0 has finished them)
+  float post_q = 0.f;
   float cq[kHC];
+  if constexpr (!DEFER) {
+    post_q = p.post[r * kHC + q];
 #pragma unroll
-  for (int d = 0; d < kHC; ++d) cq[d] = p.comb[(r * kHC + q) * kHC + (q ^ d)];
+    for (int d = 0; d < kHC; ++d) cq[d] = p.comb[(r * kHC + q) * kHC + (q ^ d)];
+  }
   const uint4 sv = load_nt(p.res_in + ((size_t)r * kHC + q) * p.hv + va);
+  CoeffPrefetch<kBoundaryPrefetch> cf;
+  if constexpr (DEFER)
+    if (tid < kWave) coeff_row_prefetch<true>(dp.coef, r, tid, cf);
 
   if constexpr (!FINALIZE) {
     // lane q sums slices t = q, q+4, q+8, ... (ascending)
@@ -196,6 +243,13 @@ __device__ __forceinline__ void boundary_item_quad(const BoundaryParams& p, int 
     x[e] += dpp_f32<kDppQuadXor2>(x[e]);
   }
   round8_bf16(x);  // the reduced output is a bf16 tensor
+  if constexpr (DEFER) {
+    if (tid < kWave) deferred_finish(dp, r, c, cf, sc_l, base_l, s_coef);
+    __syncthreads();
+    post_q = s_coef[kHC + q];
+#pragma unroll
+    for (int d = 0; d < kHC; ++d) cq[d] = s_coef[2 * kHC + q * kHC + (q ^ d)];
+  }
 
   // --- mHC post for stream q: s'_q = post_q x + sum_j comb_qj s_j -------------------
   uint4 sj[kHC];
@@ -214,18 +268,21 @@ __device__ __forceinline__ void boundary_item_quad(const BoundaryParams& p, int 
     for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(cq[d], f[e], o[e]);
   }
   if (active) p.res_out[((size_t)r * kHC + q) * p.hv + v] = pack8_round(o);
+  if constexpr (DEFER) __syncthreads();  // s_coef is rewritten for the next row
 }
 
 // One lane per 16-byte vector: lane owns 8 elements of the row and all four streams of
 // them (BS vectors per workgroup). Same dataflow and handoff as the quad layout above.
-template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8, int MODE>
+template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8, int MODE, bool DEFER>
 __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
                                                    const float* __restrict__ post,
                                                    const float* __restrict__ comb,
                                                    const float* __restrict__ pre,
                                                    const int* __restrict__ idx,
-                                                   const float* __restrict__ ew, int r, int c,
-                                                   float* s_red, float* s_inv) {
+                                                   const float* __restrict__ ew,
+                                                   const DeferArg<DEFER>& dp, int r, int c,
+                                                   float* s_red, float* s_inv, float* s_coef,
+                                                   float sc_l, float base_l) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -256,13 +313,13 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     }
   }
   float pst[kHC], cmb[kHC * kHC], pr[kHC];
-  if constexpr (MODE == kBoundaryMix) {
+  if constexpr (MODE == kBoundaryMix && !DEFER) {
 #pragma unroll
     for (int i = 0; i < kHC; ++i) pst[i] = post[r * kHC + i];
 #pragma unroll
     for (int i = 0; i < kHC * kHC; ++i) cmb[i] = comb[r * kHC * kHC + i];
   }
-  if constexpr (HAS_PRE && MODE != kBoundaryFirst) {
+  if constexpr (HAS_PRE && MODE != kBoundaryFirst && !DEFER) {
 #pragma unroll
     for (int i = 0; i < kHC; ++i) pr[i] = pre[r * kHC + i];
   }
@@ -276,6 +333,9 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     for (int j = 0; j < kHC; ++j) sv[j] = load_nt(p.res_in + ((size_t)r * kHC + j) * p.hv + va);
   }
   uint4 xr = make_uint4(0u, 0u, 0u, 0u);  // first: the embedding vector itself
+  CoeffPrefetch<kBoundaryPrefetch> cf;
+  if constexpr (DEFER)
+    if (wave == 0) coeff_row_prefetch<true>(dp.coef, r, lane, cf);
 
   if constexpr (MODE == kBoundaryFirst) {
     xr = load_nt(p.xp + (size_t)r * p.hv + va);
@@ -338,6 +398,17 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     for (int e = 0; e < 8; ++e) x[e] += f[e];
   }
   if constexpr (MODE == kBoundaryMix) round8_bf16(x);  // the reduced output is a bf16 tensor
+  if constexpr (DEFER) {
+    if (wave == 0) deferred_finish(dp, r, c, cf, sc_l, base_l, s_coef);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kHC; ++i) {
+      pr[i] = s_coef[i];
+      pst[i] = s_coef[kHC + i];
+    }
+#pragma unroll
+    for (int i = 0; i < kHC * kHC; ++i) cmb[i] = s_coef[2 * kHC + i];
+  }
 
   float sn[kHC][8];
   if constexpr (MODE == kBoundaryFirst) {
@@ -453,17 +524,23 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   }
 }
 
-template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8, int MODE>
-__global__ __launch_bounds__(BS) void boundary_kernel(const BoundaryParams p,
+// The deferred variants are held to at least 4 waves per SIMD (at most 128 VGPRs), as
+// the others are without a hint, so that a 128-row call keeps one round.
+template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8, int MODE, bool DEFER>
+__global__ __launch_bounds__(BS, DEFER ? 4 : 1) void boundary_kernel(const BoundaryParams p,
                                                       const float* __restrict__ post,
                                                       const float* __restrict__ comb,
                                                       const float* __restrict__ pre,
                                                       const int* __restrict__ idx,
-                                                      const float* __restrict__ ew) {
+                                                      const float* __restrict__ ew,
+                                                      const DeferArg<DEFER> dp) {
   // the layer-input kernels (with the row handoff) run one lane per vector; the
   // residual-only kernels run four lanes per vector
   __shared__ float s_red[BS / kWave];
   __shared__ float s_inv;
+  __shared__ float s_coef[2 * kHC + kHC * kHC];
+  float sc_l = 0.f, base_l = 0.f;  // deferred coefficients: this lane's scale and base
+  if constexpr (DEFER) coeff_lane_scale_base(dp.coef, threadIdx.x & (kWave - 1), &sc_l, &base_l);
   const int wg = blockIdx.x;
   const int xcd = wg % kXcds;
   const int local = wg / kXcds;
@@ -473,10 +550,10 @@ __global__ __launch_bounds__(BS) void boundary_kernel(const BoundaryParams p,
     const int r = (round * p.rows_per_round + jr) * kXcds + xcd;
     if (r >= p.rows) break;  // uniform per workgroup; later rounds only go higher
     if constexpr (!HAS_PRE)
-      boundary_item_quad<BS, FINALIZE>(p, r, c);
+      boundary_item_quad<BS, FINALIZE, DEFER>(p, dp, r, c, s_coef, sc_l, base_l);
     else
-      boundary_item_lane<BS, FINALIZE, HAS_PRE, MXFP8, MODE>(p, post, comb, pre, idx, ew, r, c,
-                                                             s_red, &s_inv);
+      boundary_item_lane<BS, FINALIZE, HAS_PRE, MXFP8, MODE, DEFER>(
+          p, post, comb, pre, idx, ew, dp, r, c, s_red, &s_inv, s_coef, sc_l, base_l);
   }
 }
 
@@ -509,37 +586,47 @@ __global__ __launch_bounds__(256) void collapse_mean_kernel(const uint4* __restr
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-template <int BS, bool FIN, bool PRE, bool MX, int MODE = kBoundaryMix>
-static hipError_t launch_one(const BoundaryParams& p, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((boundary_kernel<BS, FIN, PRE, MX, MODE>), dim3(grid), dim3(BS), 0, st, p,
-                     p.post, p.comb, p.pre, p.idx, p.ew);
+template <int BS, bool FIN, bool PRE, bool MX, int MODE = kBoundaryMix, bool DEFER = false>
+static hipError_t launch_one(const BoundaryParams& p, const DeferParams& d, int grid,
+                             hipStream_t st) {
+  DeferArg<DEFER> dp;
+  if constexpr (DEFER) dp = d;
+  hipLaunchKernelGGL((boundary_kernel<BS, FIN, PRE, MX, MODE, DEFER>), dim3(grid), dim3(BS), 0,
+                     st, p, p.post, p.comb, p.pre, p.idx, p.ew, dp);
   return hipGetLastError();
 }
 
-template <int BS>
-static hipError_t launch_bs(const BoundaryParams& p, bool fin, bool pre, bool mx, int mode,
-                            int grid, hipStream_t st) {
-  if (mode == kBoundaryFirst)
-    return mx ? launch_one<BS, false, true, true, kBoundaryFirst>(p, grid, st)
-              : launch_one<BS, false, true, false, kBoundaryFirst>(p, grid, st);
-  if (mode == kBoundaryHead)
-    return mx ? launch_one<BS, false, true, true, kBoundaryHead>(p, grid, st)
-              : launch_one<BS, false, true, false, kBoundaryHead>(p, grid, st);
+template <int BS, bool DEFER>
+static hipError_t launch_mix(const BoundaryParams& p, const DeferParams& d, bool fin, bool pre,
+                             bool mx, int grid, hipStream_t st) {
   if (!fin) {
-    if (!pre) return launch_one<BS, false, false, false>(p, grid, st);
-    return mx ? launch_one<BS, false, true, true>(p, grid, st)
-              : launch_one<BS, false, true, false>(p, grid, st);
+    if (!pre) return launch_one<BS, false, false, false, kBoundaryMix, DEFER>(p, d, grid, st);
+    return mx ? launch_one<BS, false, true, true, kBoundaryMix, DEFER>(p, d, grid, st)
+              : launch_one<BS, false, true, false, kBoundaryMix, DEFER>(p, d, grid, st);
   }
-  if (!pre) return launch_one<BS, true, false, false>(p, grid, st);
-  return mx ? launch_one<BS, true, true, true>(p, grid, st)
-            : launch_one<BS, true, true, false>(p, grid, st);
+  if (!pre) return launch_one<BS, true, false, false, kBoundaryMix, DEFER>(p, d, grid, st);
+  return mx ? launch_one<BS, true, true, true, kBoundaryMix, DEFER>(p, d, grid, st)
+            : launch_one<BS, true, true, false, kBoundaryMix, DEFER>(p, d, grid, st);
 }
 
-template <int BS, bool FIN, bool PRE, bool MX, int MODE = kBoundaryMix>
+template <int BS>
+static hipError_t launch_bs(const BoundaryParams& p, const DeferParams& d, bool fin, bool pre,
+                            bool mx, int mode, bool defer, int grid, hipStream_t st) {
+  if (mode == kBoundaryFirst)
+    return mx ? launch_one<BS, false, true, true, kBoundaryFirst>(p, d, grid, st)
+              : launch_one<BS, false, true, false, kBoundaryFirst>(p, d, grid, st);
+  if (mode == kBoundaryHead)
+    return mx ? launch_one<BS, false, true, true, kBoundaryHead>(p, d, grid, st)
+              : launch_one<BS, false, true, false, kBoundaryHead>(p, d, grid, st);
+  return defer ? launch_mix<BS, true>(p, d, fin, pre, mx, grid, st)
+               : launch_mix<BS, false>(p, d, fin, pre, mx, grid, st);
+}
+
+template <int BS, bool FIN, bool PRE, bool MX, int MODE = kBoundaryMix, bool DEFER = false>
 static int occupancy_one() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, boundary_kernel<BS, FIN, PRE, MX, MODE>, BS,
-                                                   0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, boundary_kernel<BS, FIN, PRE, MX, MODE, DEFER>, BS, 0) != hipSuccess)
     return 0;
   return n;
 }
@@ -551,6 +638,10 @@ static int occupancy_bs() {
   n = min(n, occupancy_one<BS, false, true, true>());
   n = min(n, occupancy_one<BS, true, true, false>());
   n = min(n, occupancy_one<BS, true, true, true>());
+  n = min(n, occupancy_one<BS, false, true, false, kBoundaryMix, true>());
+  n = min(n, occupancy_one<BS, false, true, true, kBoundaryMix, true>());
+  n = min(n, occupancy_one<BS, true, true, false, kBoundaryMix, true>());
+  n = min(n, occupancy_one<BS, true, true, true, kBoundaryMix, true>());
   n = min(n, occupancy_one<BS, false, true, true, kBoundaryFirst>());
   n = min(n, occupancy_one<BS, false, true, true, kBoundaryHead>());
   return n;
@@ -602,6 +693,11 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   p.errors = L.errors;
   p.slot_stride = L.slot_stride;
   p.spin_limit = L.spin_limit;
+  DeferParams d;
+  d.coef = L.coef;
+  d.def_pre = L.defer ? L.pre_pending : nullptr;
+  d.def_post = L.defer ? const_cast<float*>(L.post) : nullptr;
+  d.def_comb = L.defer ? const_cast<float*>(L.comb) : nullptr;
   const bool fin = L.gemm2_permuted != nullptr;
   const bool mx = L.mx_data_out != nullptr;
   const int row_blocks = (L.rows + kXcds - 1) / kXcds;  // rows per XCD in total
@@ -620,9 +716,9 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   }
   const int grid = kXcds * p.rows_per_round * p.chunks;
   switch (block) {
-    case 128: return launch_bs<128>(p, fin, pre, mx, L.mode, grid, stream);
-    case 256: return launch_bs<256>(p, fin, pre, mx, L.mode, grid, stream);
-    case 512: return launch_bs<512>(p, fin, pre, mx, L.mode, grid, stream);
+    case 128: return launch_bs<128>(p, d, fin, pre, mx, L.mode, L.defer, grid, stream);
+    case 256: return launch_bs<256>(p, d, fin, pre, mx, L.mode, L.defer, grid, stream);
+    case 512: return launch_bs<512>(p, d, fin, pre, mx, L.mode, L.defer, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "coeff_epilogue.h"
+
 namespace mhc {
 
 struct BoundaryLaunch {
@@ -37,6 +39,12 @@ struct BoundaryLaunch {
   int max_wgs_per_xcd;          // resident workgroups of this block size on one XCD
   int block;                    // 128, 256 or 512 threads per workgroup (layer-input kernels)
   int mode;                     // kBoundaryMix, kBoundaryFirst or kBoundaryHead
+  // deferred coefficients (mix mode): post, comb and pre are computed in the kernel from a
+  // pending coefficient call's split-K partials, and written to post/comb/pre by the
+  // row's first workgroup
+  bool defer;
+  CoeffEpilogue coef;
+  float* pre_pending;           // the pending call's pre output (written even residual-only)
 };
 
 // What the layer-input kernel computes (the layer input is always RMSNorm(y) * w):
@@ -71,7 +79,10 @@ hipError_t launch_collapse_mean(const uint16_t* streams, int rows, int hidden, u
 
 void pre_plan(int rows, int hidden, int* ks_count, int* steps_per_wg, int* rows_pad);
 size_t pre_scratch_floats_for(int rows, int hidden);
-hipError_t launch_pre_coeffs(const PreLaunch& L, hipStream_t stream);
+hipError_t launch_pre_coeffs(const PreLaunch& L, hipStream_t stream);   // both kernels
+hipError_t launch_pre_partial(const PreLaunch& L, hipStream_t stream);   // split-K only
+hipError_t launch_pre_epilogue(const PreLaunch& L, hipStream_t stream);  // epilogue only
+CoeffEpilogue pre_epilogue_args(const PreLaunch& L);
 
 hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned value, hipStream_t stream);
 

@@ -18,12 +18,12 @@
 // its 16 x 25 partials to scratch laid out [row][25][k-split], so that the
 // epilogue reads each (row, logit) range contiguously.
 //
-// Kernel 2: one wave per row. Lanes 0..24 each sum one logit's (or the sum of
-// squares') partials over the k-splits in split order, then the logits get
-// 1/RMS, scale and base; lanes 0..7 write pre and post; the 16 comb entries
-// run the Sinkhorn iterations in one 16-lane DPP row (row sums over quads,
-// column sums over row rotations, each normalization one reciprocal and a
-// multiply).
+// Kernel 2: one wave per row runs the row's epilogue (coeff_epilogue.h): the
+// k-split partials added in split order, 1/RMS, scale and base, the sigmoids
+// and the Sinkhorn iterations. A deferred call (mhc_pre_coeffs_deferred)
+// launches only kernel 1 and leaves kernel 2's work to the boundary kernel
+// that consumes the coefficients, which runs the same function.
+#include "coeff_epilogue.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -145,65 +145,22 @@ __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const Pr
 }
 
 struct PreEpilogueParams {
-  const float* part;
-  const float* scale;  // [3]
-  const float* base;   // [24]
+  CoeffEpilogue e;
   float* pre_out;      // [rows][4]
   float* post_out;     // [rows][4]
   float* comb_out;     // [rows][16]
-  float rms_eps, pre_eps, sk_eps, alpha;
-  int iters, rows, K, ks_count;
 };
 
 __global__ __launch_bounds__(kWave) void pre_epilogue_kernel(const PreEpilogueParams p) {
   const int r = blockIdx.x;
   const int L = threadIdx.x;
-  // this lane's scale and base first, so that they arrive with the partials
-  const int Lc = L < kNC ? L : kNC - 1;
-  const float sc_l = p.scale[Lc < kN ? 0 : (Lc < 2 * kN ? 1 : 2)];
-  const float base_l = p.base[Lc];
-  // lanes 0..23: logits, lane 24: sum of squares; k-split partials are contiguous, and a
-  // lane fetches a whole batch of them before adding them in split order
-  float acc = 0.f;
-  if (L < kPartW) {
-    const float4* src = reinterpret_cast<const float4*>(p.part + ((size_t)r * kPartW + L) * p.ks_count);
-    constexpr int kBatch = 16;  // float4 per batch: 64 splits
-    for (int b0 = 0; b0 < p.ks_count / 4; b0 += kBatch) {
-      float4 v[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (b0 + u < p.ks_count / 4) v[u] = src[b0 + u];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (b0 + u < p.ks_count / 4) acc = (((acc + v[u].x) + v[u].y) + v[u].z) + v[u].w;
-    }
-  }
-  const float ss = __shfl(acc, kNC, kWave);
-  const float inv = 1.0f / sqrtf(ss / (float)p.K + p.rms_eps);
-  float lp = 0.f;
-  if (L < kNC) lp = (acc * inv) * sc_l + base_l;
-  if (L < kN) {
-    p.pre_out[r * kN + L] = 1.0f / (1.0f + expf(-lp)) + p.pre_eps;
-  } else if (L < 2 * kN) {
-    p.post_out[r * kN + (L - kN)] = p.alpha * (1.0f / (1.0f + expf(-lp)));
-  }
-  // comb: the 16 entries sit in lanes 32..47 (one DPP row), entry (i, j) at lane 32 + 4i + j,
-  // so a row sum is two quad steps and a column sum two row rotations. Every lane runs the
-  // same instructions (lanes outside the row carry dummies).
-  const int ce = L - 32;  // entry index for lanes 32..47
-  float a = __shfl(lp, 2 * kN + (ce & 15), kWave);
-  float mx = fmaxf(a, dpp_f32<kDppQuadXor1>(a));
-  mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
-  a = expf(a - mx);
-  for (int it = 0; it < p.iters; ++it) {
-    float rs = a + dpp_f32<kDppQuadXor1>(a);
-    rs = rs + dpp_f32<kDppQuadXor2>(rs);
-    a = a * __builtin_amdgcn_rcpf(rs + p.sk_eps);
-    float cs = a + dpp_f32<kDppRowRor4>(a);
-    cs = cs + dpp_f32<kDppRowRor8>(cs);
-    a = a * __builtin_amdgcn_rcpf(cs + p.sk_eps);
-  }
-  if (ce >= 0 && ce < kN * kN) p.comb_out[r * kN * kN + ce] = a;
+  float sc_l, base_l;
+  coeff_lane_scale_base(p.e, L, &sc_l, &base_l);  // early: they arrive with the partials
+  int slot;
+  const float v = coeff_row(p.e, r, L, sc_l, base_l, &slot);
+  if (slot >= 0 && slot < kN) p.pre_out[r * kN + slot] = v;
+  else if (slot >= kN && slot < 2 * kN) p.post_out[r * kN + slot - kN] = v;
+  else if (slot >= 2 * kN) p.comb_out[r * kN * kN + slot - 2 * kN] = v;
 }
 
 void pre_plan(int rows, int hidden, int* ks_count, int* steps_per_wg, int* rows_pad) {
@@ -228,7 +185,24 @@ size_t pre_scratch_floats_for(int rows, int hidden) {
   return (size_t)ks * rp * kPartW;
 }
 
-hipError_t launch_pre_coeffs(const PreLaunch& L, hipStream_t stream) {
+CoeffEpilogue pre_epilogue_args(const PreLaunch& L) {
+  int ks, spw, rp;
+  pre_plan(L.rows, L.hidden, &ks, &spw, &rp);
+  CoeffEpilogue e;
+  e.part = L.part;
+  e.scale = L.scale;
+  e.base = L.base;
+  e.ks_count = ks;
+  e.K = kN * L.hidden;
+  e.rms_eps = L.rms_eps;
+  e.pre_eps = L.pre_eps;
+  e.sk_eps = L.sinkhorn_eps;
+  e.alpha = L.post_alpha;
+  e.iters = L.sinkhorn_iters;
+  return e;
+}
+
+hipError_t launch_pre_partial(const PreLaunch& L, hipStream_t stream) {
   int ks, spw, rp;
   pre_plan(L.rows, L.hidden, &ks, &spw, &rp);
   if (spw > kMaxStepsPerWg) return hipErrorInvalidConfiguration;
@@ -243,25 +217,23 @@ hipError_t launch_pre_coeffs(const PreLaunch& L, hipStream_t stream) {
   a.nsteps = a.K / kStepK;
   const int grid = ks * (rp / kRB);
   hipLaunchKernelGGL(pre_partial_kernel, dim3(grid), dim3(kPreWaves * kWave), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_pre_epilogue(const PreLaunch& L, hipStream_t stream) {
   PreEpilogueParams b;
-  b.part = L.part;
-  b.scale = L.scale;
-  b.base = L.base;
+  b.e = pre_epilogue_args(L);
   b.pre_out = L.pre_out;
   b.post_out = L.post_out;
   b.comb_out = L.comb_out;
-  b.rms_eps = L.rms_eps;
-  b.pre_eps = L.pre_eps;
-  b.sk_eps = L.sinkhorn_eps;
-  b.alpha = L.post_alpha;
-  b.iters = L.sinkhorn_iters;
-  b.rows = L.rows;
-  b.K = a.K;
-  b.ks_count = ks;
   hipLaunchKernelGGL(pre_epilogue_kernel, dim3(L.rows), dim3(kWave), 0, stream, b);
   return hipGetLastError();
+}
+
+hipError_t launch_pre_coeffs(const PreLaunch& L, hipStream_t stream) {
+  hipError_t e = launch_pre_partial(L, stream);
+  if (e != hipSuccess) return e;
+  return launch_pre_epilogue(L, stream);
 }
 
 }  // namespace mhc

@@ -18,7 +18,8 @@ def test_header_declares_the_entry_points():
     names = binding.header_functions()
     for want in ("mhc_create", "mhc_destroy", "mhc_reset", "mhc_set_option", "mhc_boundary",
                  "mhc_residual_only", "mhc_finalize", "mhc_collapse_mean", "mhc_pre_coeffs",
-                 "mhc_status_string", "mhc_get_errors", "mhc_first", "mhc_collapse_norm"):
+                 "mhc_status_string", "mhc_get_errors", "mhc_first", "mhc_collapse_norm",
+                 "mhc_pre_coeffs_deferred", "mhc_pre_coeffs_flush"):
         assert want in names
 
 
@@ -72,5 +73,7 @@ def test_null_handle_is_invalid_everywhere():
     assert lib.mhc_finalize(z, z, 1, z, z, z, z, z, z, z, z, 0.0, 1, z, z, z, z, z) == 1
     assert lib.mhc_collapse_mean(z, z, 1, z, z) == 1
     assert lib.mhc_pre_coeffs(z, z, z, z, z, 0.0, 0.0, 0.0, 2.0, 20, 1, z, z, z, z) == 1
+    assert lib.mhc_pre_coeffs_deferred(z, z, z, z, z, 0.0, 0.0, 0.0, 2.0, 20, 1, z, z, z, z) == 1
+    assert lib.mhc_pre_coeffs_flush(z, z) == 1
     assert lib.mhc_first(z, z, z, 0.0, 1, z, z, z, z, z) == 1
     assert lib.mhc_collapse_norm(z, z, z, z, 0.0, 1, z, z, z, z) == 1

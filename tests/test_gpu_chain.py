@@ -145,3 +145,36 @@ def test_side_stream_and_standin_leave_the_boundaries_unchanged():
         torch.cuda.synchronize()
     assert plain.h.errors() == 0
 
+
+def test_deferred_coefficients_leave_the_step_unchanged():
+    """Every coefficient call deferred to the boundary that consumes it: the step's streams
+    and mean equal the plain step's bit for bit (eager and graph replay)."""
+    say("case: chained step, 3 layers: deferred coefficient calls")
+    plain = chain.DecodeChain.from_synth(DEV, layers=3)
+    want_mean = N(plain.run())
+    want_streams = N(plain.streams)
+    want_coeffs = [N(plain.pre), N(plain.post), N(plain.comb)]
+    dfr = chain.DecodeChain(plain.h, plain.emb, plain.subs, plain.p, DEV, deferred=True)
+    assert np.array_equal(N(dfr.run()), want_mean)
+    torch.cuda.synchronize()
+    assert np.array_equal(N(dfr.streams), want_streams)
+    for a, b in zip((dfr.pre, dfr.post, dfr.comb), want_coeffs):
+        assert np.array_equal(N(a), b)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dfr.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        out = dfr.run()
+    for rep in range(2):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(N(out), want_mean), f"replay {rep}"
+        plain.run()
+        torch.cuda.synchronize()
+    assert plain.h.errors() == 0
+
