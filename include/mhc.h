@@ -77,10 +77,10 @@ const char* mhc_status_string(int status);
  *   max_rows in [1, 65536], max_tp in [1, 64], top_k in [1, 64]  else MHC_ERR_SHAPE
  *   device   a valid HIP device index                     else MHC_ERR_HIP
  * Allocates the handle's device scratch on `device` (hipMalloc) and zeroes it
- * (synchronously) and picks the boundary block size (128, else 256, else 512:
- * the first whose row fits half an XCD's resident workgroups and one polling
- * wave); MHC_ERR_UNSUPPORTED if none does. The finalize kernels default to 256
- * when it fits (else the same size). On failure *out is set to NULL.
+ * (synchronously) and picks the boundary block sizes: for calls of up to 32
+ * rows 128, else 256, else 512 (the first whose row fits half an XCD's resident
+ * workgroups and one polling wave; MHC_ERR_UNSUPPORTED if none does); for more
+ * rows 256 when it fits (else the same size). On failure *out is set to NULL.
  * The sizes are checked before any HIP call.
  */
 int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int device,
@@ -91,8 +91,8 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
  * that a spin limit too small to cover the row handoff makes it give up, see
  * above). Takes effect for calls issued afterwards.
  *   MHC_OPT_BOUNDARY_BLOCK: threads per workgroup of the boundary kernels that write a
- *     layer input, 128, 256 or 512, for the TP-partial and the finalize kernels alike
- *     (default: see mhc_create). Each thread owns 8 hidden
+ *     layer input, 128, 256 or 512, for every call and row count (default: chosen
+ *     per call from the row count, see mhc_create). Each thread owns 8 hidden
  *     elements of a row, so a row is split into ceil(H / (8 * block)) workgroups; a size
  *     giving more than 64 of them, or more than half an XCD's resident workgroups, is
  *     MHC_ERR_UNSUPPORTED. (The residual-only kernels use 256 threads, four per 8

@@ -16,8 +16,9 @@ constexpr int kMaxTp = 64;
 constexpr int kMaxTopK = 64;
 constexpr int kMaxSinkhornIters = 1000;
 constexpr int kMinBlock = 128;      // smallest boundary workgroup: the most chunks per row
-constexpr int kDefaultBlock = 128;
-constexpr int kDefaultFinalizeBlock = 256;
+constexpr int kDefaultBlock = 128;   // up to kSmallRows rows
+constexpr int kManyRowsBlock = 256;
+constexpr int kSmallRows = 32;
 constexpr int kMaxChunks = 64;      // one polling lane per chunk
 constexpr int kMaxHidden = 65536;   // chunks per row at the largest block stay <= one wave
 constexpr int kDefaultSpinLimit = 1 << 20;
@@ -27,8 +28,9 @@ constexpr int kDefaultSpinLimit = 1 << 20;
 struct mhc_ctx {
   int hidden, hc_mult, max_rows, max_tp, top_k, device;
   int slot_stride;         // handoff words per row (chunks at the smallest block)
-  int block;               // layer-input workgroup size of the TP-partial boundary
-  int block_fin;           // ... and of the finalize boundary (equal once the option is set)
+  int block;               // layer-input workgroup size for up to kSmallRows rows (auto)
+  int block_many;          // ... for more rows (auto)
+  int block_set;           // the size MHC_OPT_BOUNDARY_BLOCK set, 0: automatic
   int spin_limit;          // polls before a handoff wait gives up
   int wgs_per_xcd[3];      // resident layer-input workgroups per XCD at block 128 / 256 / 512
   size_t pre_floats;       // coefficient-path scratch
@@ -93,7 +95,7 @@ int check_mix(const mhc_ctx* h, const uint16_t* residual, const float* post, con
   return MHC_OK;
 }
 
-void fill_mix(const mhc_ctx* h, mhc::BoundaryLaunch& L, bool finalize, const uint16_t* residual,
+void fill_mix(const mhc_ctx* h, mhc::BoundaryLaunch& L, const uint16_t* residual,
               const float* post, const float* comb, const float* pre, const uint16_t* norm_weight,
               float norm_eps, int rows, uint16_t* residual_out, uint16_t* layer_input_out,
               uint8_t* mx_data_out, uint8_t* mx_scale_out) {
@@ -114,7 +116,7 @@ void fill_mix(const mhc_ctx* h, mhc::BoundaryLaunch& L, bool finalize, const uin
   L.errors = h->errors;
   L.slot_stride = h->slot_stride;
   L.spin_limit = h->spin_limit;
-  const int block = finalize ? h->block_fin : h->block;
+  const int block = h->block_set ? h->block_set : (rows > kSmallRows ? h->block_many : h->block);
   L.max_wgs_per_xcd = h->wgs_per_xcd[block_index(block)];
   L.block = block;
 }
@@ -228,8 +230,9 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
     (void)hipSetDevice(prev);
     return MHC_ERR_UNSUPPORTED;
   }
-  // the finalize kernels run fastest at 256 threads (measured at 64 rows, top_k 8)
-  h->block_fin = block_usable(h, kDefaultFinalizeBlock) ? kDefaultFinalizeBlock : h->block;
+  // above kSmallRows rows 256 threads run faster (measured at hidden 7168, 32 to 512 rows)
+  h->block_many = block_usable(h, kManyRowsBlock) ? kManyRowsBlock : h->block;
+  h->block_set = 0;
   size_t pre_floats = 0;
   for (int r = 1; r <= max_rows; r += 16) {  // the split plan changes only every 16 rows
     const size_t f = mhc::pre_scratch_floats_for(r, hidden);
@@ -273,8 +276,7 @@ int mhc_set_option(mhc_handle h, int option, int value) {
     case MHC_OPT_BOUNDARY_BLOCK:
       if (block_index(value) < 0) return MHC_ERR_SHAPE;
       if (!block_usable(h, value)) return MHC_ERR_UNSUPPORTED;
-      h->block = value;
-      h->block_fin = value;
+      h->block_set = value;
       return MHC_OK;
     case MHC_OPT_SPIN_LIMIT:
       if (value < 0) return MHC_ERR_SHAPE;
@@ -337,7 +339,7 @@ int mhc_boundary(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_
   mhc::BoundaryLaunch L = {};
   L.x_partials = x_partials;
   L.tp = tp;
-  fill_mix(h, L, false, residual, post, comb, pre, norm_weight, norm_eps, rows, residual_out,
+  fill_mix(h, L, residual, post, comb, pre, norm_weight, norm_eps, rows, residual_out,
            layer_input_out, mx_data_out, mx_scale_out);
   st = take_pending(h, L, post, comb, pre, rows, static_cast<hipStream_t>(stream));
   if (st != MHC_OK) return st;
@@ -378,7 +380,7 @@ int mhc_finalize(mhc_handle h, const uint16_t* gemm2_permuted, int num_permuted,
   L.idx = expanded_idx_to_permuted_idx;
   L.shared_output = shared_output;
   L.top_k = h->top_k;
-  fill_mix(h, L, true, residual, post, comb, pre, norm_weight, norm_eps, rows, residual_out,
+  fill_mix(h, L, residual, post, comb, pre, norm_weight, norm_eps, rows, residual_out,
            layer_input_out, mx_data_out, mx_scale_out);
   st = take_pending(h, L, post, comb, pre, rows, static_cast<hipStream_t>(stream));
   if (st != MHC_OK) return st;
@@ -404,7 +406,7 @@ int mhc_first(mhc_handle h, const uint16_t* x, const uint16_t* norm_weight, floa
   mhc::BoundaryLaunch L = {};
   st = flush_pending(h, static_cast<hipStream_t>(stream));
   if (st != MHC_OK) return st;
-  fill_mix(h, L, false, nullptr, nullptr, nullptr, nullptr, norm_weight, norm_eps, rows,
+  fill_mix(h, L, nullptr, nullptr, nullptr, nullptr, norm_weight, norm_eps, rows,
            residual_out, layer_input_out, mx_data_out, mx_scale_out);
   L.x_partials = x;
   L.tp = 1;
@@ -431,7 +433,7 @@ int mhc_collapse_norm(mhc_handle h, const uint16_t* residual, const float* pre,
   mhc::BoundaryLaunch L = {};
   st = flush_pending(h, static_cast<hipStream_t>(stream));
   if (st != MHC_OK) return st;
-  fill_mix(h, L, false, residual, nullptr, nullptr, pre, norm_weight, norm_eps, rows, nullptr,
+  fill_mix(h, L, residual, nullptr, nullptr, pre, norm_weight, norm_eps, rows, nullptr,
            out, mx_data_out, mx_scale_out);
   L.mode = mhc::kBoundaryHead;
   return launch_status(mhc::launch_boundary(L, static_cast<hipStream_t>(stream)));
