@@ -274,6 +274,9 @@ int mhc_pre_coeffs(mhc_handle h, const uint16_t* residual, const uint16_t* fn,
  * handle, a mhc_pre_coeffs or mhc_pre_coeffs_deferred call included, first enqueues the
  * pending epilogue as mhc_pre_coeffs would have. Until then the outputs are not
  * written: a caller that reads them otherwise calls mhc_pre_coeffs_flush first.
+ * scale, base and the three outputs are used when that later call runs, so they must
+ * stay allocated until it has (the streams and fn only until this call has run).
+ * mhc_destroy drops a pending call unwritten.
  * Errors: as mhc_pre_coeffs (a failing call records nothing).
  */
 int mhc_pre_coeffs_deferred(mhc_handle h, const uint16_t* residual, const uint16_t* fn,
