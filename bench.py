@@ -234,6 +234,16 @@ def main():
                     "consumes (no epilogue launch)"}
         log(f"  chain deferred {out['chain_decode_step_deferred']}")
         del s3
+        s4 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, fused=True)
+        e4, g4 = time_calls(torch, [s4.run], k, 2)
+        out["chain_decode_step_fused"] = {
+            "us_per_step": round(g4, 1), "us_per_step_eager": None if e4 is None else round(e4, 1),
+            "algorithmic_bytes": int(s4.algorithmic_bytes()),
+            "gb_per_s": round(s4.algorithmic_bytes() / g4 / 1e3, 1),
+            "note": "each boundary and the coefficient call after it in one kernel "
+                    "(mhc_boundary_coeffs / mhc_finalize_coeffs)"}
+        log(f"  chain fused {out['chain_decode_step_fused']}")
+        del s4
         for side in (False, True):
             s2 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, standin=True,
                                        side_stream=side)
@@ -247,6 +257,85 @@ def main():
             log(f"  {name} {out[name]}")
             del s2
         del step
+        return out
+
+    def fused_rows(h):
+        Rc, nc = 128, 24
+        cq = synth.pre_inputs(12, rows=1, hidden=H)
+        nxt = {"fn": T(cq["fn"]), "scale": T(cq["scale"]), "base": T(cq["base"]),
+               "rms_eps": cq["rms_eps"], "pre_eps": cq["pre_eps"],
+               "sinkhorn_eps": cq["sinkhorn_eps"], "post_alpha": cq["post_alpha"],
+               "sinkhorn_iters": cq["sinkhorn_iters"]}
+        extra = 4 * H * nc * 2 + (3 + nc) * 4 + Rc * nc * 4  # fn, scale/base, coefficients
+        out = {}
+        for kind in ("boundary", "finalize"):
+            mx = kind == "finalize"
+            if kind == "boundary":
+                d = synth.boundary_inputs(11, rows=Rc, hidden=H, tp=TP, x_sigma=0.5)
+                nb = bytes_boundary(Rc, H, TP, mxfp8=mx)
+            else:
+                d = synth.finalize_inputs(13, rows=Rc, hidden=H, top_k=8)
+                nb = bytes_finalize(Rc, H, 8, mxfp8=mx)
+            ns = n_sets(nb)
+            co = {k: T(d[k]) for k in ("post", "comb", "pre", "norm_weight")}
+            src = {k: T(d[k]) for k in ("x_partials", "gemm2_permuted", "shared_output")
+                   if k in d}
+            small = {k: T(d[k]) for k in ("expert_weights", "expanded_idx_to_permuted_idx")
+                     if k in d}
+            res = T(d["residual"])
+            bufs = []
+            for _ in range(ns):
+                b = {k: v.clone() for k, v in src.items()}
+                b["s"] = res.clone()
+                b["li"] = torch.empty((Rc, H), dtype=torch.bfloat16, device=dev)
+                b["mx"] = ((torch.empty((Rc, H), dtype=torch.uint8, device=dev),
+                            torch.empty((Rc, H // 32), dtype=torch.uint8, device=dev))
+                           if mx else None)
+                b["nx"] = (torch.empty((Rc, 4), device=dev), torch.empty((Rc, 4), device=dev),
+                           torch.empty((Rc, 4, 4), device=dev))
+                bufs.append(b)
+
+            def fused(b):
+                kw = dict(mxfp8=mx, residual_out=b["s"], layer_input_out=b["li"],
+                          mx_out=b["mx"], next_out=b["nx"])
+                if kind == "boundary":
+                    return binding.boundary_coeffs(h, b["x_partials"], b["s"], co["post"],
+                                                   co["comb"], co["pre"], co["norm_weight"],
+                                                   d["eps"], nxt, **kw)
+                return binding.finalize_coeffs(h, b["gemm2_permuted"], small["expert_weights"],
+                                               small["expanded_idx_to_permuted_idx"],
+                                               b["shared_output"], b["s"], co["post"],
+                                               co["comb"], co["pre"], co["norm_weight"],
+                                               d["eps"], nxt, **kw)
+
+            def two(b):
+                kw = dict(mxfp8=mx, residual_out=b["s"], layer_input_out=b["li"], mx_out=b["mx"])
+                if kind == "boundary":
+                    binding.boundary(h, b["x_partials"], b["s"], co["post"], co["comb"],
+                                     co["pre"], co["norm_weight"], d["eps"], **kw)
+                else:
+                    binding.finalize(h, b["gemm2_permuted"], small["expert_weights"],
+                                     small["expanded_idx_to_permuted_idx"], b["shared_output"],
+                                     b["s"], co["post"], co["comb"], co["pre"],
+                                     co["norm_weight"], d["eps"], **kw)
+                binding.pre_coeffs(h, b["s"], nxt["fn"], nxt["scale"], nxt["base"],
+                                   nxt["rms_eps"], nxt["pre_eps"], nxt["sinkhorn_eps"],
+                                   nxt["post_alpha"], nxt["sinkhorn_iters"], out=b["nx"])
+
+            e, g = time_calls(torch, [(lambda b=b: fused(b)) for b in bufs], args.steps,
+                              args.warmup)
+            name = f"{kind}_coeffs_r128" + ("_mxfp8" if mx else "")
+            out[name] = row_entry(name, nb + extra, e, g, ns)
+            out[name]["note"] = ("boundary + the next coefficient call in one kernel "
+                                 "(no second read of the streams)")
+            log(f"  {name} {out[name]}")
+            e, g = time_calls(torch, [(lambda b=b: two(b)) for b in bufs], args.steps,
+                              args.warmup)
+            name2 = f"{kind}_then_coeffs_r128" + ("_mxfp8" if mx else "")
+            out[name2] = row_entry(name2, nb + extra + Rc * 4 * H * 2, e, g, ns)
+            out[name2]["note"] = "the same work as two calls (boundary, then mhc_pre_coeffs)"
+            log(f"  {name2} {out[name2]}")
+            del bufs
         return out
 
     if args.chain_only:
@@ -396,6 +485,11 @@ def main():
         rows["collapse_mean_r128"] = row_entry("collapse_mean", nm, e, g, s5)
         log(f"  collapse_mean {rows['collapse_mean_r128']}")
         del bufs, calls
+
+        # the boundary fused with the next coefficient call, against the two calls, at the
+        # chained step's 128 rows: the attention boundary (TP partials, bf16 layer input) and
+        # the MoE boundary (finalize, MXFP8 layer input)
+        rows.update(fused_rows(h))
 
     if not args.no_chain and not args.no_rows:
         rows.update(chain_rows())

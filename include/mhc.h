@@ -292,6 +292,66 @@ int mhc_pre_coeffs_deferred(mhc_handle h, const uint16_t* residual, const uint16
  */
 int mhc_pre_coeffs_flush(mhc_handle h, mhc_stream_t stream);
 
+/*
+ * The arguments of a coefficient call (as mhc_pre_coeffs) carried by the fused calls
+ * below. A host struct, read during the call only; the pointers are device pointers
+ * with mhc_pre_coeffs's layouts and alignments.
+ */
+typedef struct mhc_coeff_args {
+  const uint16_t* fn;       /* [n*H, 2n + n*n] bf16 row-major, 16-byte aligned */
+  const float* scale;       /* [3] */
+  const float* base;        /* [2n + n*n] */
+  float rms_eps, pre_eps, sinkhorn_eps, post_alpha;
+  int sinkhorn_iters;       /* [0, 1000] */
+  float* pre_out;           /* [R, n] */
+  float* post_out;          /* [R, n] */
+  float* comb_out;          /* [R, n, n] */
+} mhc_coeff_args;
+
+/*
+ * mhc_boundary_coeffs -- mhc_boundary followed by mhc_pre_coeffs on its new streams, in
+ * one kernel.
+ *
+ * boundary page, Boundaries.sublayer: a sublayer's boundary returns the new streams and
+ * the next sublayer's input, and the next coefficient call (Boundaries._pre) runs on
+ * those streams. This call computes exactly what
+ *   mhc_boundary(h, x_partials, tp, residual, post, comb, pre, norm_weight, norm_eps,
+ *                rows, residual_out, layer_input_out, mx_data_out, mx_scale_out, s);
+ *   mhc_pre_coeffs(h, residual_out, next->fn, next->scale, next->base, next->rms_eps,
+ *                  next->pre_eps, next->sinkhorn_eps, next->post_alpha,
+ *                  next->sinkhorn_iters, rows, next->pre_out, next->post_out,
+ *                  next->comb_out, s);
+ * compute, but the projection is taken from the new streams while they are in
+ * registers (no second read of the streams, no separate launches). The new streams are
+ * bit-identical to mhc_boundary's; the layer input, its MXFP8 form and the coefficients
+ * differ from the two calls' by the order of their sums only (the row sums are split
+ * into 256-element pieces). A layer input is required (pre, norm_weight and
+ * layer_input_out non-NULL). Arguments, layouts, aliasing and errors as the two calls,
+ * plus MHC_ERR_INVALID_ARG for a NULL `next`; next's outputs must not overlap any other
+ * argument. The single kernel runs when rows <= min(max_rows, 1024), post, comb and pre
+ * are 16-byte aligned and a row's 256-element pieces fit the workgroups one XCD holds at
+ * once (H <= 8192 on MI355X); otherwise the call runs the two calls (same results as
+ * above). A pending deferred coefficient call is enqueued first.
+ */
+int mhc_boundary_coeffs(mhc_handle h, const uint16_t* x_partials, int tp,
+                        const uint16_t* residual, const float* post, const float* comb,
+                        const float* pre, const uint16_t* norm_weight, float norm_eps, int rows,
+                        uint16_t* residual_out, uint16_t* layer_input_out, uint8_t* mx_data_out,
+                        uint8_t* mx_scale_out, const mhc_coeff_args* next, mhc_stream_t stream);
+
+/*
+ * mhc_finalize_coeffs -- mhc_finalize followed by mhc_pre_coeffs on its new streams, in
+ * one kernel: as mhc_boundary_coeffs with mhc_finalize's sublayer-output arguments
+ * (all_reduce page, BoundaryAllReduce finalize; boundary page, Boundaries.sublayer).
+ */
+int mhc_finalize_coeffs(mhc_handle h, const uint16_t* gemm2_permuted, int num_permuted,
+                        const float* expert_weights, const int32_t* expanded_idx_to_permuted_idx,
+                        const uint16_t* shared_output, const uint16_t* residual,
+                        const float* post, const float* comb, const float* pre,
+                        const uint16_t* norm_weight, float norm_eps, int rows,
+                        uint16_t* residual_out, uint16_t* layer_input_out, uint8_t* mx_data_out,
+                        uint8_t* mx_scale_out, const mhc_coeff_args* next, mhc_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

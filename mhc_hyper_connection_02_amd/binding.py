@@ -30,6 +30,13 @@ _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
 
+class CoeffArgs(ctypes.Structure):
+    """``mhc_coeff_args``: a coefficient call's arguments, for the fused calls."""
+    _fields_ = [("fn", _vp), ("scale", _vp), ("base", _vp), ("rms_eps", _f), ("pre_eps", _f),
+                ("sinkhorn_eps", _f), ("post_alpha", _f), ("sinkhorn_iters", _i),
+                ("pre_out", _vp), ("post_out", _vp), ("comb_out", _vp)]
+
+
 _SIGS = {
     "mhc_status_string": ([_i], ctypes.c_char_p),
     "mhc_create": ([_i, _i, _i, _i, _i, _i, ctypes.POINTER(_vp)], _i),
@@ -48,6 +55,10 @@ _SIGS = {
     "mhc_pre_coeffs_deferred": ([_vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f, _i, _i, _vp, _vp, _vp,
                                  _vp], _i),
     "mhc_pre_coeffs_flush": ([_vp, _vp], _i),
+    "mhc_boundary_coeffs": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _f, _i, _vp, _vp, _vp, _vp,
+                             ctypes.POINTER(CoeffArgs), _vp], _i),
+    "mhc_finalize_coeffs": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _i, _vp,
+                             _vp, _vp, _vp, ctypes.POINTER(CoeffArgs), _vp], _i),
 }
 
 
@@ -381,3 +392,84 @@ def pre_coeffs(h, residual, fn, scale, base, rms_eps, pre_eps, sinkhorn_eps, pos
 def pre_coeffs_flush(h, stream=None):
     """``mhc_pre_coeffs_flush``: complete a pending deferred coefficient call."""
     _check(load_library().mhc_pre_coeffs_flush(h.ptr, _stream(stream)), "mhc_pre_coeffs_flush")
+
+
+def _coeff_args(h, rows, dev, nxt, out):
+    """Check a coefficient call's arguments (a dict with fn, scale, base, rms_eps, pre_eps,
+    sinkhorn_eps, post_alpha, sinkhorn_iters) and its outputs; -> (CoeffArgs, outputs)."""
+    n, hidden = h.hc_mult, h.hidden
+    nc = 2 * n + n * n
+    _need(nxt["fn"], "fn", torch.bfloat16, (n * hidden, nc), dev)
+    _need(nxt["scale"], "scale", torch.float32, (3,), dev)
+    _need(nxt["base"], "base", torch.float32, (nc,), dev)
+    if out is None:
+        out = (torch.empty((rows, n), dtype=torch.float32, device=dev),
+               torch.empty((rows, n), dtype=torch.float32, device=dev),
+               torch.empty((rows, n, n), dtype=torch.float32, device=dev))
+    pre, post, comb = out
+    _need(pre, "next pre_out", torch.float32, (rows, n), dev)
+    _need(post, "next post_out", torch.float32, (rows, n), dev)
+    _need(comb, "next comb_out", torch.float32, (rows, n, n), dev)
+    a = CoeffArgs(_ptr(nxt["fn"]), _ptr(nxt["scale"]), _ptr(nxt["base"]), float(nxt["rms_eps"]),
+                  float(nxt["pre_eps"]), float(nxt["sinkhorn_eps"]), float(nxt["post_alpha"]),
+                  int(nxt["sinkhorn_iters"]), _ptr(pre), _ptr(post), _ptr(comb))
+    return a, out
+
+
+def boundary_coeffs(h, x_partials, residual, post, comb, pre, norm_weight, eps, nxt,
+                    mxfp8=False, residual_out=None, layer_input_out=None, mx_out=None,
+                    next_out=None, stream=None):
+    """``mhc_boundary_coeffs``: :func:`boundary` and then :func:`pre_coeffs` on its new streams
+    with the arguments in ``nxt`` (a dict), in one kernel. Returns boundary's dict plus
+    ``next`` = (pre, post, comb) of the next sublayer."""
+    rows, n, hidden, dev = _check_mix_inputs(h, residual, post, comb)
+    if x_partials.dim() != 3:
+        raise ValueError("x_partials must be [tp, rows, hidden]")
+    tp = x_partials.shape[0]
+    _need(x_partials, "x_partials", torch.bfloat16, (tp, rows, hidden), dev)
+    if pre is None:
+        raise ValueError("the fused call writes a layer input: pre is required")
+    ro, li, md, ms = _mix_outputs(h, residual, pre, norm_weight, mxfp8, residual_out,
+                                  layer_input_out, mx_out)
+    a, nout = _coeff_args(h, rows, dev, nxt, next_out)
+    st = load_library().mhc_boundary_coeffs(h.ptr, _ptr(x_partials), tp, _ptr(residual),
+                                            _ptr(post), _ptr(comb), _ptr(pre),
+                                            _ptr(norm_weight), float(eps), rows, _ptr(ro),
+                                            _ptr(li), _ptr(md), _ptr(ms), ctypes.byref(a),
+                                            _stream(stream))
+    _check(st, "mhc_boundary_coeffs")
+    res = _result(ro, li, md, ms)
+    res["next"] = nout
+    return res
+
+
+def finalize_coeffs(h, gemm2_permuted, expert_weights, expanded_idx_to_permuted_idx,
+                    shared_output, residual, post, comb, pre, norm_weight, eps, nxt,
+                    mxfp8=False, residual_out=None, layer_input_out=None, mx_out=None,
+                    next_out=None, stream=None):
+    """``mhc_finalize_coeffs``: :func:`finalize` and then :func:`pre_coeffs` on its new
+    streams, in one kernel; returns as :func:`boundary_coeffs`."""
+    rows, n, hidden, dev = _check_mix_inputs(h, residual, post, comb)
+    if gemm2_permuted.dim() != 2:
+        raise ValueError("gemm2_permuted must be [num_permuted, hidden]")
+    P = gemm2_permuted.shape[0]
+    _need(gemm2_permuted, "gemm2_permuted", torch.bfloat16, (P, hidden), dev)
+    _need(expert_weights, "expert_weights", torch.float32, (rows, h.top_k), dev)
+    _need(expanded_idx_to_permuted_idx, "expanded_idx_to_permuted_idx", torch.int32,
+          (rows * h.top_k,), dev)
+    _need(shared_output, "shared_output", torch.bfloat16, (rows, hidden), dev)
+    if pre is None:
+        raise ValueError("the fused call writes a layer input: pre is required")
+    ro, li, md, ms = _mix_outputs(h, residual, pre, norm_weight, mxfp8, residual_out,
+                                  layer_input_out, mx_out)
+    a, nout = _coeff_args(h, rows, dev, nxt, next_out)
+    st = load_library().mhc_finalize_coeffs(h.ptr, _ptr(gemm2_permuted), P, _ptr(expert_weights),
+                                            _ptr(expanded_idx_to_permuted_idx),
+                                            _ptr(shared_output), _ptr(residual), _ptr(post),
+                                            _ptr(comb), _ptr(pre), _ptr(norm_weight), float(eps),
+                                            rows, _ptr(ro), _ptr(li), _ptr(md), _ptr(ms),
+                                            ctypes.byref(a), _stream(stream))
+    _check(st, "mhc_finalize_coeffs")
+    res = _result(ro, li, md, ms)
+    res["next"] = nout
+    return res

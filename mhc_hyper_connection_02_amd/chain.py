@@ -26,6 +26,11 @@ computes on the layer input, joined before the next boundary. With
 ``standin=True`` each sublayer is stood in for by one bf16 GEMM of the layer input
 ([R, H] x [H, H], a projection's worth of work, outside the hot path and its
 result unused), so that the overlap has something to hide under.
+
+Fused (``fused=True``): each boundary that is followed by a coefficient call runs as one
+call with it (``mhc_boundary_coeffs`` / ``mhc_finalize_coeffs``), which reads the current
+coefficients and writes the next ones in the same kernel, so the step alternates between
+two coefficient buffer sets.
 """
 
 import torch
@@ -35,7 +40,7 @@ from . import binding, synth
 
 class DecodeChain:
     def __init__(self, handle, embedding, sublayers, params, device, standin=False,
-                 side_stream=False, deferred=False):
+                 side_stream=False, deferred=False, fused=False):
         """embedding: [R,H] bf16 tensor; sublayers: list of dicts of device tensors as built by
         :meth:`from_synth`; params: rms_eps, hc_eps, post_alpha, sinkhorn_iters, norm_eps."""
         self.h = handle
@@ -55,6 +60,20 @@ class DecodeChain:
         self.mean = torch.empty((R, H), dtype=torch.bfloat16, device=device)
         # deferred coefficient calls: each boundary finishes the coefficients it consumes
         self.deferred = deferred
+        # fused: boundary and coefficient call in one kernel, two coefficient sets
+        self.fused = fused
+        self.sets = [(self.pre, self.post, self.comb)]
+        if fused:
+            if deferred or side_stream:
+                raise ValueError("fused boundaries take neither deferred nor side-stream calls")
+            self.sets.append((torch.empty_like(self.pre), torch.empty_like(self.post),
+                              torch.empty_like(self.comb)))
+        self.next_args = [None if i + 1 == len(sublayers) else {
+            "fn": sublayers[i + 1]["fn"], "scale": sublayers[i + 1]["scale"],
+            "base": sublayers[i + 1]["base"], "rms_eps": params["rms_eps"],
+            "pre_eps": params["hc_eps"], "sinkhorn_eps": params["hc_eps"],
+            "post_alpha": params["post_alpha"], "sinkhorn_iters": params["sinkhorn_iters"]}
+            for i in range(len(sublayers))]
         self.side = torch.cuda.Stream(device=device) if side_stream else None
         self.standin_w = self.standin_out = None
         if standin:
@@ -71,7 +90,7 @@ class DecodeChain:
     @classmethod
     def from_synth(cls, device, layers=synth.CHAIN_LAYERS, rows=synth.CHAIN_ROWS,
                    hidden=synth.CHAIN_HIDDEN, tp=synth.CHAIN_TP, top_k=synth.CHAIN_TOP_K,
-                   handle=None, standin=False, side_stream=False, deferred=False):
+                   handle=None, standin=False, side_stream=False, deferred=False, fused=False):
         """The chained step on the seeded synthetic inputs (see ``synth.chain_sublayer``)."""
         T = lambda a: synth.to_torch(a, device)  # noqa: E731
         if handle is None:
@@ -91,7 +110,7 @@ class DecodeChain:
                     t["finalize"] = (T(g), T(w), T(idx), T(sh))
                 subs.append(t)
         return cls(handle, emb, subs, synth.chain_params(), device, standin=standin,
-                   side_stream=side_stream, deferred=deferred)
+                   side_stream=side_stream, deferred=deferred, fused=fused)
 
     def input_bytes(self):
         tot = self.emb.numel() * 2
@@ -114,6 +133,8 @@ class DecodeChain:
             tot += R * H + R * H // 32
         pre_call = R * n * H * 2 + n * H * nc * 2 + (3 + nc) * 4 + coef
         tot += pre_call                                       # first coefficients
+        if self.fused:  # the coefficient calls take the streams from the boundary's registers
+            pre_call -= R * n * H * 2
         for i, s in enumerate(self.subs):
             last = i + 1 == len(self.subs)
             nxt = None if last else self.subs[i + 1]
@@ -137,6 +158,8 @@ class DecodeChain:
         reduction, mean."""
         h, p = self.h, self.p
         first = self.subs[0]
+        cur = 0
+        self.pre, self.post, self.comb = self.sets[cur]
         binding.first(h, self.emb, first["norm_w"], p["norm_eps"], mxfp8=first["mxfp8"],
                       residual_out=self.streams, layer_input_out=self.layer_input,
                       mx_out=(self.mx_data, self.mx_scale) if first["mxfp8"] else None)
@@ -156,6 +179,22 @@ class DecodeChain:
                           mx_out=(self.mx_data, self.mx_scale) if nxt["mxfp8"] else None)
             if self.record is not None:
                 self.record(i, "before", self)
+            if self.fused and not last:
+                kw.update(residual_out=self.streams, next_out=self.sets[1 - cur])
+                if "partials" in s:
+                    binding.boundary_coeffs(h, s["partials"], self.streams, self.post, self.comb,
+                                            nxt=self.next_args[i], **kw)
+                else:
+                    g, w, idx, sh = s["finalize"]
+                    binding.finalize_coeffs(h, g, w, idx, sh, self.streams, self.post, self.comb,
+                                            nxt=self.next_args[i], **kw)
+                if self.record is not None:
+                    self.record(i, "after", self)
+                cur = 1 - cur
+                self.pre, self.post, self.comb = self.sets[cur]
+                if self.record is not None:
+                    self.record(i, "coeffs", self)
+                continue
             if "partials" in s:
                 binding.boundary(h, s["partials"], self.streams, self.post, self.comb,
                                  residual_out=self.streams, **kw)

@@ -22,6 +22,7 @@ constexpr int kSmallRows = 32;
 constexpr int kMaxChunks = 64;      // one polling lane per chunk
 constexpr int kMaxHidden = 65536;   // chunks per row at the largest block stay <= one wave
 constexpr int kDefaultSpinLimit = 1 << 20;
+constexpr int kTileMaxRows = 1024;  // rows of the fused boundary + coefficient scratch
 
 }  // namespace
 
@@ -33,13 +34,16 @@ struct mhc_ctx {
   int block_set;           // the size MHC_OPT_BOUNDARY_BLOCK set, 0: automatic
   int spin_limit;          // polls before a handoff wait gives up
   int wgs_per_xcd[3];      // resident layer-input workgroups per XCD at block 128 / 256 / 512
+  int tile_wgs_per_xcd;    // resident workgroups of the fused boundary + coefficient kernel
+  int tile_rows;           // rows the fused kernel's scratch covers (0: not available)
   size_t pre_floats;       // coefficient-path scratch
-  void* scratch;           // one allocation: slots | pre_part | epoch | errors
+  void* scratch;           // one allocation: slots | epoch | errors | tile_words | pre_part
   unsigned long long* slots;
   float* pre_part;
   unsigned* epoch;
   unsigned* errors;
-  size_t zero_words;       // 32-bit words of slots + epoch + errors (cleared by mhc_reset)
+  unsigned long long* tile_words;  // the fused kernel's tagged partials
+  size_t zero_words;       // 32-bit words up to pre_part (cleared by mhc_reset)
   // a deferred coefficient call whose epilogue has not been enqueued yet
   bool pending;
   mhc::PreLaunch pend;
@@ -240,11 +244,17 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   }
   h->pre_floats = pre_floats;
 
+  h->tile_wgs_per_xcd = mhc::boundary_tile_resident_wgs_per_cu() * (cus / 8);
+  h->tile_rows = mhc::boundary_tile_fits(hidden, h->tile_wgs_per_xcd)
+                     ? (max_rows < kTileMaxRows ? max_rows : kTileMaxRows)
+                     : 0;
+
   const size_t slot_bytes = round_up((size_t)max_rows * h->slot_stride * 8, 256);
   const size_t epoch_bytes = round_up((size_t)max_rows * 4, 256);
   const size_t err_bytes = 256;
+  const size_t tile_bytes = round_up(mhc::boundary_tile_words(h->tile_rows, hidden) * 8, 256);
   const size_t pre_bytes = round_up(pre_floats * sizeof(float), 256);
-  const size_t total = slot_bytes + epoch_bytes + err_bytes + pre_bytes;
+  const size_t total = slot_bytes + epoch_bytes + err_bytes + tile_bytes + pre_bytes;
   void* base = nullptr;
   if (hipMalloc(&base, total) != hipSuccess) {
     delete h;
@@ -256,8 +266,11 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   h->slots = reinterpret_cast<unsigned long long*>(b);
   h->epoch = reinterpret_cast<unsigned*>(b + slot_bytes);
   h->errors = reinterpret_cast<unsigned*>(b + slot_bytes + epoch_bytes);
-  h->pre_part = reinterpret_cast<float*>(b + slot_bytes + epoch_bytes + err_bytes);
-  h->zero_words = (slot_bytes + epoch_bytes + err_bytes) / 4;
+  h->tile_words =
+      reinterpret_cast<unsigned long long*>(b + slot_bytes + epoch_bytes + err_bytes);
+  h->pre_part =
+      reinterpret_cast<float*>(b + slot_bytes + epoch_bytes + err_bytes + tile_bytes);
+  h->zero_words = (slot_bytes + epoch_bytes + err_bytes + tile_bytes) / 4;
   hipError_t e = mhc::launch_fill_u32(reinterpret_cast<unsigned*>(base), total / 4, 0u, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   (void)hipSetDevice(prev);
@@ -453,6 +466,121 @@ int mhc_collapse_mean(mhc_handle h, const uint16_t* streams, int rows, uint16_t*
   if (st != MHC_OK) return st;
   return launch_status(
       mhc::launch_collapse_mean(streams, rows, h->hidden, out, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+int check_coeff_args(const mhc_ctx* h, const mhc_coeff_args* a) {
+  if (!a) return MHC_ERR_INVALID_ARG;
+  if (a->sinkhorn_iters < 0 || a->sinkhorn_iters > kMaxSinkhornIters) return MHC_ERR_SHAPE;
+  if (!(a->rms_eps >= 0.0f) || !(a->sinkhorn_eps >= 0.0f)) return MHC_ERR_SHAPE;
+  if (!a->fn || !a->scale || !a->base || !a->pre_out || !a->post_out || !a->comb_out)
+    return MHC_ERR_INVALID_ARG;
+  if (!aligned(a->fn, 16) || !aligned(a->scale, 4) || !aligned(a->base, 4) ||
+      !aligned(a->pre_out, 4) || !aligned(a->post_out, 4) || !aligned(a->comb_out, 4))
+    return MHC_ERR_ALIGN;
+  (void)h;
+  return MHC_OK;
+}
+
+// A boundary followed by the next coefficient call on its new streams: one kernel where
+// the fused form applies, else the two calls. L is the boundary's launch, already filled.
+int boundary_then_coeffs(mhc_ctx* h, mhc::BoundaryLaunch& L, const mhc_coeff_args* a,
+                         hipStream_t s) {
+  int st = flush_pending(h, s);
+  if (st != MHC_OK) return st;
+  const bool fused = h->tile_rows >= L.rows && aligned(L.post, 16) && aligned(L.comb, 16) &&
+                     aligned(L.pre, 16);
+  if (!fused) {
+    st = launch_status(mhc::launch_boundary(L, s));
+    if (st != MHC_OK) return st;
+    return mhc_pre_coeffs(h, L.residual_out, a->fn, a->scale, a->base, a->rms_eps, a->pre_eps,
+                          a->sinkhorn_eps, a->post_alpha, a->sinkhorn_iters, L.rows, a->pre_out,
+                          a->post_out, a->comb_out, s);
+  }
+  mhc::TileLaunch T;
+  T.b = L;
+  T.fn = a->fn;
+  T.coef = mhc::CoeffEpilogue{};
+  T.coef.scale = a->scale;
+  T.coef.base = a->base;
+  T.coef.K = h->hc_mult * h->hidden;
+  T.coef.rms_eps = a->rms_eps;
+  T.coef.pre_eps = a->pre_eps;
+  T.coef.sk_eps = a->sinkhorn_eps;
+  T.coef.alpha = a->post_alpha;
+  T.coef.iters = a->sinkhorn_iters;
+  T.next_pre = a->pre_out;
+  T.next_post = a->post_out;
+  T.next_comb = a->comb_out;
+  T.words = h->tile_words;
+  T.tile_rows = h->tile_rows;
+  T.wgs_per_xcd = h->tile_wgs_per_xcd;
+  return launch_status(mhc::launch_boundary_tile(T, s));
+}
+
+}  // namespace
+
+int mhc_boundary_coeffs(mhc_handle h, const uint16_t* x_partials, int tp,
+                        const uint16_t* residual, const float* post, const float* comb,
+                        const float* pre, const uint16_t* norm_weight, float norm_eps, int rows,
+                        uint16_t* residual_out, uint16_t* layer_input_out, uint8_t* mx_data_out,
+                        uint8_t* mx_scale_out, const mhc_coeff_args* next, mhc_stream_t stream) {
+  if (!h) return MHC_ERR_INVALID_ARG;
+  if (rows < 0 || tp < 1) return MHC_ERR_SHAPE;
+  if (rows > h->max_rows || tp > h->max_tp) return MHC_ERR_LIMIT;
+  if (rows == 0) return MHC_OK;
+  if (!x_partials || !pre) return MHC_ERR_INVALID_ARG;
+  int st = check_mix(h, residual, post, comb, pre, norm_weight, norm_eps, residual_out,
+                     layer_input_out, mx_data_out, mx_scale_out);
+  if (st != MHC_OK) return st;
+  if (!aligned(x_partials, 16)) return MHC_ERR_ALIGN;
+  st = check_coeff_args(h, next);
+  if (st != MHC_OK) return st;
+  st = check_device(h);
+  if (st != MHC_OK) return st;
+  mhc::BoundaryLaunch L = {};
+  L.x_partials = x_partials;
+  L.tp = tp;
+  fill_mix(h, L, residual, post, comb, pre, norm_weight, norm_eps, rows, residual_out,
+           layer_input_out, mx_data_out, mx_scale_out);
+  return boundary_then_coeffs(h, L, next, static_cast<hipStream_t>(stream));
+}
+
+int mhc_finalize_coeffs(mhc_handle h, const uint16_t* gemm2_permuted, int num_permuted,
+                        const float* expert_weights, const int32_t* expanded_idx_to_permuted_idx,
+                        const uint16_t* shared_output, const uint16_t* residual,
+                        const float* post, const float* comb, const float* pre,
+                        const uint16_t* norm_weight, float norm_eps, int rows,
+                        uint16_t* residual_out, uint16_t* layer_input_out, uint8_t* mx_data_out,
+                        uint8_t* mx_scale_out, const mhc_coeff_args* next, mhc_stream_t stream) {
+  if (!h) return MHC_ERR_INVALID_ARG;
+  if (rows < 0 || num_permuted < 1) return MHC_ERR_SHAPE;
+  if (rows > h->max_rows) return MHC_ERR_LIMIT;
+  if (rows == 0) return MHC_OK;
+  if (!gemm2_permuted || !expert_weights || !expanded_idx_to_permuted_idx || !shared_output ||
+      !pre)
+    return MHC_ERR_INVALID_ARG;
+  int st = check_mix(h, residual, post, comb, pre, norm_weight, norm_eps, residual_out,
+                     layer_input_out, mx_data_out, mx_scale_out);
+  if (st != MHC_OK) return st;
+  if (!aligned(gemm2_permuted, 16) || !aligned(shared_output, 16) || !aligned(expert_weights, 4) ||
+      !aligned(expanded_idx_to_permuted_idx, 4))
+    return MHC_ERR_ALIGN;
+  st = check_coeff_args(h, next);
+  if (st != MHC_OK) return st;
+  st = check_device(h);
+  if (st != MHC_OK) return st;
+  mhc::BoundaryLaunch L = {};
+  L.gemm2_permuted = gemm2_permuted;
+  L.num_permuted = num_permuted;
+  L.expert_weights = expert_weights;
+  L.idx = expanded_idx_to_permuted_idx;
+  L.shared_output = shared_output;
+  L.top_k = h->top_k;
+  fill_mix(h, L, residual, post, comb, pre, norm_weight, norm_eps, rows, residual_out,
+           layer_input_out, mx_data_out, mx_scale_out);
+  return boundary_then_coeffs(h, L, next, static_cast<hipStream_t>(stream));
 }
 
 namespace {

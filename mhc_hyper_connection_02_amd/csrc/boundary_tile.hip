@@ -1,0 +1,598 @@
+// The boundary fused with the next sublayer's coefficient call, for gfx950: one kernel
+// computes what mhc_boundary (or mhc_finalize) and then mhc_pre_coeffs on its new streams
+// compute, without the coefficient call's re-read of the streams or its launches.
+//
+// Pages: boundary page, Boundaries.sublayer (the boundary is followed by the next
+// sublayer's coefficient call on the streams it returns) and Boundaries._pre (that
+// call's arguments); the arithmetic of each step is stated in include/mhc.h.
+//
+// Work decomposition. A workgroup of 512 threads (8 waves) owns a tile of 16 rows by
+// 256 hidden elements (one chunk). Lane l of wave w owns row l % 16 of the tile and the
+// 8 elements of vector 4w + l / 16 of the chunk, with all four streams of them: the same
+// per-lane dataflow as the boundary's layer-input kernels (partial slices or gathered
+// expert rows, mHC post, collapse, RMSNorm, MXFP8), in the same arithmetic order, so the
+// new streams are bit-identical to mhc_boundary's.
+//
+// The projection. With this layout the 64 lanes of wave w hold, for each stream i, the
+// bf16 new streams of 16 rows by 32 consecutive elements: exactly the B operand of one
+// v_mfma_f32_16x16x32_bf16 (N = rows, K = 32 elements). The A operand is fn^T over the
+// same 32 elements of stream i, staged in LDS (the chunk's fn rows, 4 x 256 x 24 bf16,
+// copied with 16-byte loads and transposed to [logit][k]). Eight MFMAs per wave (4
+// streams x logits 0..15 and 16..31) give the wave's partial logits of its 16 rows; the
+// eight waves' partials are added in wave order in LDS. Only the bf16 values the call
+// stores enter the projection, as in mhc_pre_coeffs on the stored streams.
+//
+// The handoff. Every workgroup publishes, per row of its tile, 26 words: the partial sum
+// of y^2 (for the layer input's RMS), the 24 partial logits and the partial sum of the
+// new streams' squares (for the coefficients' RMS), each as a 64-bit word (call tag <<
+// 32 | fp32 bits, relaxed device-scope store). Wave 0 of every workgroup of the tile then
+// polls the y^2 words of its 16 rows across the row's chunks (four lanes per row, each
+// adding a contiguous quarter of the chunks in order; the quarters are added in order:
+// deterministic), and the layer input follows. Workgroup c of the tile also finishes the
+// coefficients of rows c, c + chunks, ... : lanes 0..24 of one wave read that row's 25
+// coefficient words across the chunks in chunk order and run the coefficient epilogue
+// (coeff_epilogue.h), writing the next pre, post and comb. Tags are the rows' epochs + 1
+// (the same epochs as the boundary's handoff); chunk 0 advances them once its poll has
+// seen every chunk's word, i.e. after every workgroup of the tile has read them.
+//
+// Co-residency and placement as the boundary's: a tile's chunks get workgroup ids
+// congruent mod 8 (one XCD, one L2), the grid holds at most the device's resident
+// capacity of this kernel, rows beyond it are walked in rounds, and every wait is bounded.
+#include "coeff_epilogue.h"
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mhc {
+
+namespace {
+
+constexpr int kN = 4;
+constexpr int kXcd = 8;
+constexpr int kTileRows = 16;
+constexpr int kTileWaves = 8;
+constexpr int kTileThreads = kTileWaves * kWave;          // 512
+constexpr int kTileVecs = kTileThreads / kTileRows;       // 32 vectors of a row per chunk
+constexpr int kTileH = kTileVecs * 8;                     // 256 elements per chunk
+constexpr int kWordsPerRow = 2 + kCoefNC;                 // y^2, 24 logits, v^2
+constexpr int kFnK = kN * kTileH;                         // 1024 k values per chunk
+constexpr int kFnLd = kFnK + 8;                           // padded LDS row of fn^T
+constexpr int kFnVecs = kFnK * kCoefNC / 8 / kTileThreads;  // 6 16-byte vectors per thread
+constexpr int kMaxTileChunks = 64;                        // 16 polled words per lane at most
+constexpr int kFinishBatch = 32;                          // coefficient words read at once
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct TileParams {
+  // sublayer output: TP partials ...
+  const uint4* xp;          // [tp][rows][hv]
+  int tp;
+  // ... or an unfinalized MoE output
+  const uint4* g;           // [num_permuted][hv]
+  const float* ew;          // [rows][top_k]
+  const int* idx;           // [rows * top_k]
+  const uint4* shared;      // [rows][hv]
+  int top_k, num_permuted;
+  // mHC
+  const uint4* res_in;      // [rows][4][hv]
+  uint4* res_out;           // [rows][4][hv]
+  const float4* post;       // [rows] (4 floats)
+  const float4* comb;       // [rows][4] (16 floats)
+  const float4* pre;        // [rows] (4 floats)
+  const uint4* norm_w;      // [hv]
+  float eps;
+  int rows, hv, hidden, chunks;
+  uint4* layer_out;         // [rows][hv]
+  uint2* mx_data;           // [rows][hv]
+  uint8_t* mx_scale;        // [rows][hidden / 32]
+  // the next coefficients
+  const uint4* fn;          // [4 * hidden][24] bf16, 3 vectors per k row
+  CoeffEpilogue coef;       // scale, base, K, eps, alpha, iters (part unused)
+  float* next_pre;          // [rows][4]
+  float* next_post;         // [rows][4]
+  float* next_comb;         // [rows][16]
+  // handoff
+  unsigned long long* words;  // y^2 words [tiles][chunks][16], then coefficient words
+                              // [tiles][chunks][16][25]
+  unsigned* epoch;            // [max_rows]
+  unsigned* errors;
+  int tile_cap, tiles_per_round, rounds, spin_limit;  // tile_cap: tiles of the scratch
+};
+
+// Handoff words, tile-major: per (tile, chunk) the 16 rows' sums of y^2, then per (tile,
+// chunk, row) the 25 coefficient partials (24 logits, the sum of v^2). One workgroup's
+// words are contiguous.
+__device__ __forceinline__ size_t ysq_index(const TileParams& p, int tile, int c, int rr) {
+  return ((size_t)tile * p.chunks + c) * kTileRows + rr;
+}
+__device__ __forceinline__ size_t coef_index(const TileParams& p, int tile, int c, int rr,
+                                             int v) {
+  // after the y^2 words of every tile the handle holds: each word's place belongs to one
+  // row whatever the call's row count, so a stale word carries an older tag of that row
+  const size_t base = (size_t)p.tile_cap * p.chunks * kTileRows;
+  return base + (((size_t)tile * p.chunks + c) * kTileRows + rr) * kCoefPartW + v;
+}
+
+__device__ __forceinline__ unsigned long long tagged(unsigned tag, float f) {
+  return ((unsigned long long)tag << 32) | __float_as_uint(f);
+}
+
+// Sum over the 32 lanes of each half wave (a tile row's lanes), in a fixed order.
+__device__ __forceinline__ float half_wave_sum(float v) {
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppRowRor4>(v);
+  v += dpp_f32<kDppRowRor8>(v);
+  return v + __shfl_xor(v, 16, kWave);
+}
+
+struct TileShared {
+  uint16_t fnT[kCoefNC][kFnLd];                 // fn^T of the chunk, [logit][k]
+  uint4 sT[kN][kTileRows][kTileVecs + 1];       // new streams, bf16, padded rows
+  float red[kTileWaves][kTileRows][kCoefNC];    // per-wave partial logits
+  float rowsum[kTileRows][2];                   // per-row sum of y^2, of v^2
+  unsigned want[kTileRows];
+  float inv[kTileRows];
+};
+
+template <bool FINALIZE, bool MXFP8>
+__device__ __forceinline__ void tile_item(const TileParams& p, int tile, int c, TileShared& S,
+                                          float sc_l, float base_l) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  // global traffic: the 32 lanes of a half wave own one row's 32 vectors of the chunk
+  const int m = tid >> 5;           // row of the tile
+  const int vl = tid & 31;          // vector of the chunk
+  const int row0 = tile * kTileRows;
+  const int r = row0 + m;
+  const int v = c * kTileVecs + vl;
+  const bool row_ok = r < p.rows;
+  const bool active = row_ok && v < p.hv;
+  const int rl = row_ok ? r : 0;    // loads of inactive lanes stay in bounds
+  const int va = v < p.hv ? v : 0;
+
+  // Every load below is unconditional, with indices clamped into bounds (results of
+  // out-of-range lanes are dropped later): a load behind a lane-dependent branch makes the
+  // compiler wait for it before going on, which serializes the loads.
+  // the rows' epochs (the call tag), kept in a register until the loads are issued
+  const unsigned epoch_now = __hip_atomic_load(p.epoch + min(row0 + (tid & 15), p.rows - 1),
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // --- loads: fn slice (mostly L2 hits), the row's mixes, norm weight, streams, sublayer
+  uint4 fv[kFnVecs];
+#pragma unroll
+  for (int j = 0; j < kFnVecs; ++j) {
+    const int q = tid + j * kTileThreads;        // < 4 * 256 * 3
+    const int i = q / (kTileH * 3), rem = q % (kTileH * 3);
+    const int kk = rem / 3, part = rem % 3;
+    const int h = min(c * kTileH + kk, p.hidden - 1);  // past the end: zeroed below
+    fv[j] = p.fn[((size_t)i * p.hidden + h) * 3 + part];
+  }
+  const float4 pst4 = p.post[rl];
+  float4 cmb4[kN];
+#pragma unroll
+  for (int i = 0; i < kN; ++i) cmb4[i] = p.comb[rl * kN + i];
+  const float4 pr4 = p.pre[rl];
+  int pk[8];
+  float wk[8];
+  if constexpr (FINALIZE) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int uu = u < p.top_k ? u : p.top_k - 1;
+      const int pi = p.idx[rl * p.top_k + uu];
+      const float w = p.ew[rl * p.top_k + uu];
+      pk[u] = u < p.top_k ? pi : -1;
+      wk[u] = u < p.top_k ? w : 0.f;
+    }
+  }
+  const uint4 wv = p.norm_w[va];
+  uint4 sv[kN];
+#pragma unroll
+  for (int j = 0; j < kN; ++j) sv[j] = load_nt(p.res_in + ((size_t)rl * kN + j) * p.hv + va);
+
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  if constexpr (!FINALIZE) {
+    // t ascending
+    const uint4* src = p.xp + (size_t)rl * p.hv + va;
+    const size_t slice = (size_t)p.rows * p.hv;
+    for (int t0 = 0; t0 < p.tp; t0 += 8) {
+      uint4 xv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (t0 + u < p.tp) xv[u] = load_nt(src + (size_t)(t0 + u) * slice);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (t0 + u < p.tp) {
+          float f[8];
+          unpack8(xv[u], f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] += f[e];
+        }
+      }
+    }
+  } else {
+    // k ascending, then the shared row
+    const uint4 shv = load_nt(p.shared + (size_t)rl * p.hv + va);
+    uint4 gv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < p.top_k) {
+        const bool ok = pk[u] >= 0 && pk[u] < p.num_permuted;
+        gv[u] = load_nt(p.g + (size_t)(ok ? pk[u] : 0) * p.hv + va);
+        if (!ok) wk[u] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < p.top_k) {
+        float f[8];
+        unpack8(gv[u], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(wk[u], f[e], x[e]);
+      }
+    }
+    for (int k = 8; k < p.top_k; ++k) {  // slots beyond 8, in order
+      const int pi = p.idx[rl * p.top_k + k];
+      const bool ok = pi >= 0 && pi < p.num_permuted;
+      const float w = ok ? p.ew[rl * p.top_k + k] : 0.f;
+      const uint4 gk = load_nt(p.g + (size_t)(ok ? pi : 0) * p.hv + va);
+      float f[8];
+      unpack8(gk, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(w, f[e], x[e]);
+    }
+    float f[8];
+    unpack8(shv, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] += f[e];
+  }
+  round8_bf16(x);  // the reduced output is a bf16 tensor
+
+  // --- new streams (stored at once, and into LDS for the projection), collapse
+  const float pst[kN] = {pst4.x, pst4.y, pst4.z, pst4.w};
+  const float cmb[kN * kN] = {cmb4[0].x, cmb4[0].y, cmb4[0].z, cmb4[0].w,
+                              cmb4[1].x, cmb4[1].y, cmb4[1].z, cmb4[1].w,
+                              cmb4[2].x, cmb4[2].y, cmb4[2].z, cmb4[2].w,
+                              cmb4[3].x, cmb4[3].y, cmb4[3].z, cmb4[3].w};
+  const float pr[kN] = {pr4.x, pr4.y, pr4.z, pr4.w};
+  float s[kN][8], sn[kN][8];
+#pragma unroll
+  for (int j = 0; j < kN; ++j) unpack8(sv[j], s[j]);
+  uint4* out = p.res_out + (size_t)rl * kN * p.hv + va;
+  float vsq = 0.f;
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = pst[i] * x[e];
+#pragma unroll
+      for (int j = 0; j < kN; ++j) a = __builtin_fmaf(cmb[i * kN + j], s[j][e], a);
+      sn[i][e] = a;
+    }
+    const uint4 o = pack8_round(sn[i]);
+    if (active) out[(size_t)i * p.hv] = o;
+    S.sT[i][m][vl] = active ? o : make_uint4(0u, 0u, 0u, 0u);
+    unpack8(o, sn[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vsq = __builtin_fmaf(sn[i][e], sn[i][e], vsq);
+  }
+  float y[8];
+  float sq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < kN; ++j) a = __builtin_fmaf(pr[j], sn[j][e], a);
+    y[e] = a;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sq = __builtin_fmaf(y[e], y[e], sq);
+  if (!active) {
+    sq = 0.f;
+    vsq = 0.f;
+  }
+  sq = half_wave_sum(sq);
+  vsq = half_wave_sum(vsq);
+  if (vl == 0) {
+    S.rowsum[m][0] = sq;
+    S.rowsum[m][1] = vsq;
+  }
+
+  // --- fn slice -> LDS, transposed to [logit][k] (k = stream * 256 + element of the chunk)
+  if (tid < kTileRows) S.want[tid] = epoch_now + 1u;
+#pragma unroll
+  for (int j = 0; j < kFnVecs; ++j) {
+    const int q = tid + j * kTileThreads;
+    const int i = q / (kTileH * 3), rem = q % (kTileH * 3);
+    const int kk = rem / 3, c0 = (rem % 3) * 8;
+    const bool ok = c * kTileH + kk < p.hidden;
+    const uint32_t u[4] = {ok ? fv[j].x : 0u, ok ? fv[j].y : 0u, ok ? fv[j].z : 0u,
+                           ok ? fv[j].w : 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      S.fnT[c0 + 2 * e][i * kTileH + kk] = (uint16_t)(u[e] & 0xFFFFu);
+      S.fnT[c0 + 2 * e + 1][i * kTileH + kk] = (uint16_t)(u[e] >> 16);
+    }
+  }
+  __syncthreads();  // fnT, sT, rowsum and want complete
+
+  // --- the rows' sums of y^2 go out first (the handoff waits for them)
+  if (tid < kTileRows && row0 + tid < p.rows)
+    __hip_atomic_store(p.words + ysq_index(p, tile, c, tid), tagged(S.want[tid], S.rowsum[tid][0]),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // --- partial logits: wave w takes elements 32w .. 32w + 31 of the chunk for all 16 rows;
+  // lane (row mm, group kg) holds the MFMA operands of 8 of them
+  {
+    const int mm = lane & 15, kg = lane >> 4;
+    const int hg = wave * 4 + kg;  // vector of the chunk
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int kl = i * kTileH + hg * 8;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(&S.fnT[mm][kl]);
+      const uint4 a1 =
+          (16 + mm < kCoefNC) ? *reinterpret_cast<const uint4*>(&S.fnT[16 + mm][kl]) : zero;
+      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, S.sT[i][mm][hg]);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), b, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), b, acc1, 0, 0, 0);
+    }
+    // D layout: lane holds D[4 kg + i][mm]: logit 4 kg + i (+16) of row mm
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      S.red[wave][mm][4 * kg + i] = acc0[i];
+      if (kg < 2) S.red[wave][mm][16 + 4 * kg + i] = acc1[i];
+    }
+  }
+
+  __syncthreads();  // red complete
+  // --- the coefficient partials of this chunk (waves added in order), out before the
+  // handoff wait so that they travel while it runs
+  if (tid < kTileRows * kCoefPartW) {
+    const int rr = tid / kCoefPartW, vv = tid % kCoefPartW;
+    if (row0 + rr < p.rows) {
+      float t = 0.f;
+      if (vv < kCoefNC) {
+#pragma unroll
+        for (int w = 0; w < kTileWaves; ++w) t += S.red[w][rr][vv];
+      } else {
+        t = S.rowsum[rr][1];
+      }
+      __hip_atomic_store(p.words + coef_index(p, tile, c, rr, vv), tagged(S.want[rr], t),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // --- wave 0: the rows' sums of y^2 over every chunk (lanes 16g + row: a quarter of the
+  // chunks each, in order; the quarters in order)
+  if (wave == 0) {
+    const int pm = lane & 15, g = lane >> 4;
+    const int q4 = (p.chunks + 3) >> 2;
+    const int cb = g * q4;
+    const int n = min(cb + q4, p.chunks) - cb;  // chunks of this lane (may be <= 0)
+    float part = 0.f;
+    if (row0 + pm < p.rows && n > 0) {
+      const unsigned want = S.want[pm];
+      for (int spins = 0;; ++spins) {
+        unsigned long long w[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          w[u] = __hip_atomic_load(p.words + ysq_index(p, tile, cb + (u < n ? u : n - 1), pm),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool ok = true;
+        part = 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (u < n) {
+            ok = ok && (unsigned)(w[u] >> 32) == want;
+            part += __uint_as_float((unsigned)w[u]);
+          }
+        }
+        if (ok) break;
+        if (spins >= p.spin_limit) {
+          __hip_atomic_fetch_add(p.errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    const float p0 = __shfl(part, pm, kWave), p1 = __shfl(part, pm + 16, kWave);
+    const float p2 = __shfl(part, pm + 32, kWave), p3 = __shfl(part, pm + 48, kWave);
+    const float tot = ((p0 + p1) + p2) + p3;
+    if (g == 0) {
+      S.inv[pm] = 1.0f / sqrtf(tot / (float)p.hidden + p.eps);
+      if (c == 0 && row0 + pm < p.rows)
+        __hip_atomic_store(p.epoch + row0 + pm, S.want[pm], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();  // inv complete
+
+  // --- layer input (and MXFP8)
+  {
+    const float inv = S.inv[m];
+    float w[8], o[8];
+    unpack8(wv, w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (y[e] * inv) * w[e];
+    const uint4 ob = pack8_round(o);
+    if (active) p.layer_out[(size_t)r * p.hv + v] = ob;
+    if constexpr (MXFP8) {
+      // 32-element block = the quad of lanes holding vectors v & ~3 .. v | 3
+      float q[8];
+      unpack8(ob, q);
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(q[e]));
+      amax = fmaxf(amax, dpp_f32<kDppQuadXor1>(amax));
+      amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
+      const int ex = e8m0_exponent(__float_as_uint(amax));
+      const float sc = __uint_as_float((uint32_t)(127 - ex) << 23);
+      const uint32_t lo = cvt_pk4_e4m3(q[0] * sc, q[1] * sc, q[2] * sc, q[3] * sc);
+      const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
+      if (active) {
+        p.mx_data[(size_t)r * p.hv + v] = make_uint2(lo, hi);
+        if ((v & 3) == 0) p.mx_scale[(size_t)r * (p.hidden / 32) + (v >> 2)] = (uint8_t)(ex + 127);
+      }
+    }
+  }
+
+  // --- the next coefficients of rows c, c + chunks, ... (row j on wave j % 8); lane L < 25
+  // adds value L of every chunk in chunk order
+  int j = 0;
+  for (int rt = c; rt < kTileRows; rt += p.chunks, ++j) {
+    if (j % kTileWaves != wave) continue;  // wave-uniform
+    const int rc = row0 + rt;
+    if (rc >= p.rows) continue;
+    const unsigned want = S.want[rt];
+    float acc = 0.f;
+    if (lane < kCoefPartW) {
+      for (int spins = 0;; ++spins) {
+        bool ok = true;
+        acc = 0.f;
+        for (int b0 = 0; b0 < p.chunks; b0 += kFinishBatch) {  // one batch up to 32 chunks
+          unsigned long long w[kFinishBatch];
+#pragma unroll
+          for (int u = 0; u < kFinishBatch; ++u) {
+            const int cc = b0 + u < p.chunks ? b0 + u : p.chunks - 1;
+            w[u] = __hip_atomic_load(p.words + coef_index(p, tile, cc, rt, lane),
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+#pragma unroll
+          for (int u = 0; u < kFinishBatch; ++u) {
+            if (b0 + u < p.chunks) {
+              ok = ok && (unsigned)(w[u] >> 32) == want;
+              acc += __uint_as_float((unsigned)w[u]);
+            }
+          }
+        }
+        if (ok) break;
+        if (spins >= p.spin_limit) {
+          __hip_atomic_fetch_add(p.errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    int slot;
+    const float val = coeff_from_sums(p.coef, lane, acc, sc_l, base_l, &slot);
+    if (slot >= 0 && slot < kN) p.next_pre[rc * kN + slot] = val;
+    else if (slot >= kN && slot < 2 * kN) p.next_post[rc * kN + slot - kN] = val;
+    else if (slot >= 2 * kN) p.next_comb[rc * kN * kN + slot - 2 * kN] = val;
+  }
+}
+
+template <bool FINALIZE, bool MXFP8>
+__global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_kernel(const TileParams p) {
+  __shared__ __attribute__((aligned(16))) TileShared S;
+  float sc_l, base_l;
+  coeff_lane_scale_base(p.coef, threadIdx.x & (kWave - 1), &sc_l, &base_l);
+  const int wg = blockIdx.x;
+  const int xcd = wg % kXcd;
+  const int local = wg / kXcd;
+  const int c = local % p.chunks;
+  const int jt = local / p.chunks;  // which tile of this XCD's block in a round
+  for (int round = 0; round < p.rounds; ++round) {
+    const int tile = (round * p.tiles_per_round + jt) * kXcd + xcd;
+    if (tile * kTileRows >= p.rows) break;  // uniform per workgroup; later rounds go higher
+    if (round > 0) __syncthreads();          // LDS reused
+    tile_item<FINALIZE, MXFP8>(p, tile, c, S, sc_l, base_l);
+  }
+}
+
+template <bool FIN, bool MX>
+int occupancy_tile() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, boundary_tile_kernel<FIN, MX>,
+                                                   kTileThreads, 0) != hipSuccess)
+    return 0;
+  return n;
+}
+
+}  // namespace
+
+int boundary_tile_resident_wgs_per_cu() {
+  int n = occupancy_tile<false, false>();
+  n = min(n, occupancy_tile<false, true>());
+  n = min(n, occupancy_tile<true, false>());
+  n = min(n, occupancy_tile<true, true>());
+  return n;
+}
+
+int boundary_tile_chunks(int hidden) { return (hidden + kTileH - 1) / kTileH; }
+
+size_t boundary_tile_words(int rows, int hidden) {
+  const size_t tiles = (rows + kTileRows - 1) / kTileRows;
+  return tiles * kTileRows * kWordsPerRow * boundary_tile_chunks(hidden);
+}
+
+bool boundary_tile_fits(int hidden, int wgs_per_xcd) {
+  const int chunks = boundary_tile_chunks(hidden);
+  return chunks <= kMaxTileChunks && chunks <= kFinishBatch && chunks <= wgs_per_xcd;
+}
+
+hipError_t launch_boundary_tile(const TileLaunch& T, hipStream_t stream) {
+  const BoundaryLaunch& L = T.b;
+  TileParams p;
+  p.xp = reinterpret_cast<const uint4*>(L.x_partials);
+  p.tp = L.tp;
+  p.g = reinterpret_cast<const uint4*>(L.gemm2_permuted);
+  p.ew = L.expert_weights;
+  p.idx = L.idx;
+  p.shared = reinterpret_cast<const uint4*>(L.shared_output);
+  p.top_k = L.top_k;
+  p.num_permuted = L.num_permuted;
+  p.res_in = reinterpret_cast<const uint4*>(L.residual);
+  p.res_out = reinterpret_cast<uint4*>(L.residual_out);
+  p.post = reinterpret_cast<const float4*>(L.post);
+  p.comb = reinterpret_cast<const float4*>(L.comb);
+  p.pre = reinterpret_cast<const float4*>(L.pre);
+  p.norm_w = reinterpret_cast<const uint4*>(L.norm_weight);
+  p.eps = L.eps;
+  p.rows = L.rows;
+  p.hidden = L.hidden;
+  p.hv = L.hidden / 8;
+  p.chunks = boundary_tile_chunks(L.hidden);
+  p.layer_out = reinterpret_cast<uint4*>(L.layer_input_out);
+  p.mx_data = reinterpret_cast<uint2*>(L.mx_data_out);
+  p.mx_scale = L.mx_scale_out;
+  p.fn = reinterpret_cast<const uint4*>(T.fn);
+  p.coef = T.coef;
+  p.next_pre = T.next_pre;
+  p.next_post = T.next_post;
+  p.next_comb = T.next_comb;
+  p.words = T.words;
+  p.epoch = L.epoch;
+  p.errors = L.errors;
+  p.spin_limit = L.spin_limit;
+  if (!boundary_tile_fits(L.hidden, T.wgs_per_xcd)) return hipErrorInvalidConfiguration;
+  const int tiles = (L.rows + kTileRows - 1) / kTileRows;
+  p.tile_cap = (T.tile_rows + kTileRows - 1) / kTileRows;
+  if (tiles > p.tile_cap) return hipErrorInvalidConfiguration;
+  const int tile_blocks = (tiles + kXcd - 1) / kXcd;  // tiles per XCD in total
+  // a round may use half of the XCD's resident workgroups, or all of them where half
+  // does not hold one tile
+  int per_xcd = T.wgs_per_xcd / 2;
+  if (per_xcd < p.chunks) per_xcd = T.wgs_per_xcd;
+  int tpr = per_xcd / p.chunks;
+  if (tpr > tile_blocks) tpr = tile_blocks;
+  p.tiles_per_round = tpr;
+  p.rounds = (tile_blocks + tpr - 1) / tpr;
+  const int grid = kXcd * tpr * p.chunks;
+  const bool fin = L.gemm2_permuted != nullptr;
+  const bool mx = L.mx_data_out != nullptr;
+  if (fin) {
+    if (mx) hipLaunchKernelGGL((boundary_tile_kernel<true, true>), dim3(grid), dim3(kTileThreads), 0, stream, p);
+    else hipLaunchKernelGGL((boundary_tile_kernel<true, false>), dim3(grid), dim3(kTileThreads), 0, stream, p);
+  } else {
+    if (mx) hipLaunchKernelGGL((boundary_tile_kernel<false, true>), dim3(grid), dim3(kTileThreads), 0, stream, p);
+    else hipLaunchKernelGGL((boundary_tile_kernel<false, false>), dim3(grid), dim3(kTileThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mhc

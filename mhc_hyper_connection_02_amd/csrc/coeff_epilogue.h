@@ -60,6 +60,9 @@ __device__ __forceinline__ void coeff_row_prefetch(const CoeffEpilogue& e, int r
   for (int u = 0; u < NP; ++u) f.v[u] = src[u < last ? u : last];
 }
 
+__device__ __forceinline__ float coeff_from_sums(const CoeffEpilogue& e, int L, float acc,
+                                                 float sc_l, float base_l, int* slot);
+
 // Row r's coefficients after coeff_row_prefetch; every lane of the wave must call it
 // (lane = L). Returns this lane's value and sets *slot: 0..3 pre, 4..7 post, 8..23 comb
 // (row-major), -1 none.
@@ -89,6 +92,14 @@ __device__ __forceinline__ float coeff_row_finish(const CoeffEpilogue& e, int r,
         if (b0 + u < n4) acc = (((acc + v[u].x) + v[u].y) + v[u].z) + v[u].w;
     }
   }
+  return coeff_from_sums(e, L, acc, sc_l, base_l, slot);
+}
+
+// Row coefficients from this lane's complete sum (lane L < 24: logit L, lane 24: the sum
+// of squares, others unused); every lane of the wave must call it. Returns this lane's
+// value and sets *slot as coeff_row_finish.
+__device__ __forceinline__ float coeff_from_sums(const CoeffEpilogue& e, int L, float acc,
+                                                 float sc_l, float base_l, int* slot) {
   const float ss = __shfl(acc, kCoefNC, kWave);
   const float inv = 1.0f / sqrtf(ss / (float)e.K + e.rms_eps);
   float lp = 0.f;

@@ -71,6 +71,25 @@ struct PreLaunch {
   float* part;                  // pre_scratch_floats(max_rows, hidden) floats
 };
 
+// The boundary fused with the next coefficient call (boundary_tile.hip): the boundary's
+// launch (mix mode, with a layer input) plus the coefficient call's arguments.
+struct TileLaunch {
+  BoundaryLaunch b;
+  const uint16_t* fn;           // [4 * hidden][24] bf16
+  CoeffEpilogue coef;           // scale, base, K, eps, alpha, iters (part unused)
+  float* next_pre;
+  float* next_post;
+  float* next_comb;
+  unsigned long long* words;    // boundary_tile_words(tile_rows, hidden) tagged partials
+  int tile_rows;                // rows the words cover (the handle's), >= the call's rows
+  int wgs_per_xcd;              // resident workgroups of the tile kernel on one XCD
+};
+int boundary_tile_resident_wgs_per_cu();
+int boundary_tile_chunks(int hidden);
+size_t boundary_tile_words(int rows, int hidden);
+bool boundary_tile_fits(int hidden, int wgs_per_xcd);
+hipError_t launch_boundary_tile(const TileLaunch& T, hipStream_t stream);
+
 int boundary_chunks(int hidden, int block, bool has_pre);
 int boundary_resident_wgs_per_cu(int block);
 hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream);

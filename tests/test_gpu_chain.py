@@ -178,3 +178,42 @@ def test_deferred_coefficients_leave_the_step_unchanged():
         torch.cuda.synchronize()
     assert plain.h.errors() == 0
 
+
+
+def test_fused_chain_every_step_and_graph_replays():
+    """Boundaries fused with the coefficient call after them: every boundary and every
+    coefficient set against the oracle on the step's own inputs; graph replays equal the
+    eager step bit for bit."""
+    say("case: chained step, 3 layers: fused boundary + coefficient calls, every boundary")
+    step = chain.DecodeChain.from_synth(DEV, layers=3, fused=True)
+    _teacher_forced_checks(step, set(range(len(step.subs))))
+    want = N(step.run())
+    torch.cuda.synchronize()
+    again = N(step.run())
+    torch.cuda.synchronize()
+    assert np.array_equal(again, want), "fused step not deterministic"
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        out = step.run()
+    for rep in range(2):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(N(out), want), f"replay {rep}"
+        step.run()
+        torch.cuda.synchronize()
+    assert step.h.errors() == 0
+
+
+def test_fused_chain_61_layers_sampled_steps():
+    say("case: chained step, 61 layers, fused boundary + coefficient calls: sampled boundaries")
+    step = chain.DecodeChain.from_synth(DEV, fused=True)
+    n = len(step.subs)
+    _teacher_forced_checks(step, {0, 1, 2, n // 2 - 1, n // 2, n - 2, n - 1})
+    assert step.h.errors() == 0

@@ -1,0 +1,248 @@
+"""The boundary fused with the next coefficient call (mhc_boundary_coeffs, mhc_finalize_coeffs):
+its new streams bit-identical to mhc_boundary's / mhc_finalize's, its layer input and MXFP8
+form against the oracle, and the next coefficients against the oracle's coefficient path on
+the new streams; plus the fallback to the two calls, graph replays, changing row counts
+interleaved with the other calls, mhc_reset and argument checks."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mhc_hyper_connection_02_amd import binding, synth
+
+from gpu_helpers import (N, T, assert_f32_close, compare_boundary_outputs, handle_for,
+                         oracle_boundary, oracle_finalize, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _next_args(seed, hidden):
+    d = synth.pre_inputs(seed, rows=1, hidden=hidden)
+    return {"fn": T(d["fn"]), "scale": T(d["scale"]), "base": T(d["base"]),
+            "rms_eps": d["rms_eps"], "pre_eps": d["pre_eps"], "sinkhorn_eps": d["sinkhorn_eps"],
+            "post_alpha": d["post_alpha"], "sinkhorn_iters": d["sinkhorn_iters"]}, d
+
+
+def _oracle_next(streams_bits, c):
+    return oracle.pre_coeffs(streams_bits, c["fn"], c["scale"], c["base"], c["rms_eps"],
+                             c["pre_eps"], c["sinkhorn_eps"], c["post_alpha"], c["sinkhorn_iters"])
+
+
+def _run_fused(h, kind, d, nxt, mx):
+    if kind == "boundary":
+        o = binding.boundary_coeffs(h, T(d["x_partials"]), T(d["residual"]), T(d["post"]),
+                                    T(d["comb"]), T(d["pre"]), T(d["norm_weight"]), d["eps"], nxt,
+                                    mxfp8=mx)
+    else:
+        o = binding.finalize_coeffs(h, T(d["gemm2_permuted"]), T(d["expert_weights"]),
+                                    T(d["expanded_idx_to_permuted_idx"]), T(d["shared_output"]),
+                                    T(d["residual"]), T(d["post"]), T(d["comb"]), T(d["pre"]),
+                                    T(d["norm_weight"]), d["eps"], nxt, mxfp8=mx)
+    torch.cuda.synchronize()
+    nx = [N(t) for t in o.pop("next")]
+    return {k: N(v) for k, v in o.items()}, nx
+
+
+def _run_plain(h, kind, d, mx):
+    if kind == "boundary":
+        o = binding.boundary(h, T(d["x_partials"]), T(d["residual"]), T(d["post"]), T(d["comb"]),
+                             T(d["pre"]), T(d["norm_weight"]), d["eps"], mxfp8=mx)
+    else:
+        o = binding.finalize(h, T(d["gemm2_permuted"]), T(d["expert_weights"]),
+                             T(d["expanded_idx_to_permuted_idx"]), T(d["shared_output"]),
+                             T(d["residual"]), T(d["post"]), T(d["comb"]), T(d["pre"]),
+                             T(d["norm_weight"]), d["eps"], mxfp8=mx)
+    torch.cuda.synchronize()
+    return {k: N(v) for k, v in o.items()}
+
+
+def _inputs(kind, seed, rows, hidden, mx):
+    if kind == "boundary":
+        return synth.boundary_inputs(seed, rows=rows, hidden=hidden, tp=8, x_sigma=0.5, mxfp8=mx)
+    return synth.finalize_inputs(seed, rows=rows, hidden=hidden, top_k=8, mxfp8=mx)
+
+
+def _check_case(kind, rows, hidden, seed):
+    mx = hidden % 32 == 0
+    d = _inputs(kind, seed, rows, hidden, mx)
+    nxt, c = _next_args(seed + 1, hidden)
+    h = handle_for(hidden, rows)
+    got, nx = _run_fused(h, kind, d, nxt, mx)
+    want = oracle_boundary(d) if kind == "boundary" else oracle_finalize(d)
+    compare_boundary_outputs(got, want, f"fused {kind} {rows}x{hidden}")
+    plain = _run_plain(h, kind, d, mx)
+    assert np.array_equal(got["residual"], plain["residual"]), "new streams differ from the boundary's"
+    for name, a, b in zip(("pre", "post", "comb"), nx, _oracle_next(got["residual"], c)):
+        assert_f32_close(a, b, f"fused {kind} {rows}x{hidden} next {name}")
+    assert h.errors() == 0
+    return got, nx
+
+
+@pytest.mark.parametrize("kind,rows,hidden", [
+    ("boundary", 128, 7168), ("finalize", 128, 7168), ("boundary", 32, 7168),
+    ("finalize", 64, 7168), ("boundary", 16, 1024), ("boundary", 5, 1056), ("finalize", 3, 1056),
+    ("boundary", 200, 2048), ("finalize", 130, 4096), ("boundary", 1, 8), ("boundary", 17, 1000),
+    ("finalize", 33, 4096), ("boundary", 9, 16384),
+])
+def test_fused_matches_oracle(kind, rows, hidden):
+    say(f"case: fused {kind} + next coefficients rows={rows} hidden={hidden}")
+    _check_case(kind, rows, hidden, 6000 + rows + hidden)
+
+
+def test_fallback_paths_equal_the_two_calls():
+    """Misaligned post/comb/pre (4-byte aligned views) and rows beyond the fused scratch run
+    the two calls: every output equals mhc_boundary + mhc_pre_coeffs bit for bit."""
+    for rows, hidden, misalign in ((40, 2048, True), (1030, 1024, False)):
+        say(f"case: fused call fallback rows={rows} hidden={hidden} misaligned={misalign}")
+        d = synth.boundary_inputs(77 + rows, rows=rows, hidden=hidden, tp=2, mxfp8=True)
+        nxt, c = _next_args(78, hidden)
+        h = handle_for(hidden, rows, tp=2)
+        tensors = {k: T(d[k]) for k in ("post", "comb", "pre")}
+        if misalign:  # the same values at a 4-byte offset
+            for k, t in tensors.items():
+                buf = torch.empty(t.numel() + 1, dtype=torch.float32, device=t.device)
+                view = buf[1:].view(t.shape)
+                view.copy_(t)
+                tensors[k] = view
+        o = binding.boundary_coeffs(h, T(d["x_partials"]), T(d["residual"]), tensors["post"],
+                                    tensors["comb"], tensors["pre"], T(d["norm_weight"]), d["eps"],
+                                    nxt, mxfp8=True)
+        ref = binding.boundary(h, T(d["x_partials"]), T(d["residual"]), tensors["post"],
+                               tensors["comb"], tensors["pre"], T(d["norm_weight"]), d["eps"],
+                               mxfp8=True)
+        refc = binding.pre_coeffs(h, ref["residual"], nxt["fn"], nxt["scale"], nxt["base"],
+                                  nxt["rms_eps"], nxt["pre_eps"], nxt["sinkhorn_eps"],
+                                  nxt["post_alpha"], nxt["sinkhorn_iters"])
+        torch.cuda.synchronize()
+        for k in ref:
+            assert np.array_equal(N(o[k]), N(ref[k])), k
+        for a, b in zip(o["next"], refc):
+            assert np.array_equal(N(a), N(b))
+        assert h.errors() == 0
+
+
+def test_changing_rows_interleaved_with_other_calls_and_reset():
+    """One handle: fused calls over changing row counts, interleaved with plain boundaries and
+    coefficient calls (which share the rows' epochs), a mhc_reset halfway; every fused call
+    against the oracle, repeats of one input bit-identical."""
+    hidden = 2048
+    seq = [128, 5, 64, 128, 1, 300, 64, 16]
+    say(f"case: fused calls rows {seq} twice, interleaved, hidden={hidden}")
+    h = handle_for(hidden, 300)
+    first = {}
+    for rep in range(2):
+        if rep == 1:
+            binding.load_library().mhc_reset(h.ptr, None)
+        for i, rows in enumerate(seq):
+            d = synth.boundary_inputs(8000 + rows, rows=rows, hidden=hidden, tp=8, mxfp8=True)
+            nxt, c = _next_args(8001 + rows, hidden)
+            got, nx = _run_fused(h, "boundary", d, nxt, True)
+            compare_boundary_outputs(got, oracle_boundary(d), f"call {i} rows={rows}")
+            for name, a, b in zip(("pre", "post", "comb"), nx, _oracle_next(got["residual"], c)):
+                assert_f32_close(a, b, f"call {i} rows={rows} next {name}")
+            key = rows
+            if key in first:
+                g0, n0 = first[key]
+                for k in g0:
+                    assert np.array_equal(got[k], g0[k]), f"rows={rows} {k} not deterministic"
+                for a, b in zip(nx, n0):
+                    assert np.array_equal(a, b)
+            else:
+                first[key] = (got, nx)
+            _run_plain(h, "boundary", d, True)  # the plain call advances the same epochs
+            binding.pre_coeffs(h, T(d["residual"]), nxt["fn"], nxt["scale"], nxt["base"],
+                               nxt["rms_eps"], nxt["pre_eps"], nxt["sinkhorn_eps"],
+                               nxt["post_alpha"], nxt["sinkhorn_iters"])
+    torch.cuda.synchronize()
+    assert h.errors() == 0
+
+
+def test_graph_replays_of_fused_calls():
+    """Two captured fused calls (boundary then finalize on its streams), replayed three times
+    with eager calls on the handle in between: every replay equals the eager run bit for bit."""
+    rows, hidden = 128, 7168
+    say(f"case: HIP graph replays of fused calls rows={rows} hidden={hidden}")
+    h = handle_for(hidden, rows)
+    d = synth.boundary_inputs(91, rows=rows, hidden=hidden, tp=8, x_sigma=0.5, mxfp8=True)
+    f = synth.finalize_inputs(92, rows=rows, hidden=hidden, top_k=8)
+    n1, _ = _next_args(93, hidden)
+    n2, _ = _next_args(94, hidden)
+    dv = {k: T(v) for k, v in d.items() if isinstance(v, np.ndarray)}
+    fv = {k: T(v) for k, v in f.items() if isinstance(v, np.ndarray)}
+
+    def run():
+        a = binding.boundary_coeffs(h, dv["x_partials"], dv["residual"], dv["post"], dv["comb"],
+                                    dv["pre"], dv["norm_weight"], d["eps"], n1, mxfp8=True)
+        p, q, cm = a["next"]
+        b = binding.finalize_coeffs(h, fv["gemm2_permuted"], fv["expert_weights"],
+                                    fv["expanded_idx_to_permuted_idx"], fv["shared_output"],
+                                    a["residual"], q, cm, p, dv["norm_weight"], d["eps"], n2,
+                                    mxfp8=True)
+        return [a["residual"], a["layer_input"], a["mx_data"], a["mx_scale"], p, q, cm,
+                b["residual"], b["layer_input"], b["mx_data"], b["mx_scale"], *b["next"]]
+
+    eager = [N(t) for t in run()]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = run()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, eager)):
+            assert np.array_equal(N(a), b), f"replay {rep} output {i}"
+        run()
+        torch.cuda.synchronize()
+    assert h.errors() == 0
+
+
+def test_fused_argument_checks():
+    say("case: mhc_boundary_coeffs / mhc_finalize_coeffs argument checks")
+    lib = binding.load_library()
+    R, H = 4, 1024
+    h = handle_for(H, R, tp=2)
+    d = synth.boundary_inputs(5, rows=R, hidden=H, tp=2, mxfp8=True)
+    nxt, _ = _next_args(6, H)
+    p = binding._ptr
+    dv = {k: T(v) for k, v in d.items() if isinstance(v, np.ndarray)}
+    so = torch.empty_like(dv["residual"])
+    li = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
+    outs = [torch.empty((R, 4), device="cuda"), torch.empty((R, 4), device="cuda"),
+            torch.empty((R, 4, 4), device="cuda")]
+    a = binding.CoeffArgs(p(nxt["fn"]), p(nxt["scale"]), p(nxt["base"]), 1e-6, 1e-6, 1e-6, 2.0,
+                          20, p(outs[0]), p(outs[1]), p(outs[2]))
+
+    def call(args, pre=dv["pre"], rows=R):
+        return lib.mhc_boundary_coeffs(h.ptr, p(dv["x_partials"]), 2, p(dv["residual"]),
+                                       p(dv["post"]), p(dv["comb"]), p(pre), p(dv["norm_weight"]),
+                                       1e-6, rows, p(so), p(li), None, None, args, None)
+
+    assert call(ctypes.byref(a), rows=0) == 0        # empty call
+    assert call(None) == 1                            # no coefficient arguments
+    assert call(ctypes.byref(a), pre=None) == 1       # a layer input is required
+    bad = binding.CoeffArgs.from_buffer_copy(a)
+    bad.sinkhorn_iters = 1001
+    assert call(ctypes.byref(bad)) == 2
+    bad = binding.CoeffArgs.from_buffer_copy(a)
+    bad.rms_eps = float("nan")
+    assert call(ctypes.byref(bad)) == 2
+    bad = binding.CoeffArgs.from_buffer_copy(a)
+    bad.comb_out = None
+    assert call(ctypes.byref(bad)) == 1
+    assert call(ctypes.byref(a), rows=R + 1) == 4
+    assert lib.mhc_finalize_coeffs(h.ptr, None, 1, None, None, None, p(dv["residual"]),
+                                   p(dv["post"]), p(dv["comb"]), p(dv["pre"]),
+                                   p(dv["norm_weight"]), 1e-6, R, p(so), p(li), None, None,
+                                   ctypes.byref(a), None) == 1
+    torch.cuda.synchronize()
