@@ -7,33 +7,39 @@
 // call's arguments); the arithmetic of each step is stated in include/mhc.h.
 //
 // Work decomposition. A workgroup of 512 threads (8 waves) owns a tile of 16 rows by
-// 256 hidden elements (one chunk). Lane l of wave w owns row l % 16 of the tile and the
-// 8 elements of vector 4w + l / 16 of the chunk, with all four streams of them: the same
-// per-lane dataflow as the boundary's layer-input kernels (partial slices or gathered
-// expert rows, mHC post, collapse, RMSNorm, MXFP8), in the same arithmetic order, so the
-// new streams are bit-identical to mhc_boundary's.
+// 256 hidden elements (one chunk). For every global load and store, the 32 lanes of a half
+// wave own one row's 32 vectors of the chunk (512 contiguous bytes), with all four streams
+// of them: the same per-lane dataflow as the boundary's layer-input kernels (partial
+// slices or gathered expert rows, mHC post, collapse, RMSNorm, MXFP8), in the same
+// arithmetic order, so the new streams are bit-identical to mhc_boundary's. (A layout
+// with 16 rows across consecutive lanes, the MFMA operand layout, made every 16-lane
+// memory pass touch 16 cache lines and was measured 2.6x slower.)
 //
-// The projection. With this layout the 64 lanes of wave w hold, for each stream i, the
-// bf16 new streams of 16 rows by 32 consecutive elements: exactly the B operand of one
-// v_mfma_f32_16x16x32_bf16 (N = rows, K = 32 elements). The A operand is fn^T over the
-// same 32 elements of stream i, staged in LDS (the chunk's fn rows, 4 x 256 x 24 bf16,
-// copied with 16-byte loads and transposed to [logit][k]). Eight MFMAs per wave (4
-// streams x logits 0..15 and 16..31) give the wave's partial logits of its 16 rows; the
-// eight waves' partials are added in wave order in LDS. Only the bf16 values the call
-// stores enter the projection, as in mhc_pre_coeffs on the stored streams.
+// The projection. The bf16 new streams are also written to LDS ([stream][row][vector],
+// rows padded against bank conflicts). Wave w then reads, for each stream i, 16 rows by
+// elements 32w .. 32w + 31 of the chunk as the B operand of one v_mfma_f32_16x16x32_bf16
+// (lane = row + 16 x 8-element group; N = rows, K = 32 elements); the A operand is fn^T
+// over the same elements, staged in LDS (the chunk's fn rows, 4 x 256 x 24 bf16, copied
+// with 16-byte loads and transposed to [logit][k]). Eight MFMAs per wave (4 streams x
+// logits 0..15 and 16..31) give the wave's partial logits of the 16 rows; the eight
+// waves' partials are added in wave order. Only the bf16 values the call stores enter the
+// projection, as in mhc_pre_coeffs on the stored streams.
 //
-// The handoff. Every workgroup publishes, per row of its tile, 26 words: the partial sum
-// of y^2 (for the layer input's RMS), the 24 partial logits and the partial sum of the
-// new streams' squares (for the coefficients' RMS), each as a 64-bit word (call tag <<
-// 32 | fp32 bits, relaxed device-scope store). Wave 0 of every workgroup of the tile then
-// polls the y^2 words of its 16 rows across the row's chunks (four lanes per row, each
-// adding a contiguous quarter of the chunks in order; the quarters are added in order:
-// deterministic), and the layer input follows. Workgroup c of the tile also finishes the
-// coefficients of rows c, c + chunks, ... : lanes 0..24 of one wave read that row's 25
-// coefficient words across the chunks in chunk order and run the coefficient epilogue
-// (coeff_epilogue.h), writing the next pre, post and comb. Tags are the rows' epochs + 1
-// (the same epochs as the boundary's handoff); chunk 0 advances them once its poll has
-// seen every chunk's word, i.e. after every workgroup of the tile has read them.
+// The handoff. Every workgroup publishes, per row of its tile, the partial sum of y^2 (for
+// the layer input's RMS; first, one contiguous line per workgroup), then the 24 partial
+// logits and the partial sum of the new streams' squares (for the coefficients' RMS),
+// each as a 64-bit word (call tag << 32 | fp32 bits, relaxed device-scope store). Each
+// half wave then reads its row's y^2 words, one chunk per lane (so chunks <= 32), until
+// all carry the call's tag, adds them in a fixed tree order (deterministic) and writes
+// its share of the layer input: no barrier. Workgroup c of the tile also finishes the
+// coefficients of rows c, c + chunks, ...: lanes 0..24 of one wave read the row's 25
+// coefficient words of every chunk, add them in chunk order and run the coefficient
+// epilogue (coeff_epilogue.h), writing the next pre, post and comb; it does so before its
+// own layer-input stores, since a wait for loads also waits for the stores before them.
+// Tags are the rows' epochs + 1 (the same epochs as the boundary's handoff); chunk 0
+// advances a row's epoch once it has seen the row's every word, i.e. after every
+// workgroup of the tile has read it. A word's place depends only on its row and chunk
+// (the layout is sized for the handle's rows), so a stale word carries an older tag.
 //
 // Co-residency and placement as the boundary's: a tile's chunks get workgroup ids
 // congruent mod 8 (one XCD, one L2), the grid holds at most the device's resident
@@ -57,8 +63,7 @@ constexpr int kWordsPerRow = 2 + kCoefNC;                 // y^2, 24 logits, v^2
 constexpr int kFnK = kN * kTileH;                         // 1024 k values per chunk
 constexpr int kFnLd = kFnK + 8;                           // padded LDS row of fn^T
 constexpr int kFnVecs = kFnK * kCoefNC / 8 / kTileThreads;  // 6 16-byte vectors per thread
-constexpr int kMaxTileChunks = 64;                        // 16 polled words per lane at most
-constexpr int kFinishBatch = 32;                          // coefficient words read at once
+constexpr int kFinishBatch = 32;                          // chunks per row at most (a half wave)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -132,7 +137,6 @@ struct TileShared {
   float red[kTileWaves][kTileRows][kCoefNC];    // per-wave partial logits
   float rowsum[kTileRows][2];                   // per-row sum of y^2, of v^2
   unsigned want[kTileRows];
-  float inv[kTileRows];
 };
 
 template <bool FINALIZE, bool MXFP8>
@@ -367,82 +371,36 @@ __device__ __forceinline__ void tile_item(const TileParams& p, int tile, int c, 
     }
   }
 
-  // --- wave 0: the rows' sums of y^2 over every chunk (lanes 16g + row: a quarter of the
-  // chunks each, in order; the quarters in order)
-  if (wave == 0) {
-    const int pm = lane & 15, g = lane >> 4;
-    const int q4 = (p.chunks + 3) >> 2;
-    const int cb = g * q4;
-    const int n = min(cb + q4, p.chunks) - cb;  // chunks of this lane (may be <= 0)
+  // --- each half wave: its row's sum of y^2 over every chunk (lane l reads chunk l's word;
+  // chunks <= 32), added in a fixed tree order
+  float inv;
+  {
+    const int cl = vl < p.chunks ? vl : p.chunks - 1;  // lanes past the chunks repeat the last
     float part = 0.f;
-    if (row0 + pm < p.rows && n > 0) {
-      const unsigned want = S.want[pm];
+    if (row_ok) {
+      const unsigned want = S.want[m];
+      unsigned long long w = 0;
       for (int spins = 0;; ++spins) {
-        unsigned long long w[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          w[u] = __hip_atomic_load(p.words + ysq_index(p, tile, cb + (u < n ? u : n - 1), pm),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        bool ok = true;
-        part = 0.f;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          if (u < n) {
-            ok = ok && (unsigned)(w[u] >> 32) == want;
-            part += __uint_as_float((unsigned)w[u]);
-          }
-        }
-        if (ok) break;
+        w = __hip_atomic_load(p.words + ysq_index(p, tile, cl, m), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+        if ((unsigned)(w >> 32) == want) break;
         if (spins >= p.spin_limit) {
           __hip_atomic_fetch_add(p.errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
         __builtin_amdgcn_s_sleep(1);
       }
+      part = vl < p.chunks ? __uint_as_float((unsigned)w) : 0.f;
     }
-    const float p0 = __shfl(part, pm, kWave), p1 = __shfl(part, pm + 16, kWave);
-    const float p2 = __shfl(part, pm + 32, kWave), p3 = __shfl(part, pm + 48, kWave);
-    const float tot = ((p0 + p1) + p2) + p3;
-    if (g == 0) {
-      S.inv[pm] = 1.0f / sqrtf(tot / (float)p.hidden + p.eps);
-      if (c == 0 && row0 + pm < p.rows)
-        __hip_atomic_store(p.epoch + row0 + pm, S.want[pm], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __syncthreads();  // inv complete
-
-  // --- layer input (and MXFP8)
-  {
-    const float inv = S.inv[m];
-    float w[8], o[8];
-    unpack8(wv, w);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (y[e] * inv) * w[e];
-    const uint4 ob = pack8_round(o);
-    if (active) p.layer_out[(size_t)r * p.hv + v] = ob;
-    if constexpr (MXFP8) {
-      // 32-element block = the quad of lanes holding vectors v & ~3 .. v | 3
-      float q[8];
-      unpack8(ob, q);
-      float amax = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(q[e]));
-      amax = fmaxf(amax, dpp_f32<kDppQuadXor1>(amax));
-      amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
-      const int ex = e8m0_exponent(__float_as_uint(amax));
-      const float sc = __uint_as_float((uint32_t)(127 - ex) << 23);
-      const uint32_t lo = cvt_pk4_e4m3(q[0] * sc, q[1] * sc, q[2] * sc, q[3] * sc);
-      const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
-      if (active) {
-        p.mx_data[(size_t)r * p.hv + v] = make_uint2(lo, hi);
-        if ((v & 3) == 0) p.mx_scale[(size_t)r * (p.hidden / 32) + (v >> 2)] = (uint8_t)(ex + 127);
-      }
-    }
+    const float tot = half_wave_sum(part);
+    inv = 1.0f / sqrtf(tot / (float)p.hidden + p.eps);
+    if (c == 0 && row_ok && vl == 0)
+      __hip_atomic_store(p.epoch + r, S.want[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // --- the next coefficients of rows c, c + chunks, ... (row j on wave j % 8); lane L < 25
-  // adds value L of every chunk in chunk order
+  // --- the next coefficients of rows c, c + chunks, ... (row j on wave j % 8), before that
+  // wave's layer-input stores so that its wait for the words does not wait for them; lane
+  // L < 25 adds value L of every chunk in chunk order
   int j = 0;
   for (int rt = c; rt < kTileRows; rt += p.chunks, ++j) {
     if (j % kTileWaves != wave) continue;  // wave-uniform
@@ -483,6 +441,34 @@ __device__ __forceinline__ void tile_item(const TileParams& p, int tile, int c, 
     if (slot >= 0 && slot < kN) p.next_pre[rc * kN + slot] = val;
     else if (slot >= kN && slot < 2 * kN) p.next_post[rc * kN + slot - kN] = val;
     else if (slot >= 2 * kN) p.next_comb[rc * kN * kN + slot - 2 * kN] = val;
+  }
+
+  // --- layer input (and MXFP8)
+  {
+    float w[8], o[8];
+    unpack8(wv, w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (y[e] * inv) * w[e];
+    const uint4 ob = pack8_round(o);
+    if (active) p.layer_out[(size_t)r * p.hv + v] = ob;
+    if constexpr (MXFP8) {
+      // 32-element block = the quad of lanes holding vectors v & ~3 .. v | 3
+      float q[8];
+      unpack8(ob, q);
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(q[e]));
+      amax = fmaxf(amax, dpp_f32<kDppQuadXor1>(amax));
+      amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
+      const int ex = e8m0_exponent(__float_as_uint(amax));
+      const float sc = __uint_as_float((uint32_t)(127 - ex) << 23);
+      const uint32_t lo = cvt_pk4_e4m3(q[0] * sc, q[1] * sc, q[2] * sc, q[3] * sc);
+      const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
+      if (active) {
+        p.mx_data[(size_t)r * p.hv + v] = make_uint2(lo, hi);
+        if ((v & 3) == 0) p.mx_scale[(size_t)r * (p.hidden / 32) + (v >> 2)] = (uint8_t)(ex + 127);
+      }
+    }
   }
 }
 
@@ -532,7 +518,7 @@ size_t boundary_tile_words(int rows, int hidden) {
 
 bool boundary_tile_fits(int hidden, int wgs_per_xcd) {
   const int chunks = boundary_tile_chunks(hidden);
-  return chunks <= kMaxTileChunks && chunks <= kFinishBatch && chunks <= wgs_per_xcd;
+  return chunks <= kFinishBatch && chunks <= wgs_per_xcd;
 }
 
 hipError_t launch_boundary_tile(const TileLaunch& T, hipStream_t stream) {
