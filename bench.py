@@ -218,13 +218,25 @@ def main():
         step = chain_mod.DecodeChain.from_synth(dev)
         log(f"  inputs ready in {time.time() - t0:.1f} s ({step.input_bytes() / 1e9:.2f} GB)")
         k = max(3, args.steps // 40)
+        out = {}
+        s4 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, fused=True)
+        e4, g4 = time_calls(torch, [s4.run], k, 2)
+        out["chain_decode_step"] = {
+            "us_per_step": round(g4, 1), "us_per_step_eager": None if e4 is None else round(e4, 1),
+            "algorithmic_bytes": int(s4.algorithmic_bytes()),
+            "gb_per_s": round(s4.algorithmic_bytes() / g4 / 1e3, 1),
+            "note": "each boundary and the coefficient call after it in one kernel "
+                    "(mhc_boundary_coeffs / mhc_finalize_coeffs)"}
+        log(f"  chain (fused) {out['chain_decode_step']}")
+        del s4
         us_e, us_g = time_calls(torch, [step.run], k, 2)
-        out = {"chain_decode_step": {
+        out["chain_decode_step_unfused"] = {
             "us_per_step": round(us_g, 1),
             "us_per_step_eager": None if us_e is None else round(us_e, 1),
             "algorithmic_bytes": int(step.algorithmic_bytes()),
-            "gb_per_s": round(step.algorithmic_bytes() / us_g / 1e3, 1)}}
-        log(f"  chain {out['chain_decode_step']}")
+            "gb_per_s": round(step.algorithmic_bytes() / us_g / 1e3, 1),
+            "note": "boundary calls, each followed by a separate mhc_pre_coeffs call"}
+        log(f"  chain (unfused) {out['chain_decode_step_unfused']}")
         s3 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, deferred=True)
         e3, g3 = time_calls(torch, [s3.run], k, 2)
         out["chain_decode_step_deferred"] = {
@@ -234,16 +246,7 @@ def main():
                     "consumes (no epilogue launch)"}
         log(f"  chain deferred {out['chain_decode_step_deferred']}")
         del s3
-        s4 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, fused=True)
-        e4, g4 = time_calls(torch, [s4.run], k, 2)
-        out["chain_decode_step_fused"] = {
-            "us_per_step": round(g4, 1), "us_per_step_eager": None if e4 is None else round(e4, 1),
-            "algorithmic_bytes": int(s4.algorithmic_bytes()),
-            "gb_per_s": round(s4.algorithmic_bytes() / g4 / 1e3, 1),
-            "note": "each boundary and the coefficient call after it in one kernel "
-                    "(mhc_boundary_coeffs / mhc_finalize_coeffs)"}
-        log(f"  chain fused {out['chain_decode_step_fused']}")
-        del s4
+
         for side in (False, True):
             s2 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, standin=True,
                                        side_stream=side)
