@@ -86,13 +86,16 @@ struct TileParams {
   const float4* pre;        // [rows] (4 floats)
   const uint4* norm_w;      // [hv]
   float eps;
-  int rows, hv, hidden, chunks;
+  int rows, hv, chunks;     // hidden = 8 hv
   uint4* layer_out;         // [rows][hv]
   uint2* mx_data;           // [rows][hv]
   uint8_t* mx_scale;        // [rows][hidden / 32]
   // the next coefficients
   const uint4* fn;          // [4 * hidden][24] bf16, 3 vectors per k row
-  CoeffEpilogue coef;       // scale, base, K, eps, alpha, iters (part unused)
+  const float* scale;       // [3]
+  const float* base;        // [24]
+  float rms_eps, pre_eps, sk_eps, alpha;
+  int iters;
   float* next_pre;          // [rows][4]
   float* next_post;         // [rows][4]
   float* next_comb;         // [rows][16]
@@ -140,8 +143,9 @@ struct TileShared {
 };
 
 template <bool FINALIZE, bool MXFP8>
-__device__ __forceinline__ void tile_item(const TileParams& p, int tile, int c, TileShared& S,
-                                          float sc_l, float base_l) {
+__device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilogue& coef,
+                                          int tile, int c, TileShared& S, float sc_l,
+                                          float base_l) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -170,8 +174,8 @@ __device__ __forceinline__ void tile_item(const TileParams& p, int tile, int c, 
     const int q = tid + j * kTileThreads;        // < 4 * 256 * 3
     const int i = q / (kTileH * 3), rem = q % (kTileH * 3);
     const int kk = rem / 3, part = rem % 3;
-    const int h = min(c * kTileH + kk, p.hidden - 1);  // past the end: zeroed below
-    fv[j] = p.fn[((size_t)i * p.hidden + h) * 3 + part];
+    const int h = min(c * kTileH + kk, (p.hv * 8) - 1);  // past the end: zeroed below
+    fv[j] = p.fn[((size_t)i * (p.hv * 8) + h) * 3 + part];
   }
   const float4 pst4 = p.post[rl];
   float4 cmb4[kN];
@@ -312,7 +316,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, int tile, int c, 
     const int q = tid + j * kTileThreads;
     const int i = q / (kTileH * 3), rem = q % (kTileH * 3);
     const int kk = rem / 3, c0 = (rem % 3) * 8;
-    const bool ok = c * kTileH + kk < p.hidden;
+    const bool ok = c * kTileH + kk < (p.hv * 8);
     const uint32_t u[4] = {ok ? fv[j].x : 0u, ok ? fv[j].y : 0u, ok ? fv[j].z : 0u,
                            ok ? fv[j].w : 0u};
 #pragma unroll
@@ -393,7 +397,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, int tile, int c, 
       part = vl < p.chunks ? __uint_as_float((unsigned)w) : 0.f;
     }
     const float tot = half_wave_sum(part);
-    inv = 1.0f / sqrtf(tot / (float)p.hidden + p.eps);
+    inv = 1.0f / sqrtf(tot / (float)(p.hv * 8) + p.eps);
     if (c == 0 && row_ok && vl == 0)
       __hip_atomic_store(p.epoch + r, S.want[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -437,7 +441,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, int tile, int c, 
       }
     }
     int slot;
-    const float val = coeff_from_sums(p.coef, lane, acc, sc_l, base_l, &slot);
+    const float val = coeff_from_sums(coef, lane, acc, sc_l, base_l, &slot);
     if (slot >= 0 && slot < kN) p.next_pre[rc * kN + slot] = val;
     else if (slot >= kN && slot < 2 * kN) p.next_post[rc * kN + slot - kN] = val;
     else if (slot >= 2 * kN) p.next_comb[rc * kN * kN + slot - 2 * kN] = val;
@@ -466,7 +470,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, int tile, int c, 
       const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
       if (active) {
         p.mx_data[(size_t)r * p.hv + v] = make_uint2(lo, hi);
-        if ((v & 3) == 0) p.mx_scale[(size_t)r * (p.hidden / 32) + (v >> 2)] = (uint8_t)(ex + 127);
+        if ((v & 3) == 0) p.mx_scale[(size_t)r * ((p.hv * 8) / 32) + (v >> 2)] = (uint8_t)(ex + 127);
       }
     }
   }
@@ -475,8 +479,21 @@ __device__ __forceinline__ void tile_item(const TileParams& p, int tile, int c, 
 template <bool FINALIZE, bool MXFP8>
 __global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_kernel(const TileParams p) {
   __shared__ __attribute__((aligned(16))) TileShared S;
+  // the coefficient epilogue's arguments (kept out of the kernel argument block, which
+  // stays within 256 bytes)
+  CoeffEpilogue coef;
+  coef.part = nullptr;
+  coef.ks_count = 0;
+  coef.scale = p.scale;
+  coef.base = p.base;
+  coef.K = kN * p.hv * 8;
+  coef.rms_eps = p.rms_eps;
+  coef.pre_eps = p.pre_eps;
+  coef.sk_eps = p.sk_eps;
+  coef.alpha = p.alpha;
+  coef.iters = p.iters;
   float sc_l, base_l;
-  coeff_lane_scale_base(p.coef, threadIdx.x & (kWave - 1), &sc_l, &base_l);
+  coeff_lane_scale_base(coef, threadIdx.x & (kWave - 1), &sc_l, &base_l);
   const int wg = blockIdx.x;
   const int xcd = wg % kXcd;
   const int local = wg / kXcd;
@@ -486,7 +503,7 @@ __global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_kernel(const Ti
     const int tile = (round * p.tiles_per_round + jt) * kXcd + xcd;
     if (tile * kTileRows >= p.rows) break;  // uniform per workgroup; later rounds go higher
     if (round > 0) __syncthreads();          // LDS reused
-    tile_item<FINALIZE, MXFP8>(p, tile, c, S, sc_l, base_l);
+    tile_item<FINALIZE, MXFP8>(p, coef, tile, c, S, sc_l, base_l);
   }
 }
 
@@ -540,14 +557,19 @@ hipError_t launch_boundary_tile(const TileLaunch& T, hipStream_t stream) {
   p.norm_w = reinterpret_cast<const uint4*>(L.norm_weight);
   p.eps = L.eps;
   p.rows = L.rows;
-  p.hidden = L.hidden;
   p.hv = L.hidden / 8;
   p.chunks = boundary_tile_chunks(L.hidden);
   p.layer_out = reinterpret_cast<uint4*>(L.layer_input_out);
   p.mx_data = reinterpret_cast<uint2*>(L.mx_data_out);
   p.mx_scale = L.mx_scale_out;
   p.fn = reinterpret_cast<const uint4*>(T.fn);
-  p.coef = T.coef;
+  p.scale = T.coef.scale;
+  p.base = T.coef.base;
+  p.rms_eps = T.coef.rms_eps;
+  p.pre_eps = T.coef.pre_eps;
+  p.sk_eps = T.coef.sk_eps;
+  p.alpha = T.coef.alpha;
+  p.iters = T.coef.iters;
   p.next_pre = T.next_pre;
   p.next_post = T.next_post;
   p.next_comb = T.next_comb;
