@@ -86,6 +86,9 @@ def _check_case(kind, rows, hidden, seed):
     ("finalize", 64, 7168), ("boundary", 16, 1024), ("boundary", 5, 1056), ("finalize", 3, 1056),
     ("boundary", 200, 2048), ("finalize", 130, 4096), ("boundary", 1, 8), ("boundary", 17, 1000),
     ("finalize", 33, 4096), ("boundary", 9, 16384),
+    # 32 chunks (the most the kernel takes: one per lane of a half wave), and rounds of
+    # tiles at hidden 7168 (one tile per XCD per round)
+    ("boundary", 20, 8192), ("finalize", 300, 7168), ("boundary", 257, 7168),
 ])
 def test_fused_matches_oracle(kind, rows, hidden):
     say(f"case: fused {kind} + next coefficients rows={rows} hidden={hidden}")
