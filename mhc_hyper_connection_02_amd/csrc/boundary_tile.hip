@@ -13,7 +13,8 @@
 // slices or gathered expert rows, mHC post, collapse, RMSNorm, MXFP8), in the same
 // arithmetic order, so the new streams are bit-identical to mhc_boundary's. (A layout
 // with 16 rows across consecutive lanes, the MFMA operand layout, made every 16-lane
-// memory pass touch 16 cache lines and was measured 2.6x slower.)
+// memory pass touch 16 cache lines: 25.8 us per 128-row call against 17.8 with this one,
+// before the later changes.)
 //
 // The projection. The bf16 new streams are also written to LDS ([stream][row][vector],
 // rows padded against bank conflicts). Wave w then reads, for each stream i, 16 rows by
