@@ -470,7 +470,7 @@ int mhc_collapse_mean(mhc_handle h, const uint16_t* streams, int rows, uint16_t*
 
 namespace {
 
-int check_coeff_args(const mhc_ctx* h, const mhc_coeff_args* a) {
+int check_coeff_args(const mhc_coeff_args* a) {
   if (!a) return MHC_ERR_INVALID_ARG;
   if (a->sinkhorn_iters < 0 || a->sinkhorn_iters > kMaxSinkhornIters) return MHC_ERR_SHAPE;
   if (!(a->rms_eps >= 0.0f) || !(a->sinkhorn_eps >= 0.0f)) return MHC_ERR_SHAPE;
@@ -479,7 +479,6 @@ int check_coeff_args(const mhc_ctx* h, const mhc_coeff_args* a) {
   if (!aligned(a->fn, 16) || !aligned(a->scale, 4) || !aligned(a->base, 4) ||
       !aligned(a->pre_out, 4) || !aligned(a->post_out, 4) || !aligned(a->comb_out, 4))
     return MHC_ERR_ALIGN;
-  (void)h;
   return MHC_OK;
 }
 
@@ -535,7 +534,7 @@ int mhc_boundary_coeffs(mhc_handle h, const uint16_t* x_partials, int tp,
                      layer_input_out, mx_data_out, mx_scale_out);
   if (st != MHC_OK) return st;
   if (!aligned(x_partials, 16)) return MHC_ERR_ALIGN;
-  st = check_coeff_args(h, next);
+  st = check_coeff_args(next);
   if (st != MHC_OK) return st;
   st = check_device(h);
   if (st != MHC_OK) return st;
@@ -567,7 +566,7 @@ int mhc_finalize_coeffs(mhc_handle h, const uint16_t* gemm2_permuted, int num_pe
   if (!aligned(gemm2_permuted, 16) || !aligned(shared_output, 16) || !aligned(expert_weights, 4) ||
       !aligned(expanded_idx_to_permuted_idx, 4))
     return MHC_ERR_ALIGN;
-  st = check_coeff_args(h, next);
+  st = check_coeff_args(next);
   if (st != MHC_OK) return st;
   st = check_device(h);
   if (st != MHC_OK) return st;
