@@ -2,6 +2,11 @@
 
   python -m mhc_hyper_connection_02_amd.profiling stats <trace_dir> --cmd "<command>"
       per-kernel dispatch count and duration from a ``--kernel-trace --stats`` run
+  python -m mhc_hyper_connection_02_amd.profiling mfma <dir> [<dir> ...] --match <substr>
+      --cmd "<commands>"
+      per (kernel, grid size): mean of every counter found in the ``--pmc`` runs' CSVs
+      (e.g. SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE,
+      MfmaUtil) and the mean dispatch duration of those runs
   python -m mhc_hyper_connection_02_amd.profiling traffic --fetch <dir> --write <dir>
       --cal-fetch <dir> --cal-write <dir> --cal-bytes N --kernel <substring>
       --block B --source-hash H --cmd "<commands>" --out <json>
@@ -52,18 +57,48 @@ def counter_mean(pmc_dir, counter, kernel_substring):
     return sum(vals) / len(vals), len(vals)
 
 
+def counters_by_dispatch_shape(dirs, matches):
+    """{(kernel, grid_size): {counter: [values], "_dur_ns": [durations]}} over the counter
+    CSVs of the given ``--pmc`` runs, for kernels whose name contains one of `matches`."""
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in dirs:
+        for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+            name = r["Kernel_Name"]
+            if not any(m in name for m in matches):
+                continue
+            key = (name, int(r["Grid_Size"]))
+            out[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            out[key]["_dur_ns"].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
     s = sub.add_parser("stats")
     s.add_argument("trace_dir")
     s.add_argument("--cmd", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("dirs", nargs="+")
+    m.add_argument("--match", action="append", required=True)
+    m.add_argument("--cmd", required=True)
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "cal_fetch", "cal_write", "kernel", "source_hash", "cmd", "out"):
         t.add_argument("--" + k.replace("_", "-"), required=True)
     t.add_argument("--cal-bytes", type=int, required=True)
     t.add_argument("--block", type=int, required=True)
     a = ap.parse_args(argv)
+
+    if a.what == "mfma":
+        print(f"# rocprofv3 --pmc counters per (kernel, grid size), mean per dispatch\n"
+              f"# commands: {a.cmd}\n")
+        for (name, grid), cs in sorted(counters_by_dispatch_shape(a.dirs, a.match).items()):
+            durs = cs.pop("_dur_ns")
+            print(f"{name}\n  grid {grid} threads, {len(durs)} counter samples, "
+                  f"mean duration under --pmc {sum(durs) / len(durs) / 1e3:.2f} us")
+            for c, v in sorted(cs.items()):
+                print(f"  {c:32s} {sum(v) / len(v):14.6g}  ({len(v)} dispatches)")
+        return 0
 
     if a.what == "stats":
         print(f"# rocprofv3 kernel trace: per-dispatch duration\n# command: {a.cmd}\n")
