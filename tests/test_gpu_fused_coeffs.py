@@ -249,3 +249,35 @@ def test_fused_argument_checks():
                                    p(dv["norm_weight"]), 1e-6, R, p(so), p(li), None, None,
                                    ctypes.byref(a), None) == 1
     torch.cuda.synchronize()
+
+
+def test_fused_calls_beside_a_gemm_on_another_stream():
+    """Fused calls on one stream while a large bf16 GEMM runs on another (CUs taken by the
+    GEMM delay some of a tile's workgroups; the waits are bounded and must still end with
+    every word seen): results equal those of the same calls run alone, no timeouts."""
+    rows, hidden = 128, 7168
+    say(f"case: fused calls beside a concurrent GEMM rows={rows} hidden={hidden}")
+    h = handle_for(hidden, rows)
+    d = synth.boundary_inputs(95, rows=rows, hidden=hidden, tp=8, x_sigma=0.5, mxfp8=True)
+    nxt, _ = _next_args(96, hidden)
+    alone, alone_next = _run_fused(h, "boundary", d, nxt, True)
+    a = torch.randn((4096, 4096), device="cuda").to(torch.bfloat16)
+    b = torch.randn((4096, 4096), device="cuda").to(torch.bfloat16).contiguous()
+    other = torch.cuda.Stream()
+    dv = {k: T(v) for k, v in d.items() if isinstance(v, np.ndarray)}
+    outs = []
+    torch.cuda.synchronize()
+    with torch.cuda.stream(other):
+        for _ in range(4):
+            torch.matmul(a, b)
+    for _ in range(8):
+        o = binding.boundary_coeffs(h, dv["x_partials"], dv["residual"], dv["post"], dv["comb"],
+                                    dv["pre"], dv["norm_weight"], d["eps"], nxt, mxfp8=True)
+        outs.append(o)
+    torch.cuda.synchronize()
+    for o in outs:
+        for k in alone:
+            assert np.array_equal(N(o[k]), alone[k]), k
+        for x, y in zip(o["next"], alone_next):
+            assert np.array_equal(N(x), y)
+    assert h.errors() == 0
