@@ -189,6 +189,13 @@ def test_fused_chain_every_step_and_graph_replays():
     _teacher_forced_checks(step, set(range(len(step.subs))))
     want = N(step.run())
     torch.cuda.synchronize()
+    # end to end against the oracle chain on the same inputs
+    subs = [synth.chain_sublayer(L, ffn) for L in range(3) for ffn in (False, True)]
+    p = synth.chain_params()
+    _, mean_ora = oracle.decode_chain(synth.chain_embedding(), subs, p["rms_eps"], p["hc_eps"],
+                                      p["post_alpha"], p["sinkhorn_iters"], p["norm_eps"])
+    same = assert_bf16_close(want, mean_ora, "fused chain mean after 3 layers")
+    say(f"  final mean bit-identical to the oracle chain in {same:.2%} of elements")
     again = N(step.run())
     torch.cuda.synchronize()
     assert np.array_equal(again, want), "fused step not deterministic"
