@@ -95,6 +95,33 @@ def test_fused_matches_oracle(kind, rows, hidden):
     _check_case(kind, rows, hidden, 6000 + rows + hidden)
 
 
+@pytest.mark.parametrize("kind,rows,hidden,width", [
+    ("finalize", 24, 2048, 12), ("finalize", 40, 1024, 3), ("finalize", 7, 4096, 1),
+    ("boundary", 24, 2048, 1), ("boundary", 40, 1024, 3), ("boundary", 9, 4096, 13),
+])
+def test_fused_other_tp_and_top_k(kind, rows, hidden, width):
+    """TP slice counts and top_k other than 8: the partial-slice loop's batches and the
+    finalize's slots beyond the first eight."""
+    say(f"case: fused {kind} rows={rows} hidden={hidden} tp/top_k={width}")
+    mx = hidden % 32 == 0
+    seed = 7100 + rows + width
+    if kind == "boundary":
+        d = synth.boundary_inputs(seed, rows=rows, hidden=hidden, tp=width, x_sigma=0.5, mxfp8=mx)
+        h = handle_for(hidden, rows, tp=width)
+    else:
+        d = synth.finalize_inputs(seed, rows=rows, hidden=hidden, top_k=width, mxfp8=mx)
+        h = handle_for(hidden, rows, top_k=width)
+    nxt, c = _next_args(seed + 1, hidden)
+    got, nx = _run_fused(h, kind, d, nxt, mx)
+    want = oracle_boundary(d) if kind == "boundary" else oracle_finalize(d)
+    compare_boundary_outputs(got, want, f"fused {kind} width {width}")
+    plain = _run_plain(h, kind, d, mx)
+    assert np.array_equal(got["residual"], plain["residual"])
+    for name, a, b in zip(("pre", "post", "comb"), nx, _oracle_next(got["residual"], c)):
+        assert_f32_close(a, b, f"fused {kind} width {width} next {name}")
+    assert h.errors() == 0
+
+
 def test_fallback_paths_equal_the_two_calls():
     """Misaligned post/comb/pre (4-byte aligned views) and rows beyond the fused scratch run
     the two calls: every output equals mhc_boundary + mhc_pre_coeffs bit for bit."""
