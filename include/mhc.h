@@ -332,6 +332,11 @@ typedef struct mhc_coeff_args {
  * are 16-byte aligned and a row's 256-element pieces fit the workgroups one XCD holds at
  * once (H <= 8192 on MI355X); otherwise the call runs the two calls (same results as
  * above). A pending deferred coefficient call is enqueued first.
+ * Concurrency: the single kernel may occupy every resident slot of an XCD for its tile's
+ * workgroups, which wait on one another. Kernels of other streams only delay it, but two
+ * of these calls running at the same time on different streams can each hold part of an
+ * XCD and wait for the rest: their waits then end at the spin limit (counted by
+ * mhc_get_errors) with wrong results. Issue fused calls of one device on one stream.
  */
 int mhc_boundary_coeffs(mhc_handle h, const uint16_t* x_partials, int tp,
                         const uint16_t* residual, const float* post, const float* comb,
