@@ -19,7 +19,8 @@ def test_header_declares_the_entry_points():
     for want in ("mhc_create", "mhc_destroy", "mhc_reset", "mhc_set_option", "mhc_boundary",
                  "mhc_residual_only", "mhc_finalize", "mhc_collapse_mean", "mhc_pre_coeffs",
                  "mhc_status_string", "mhc_get_errors", "mhc_first", "mhc_collapse_norm",
-                 "mhc_pre_coeffs_deferred", "mhc_pre_coeffs_flush"):
+                 "mhc_pre_coeffs_deferred", "mhc_pre_coeffs_flush", "mhc_boundary_coeffs",
+                 "mhc_finalize_coeffs"):
         assert want in names
 
 
@@ -77,3 +78,64 @@ def test_null_handle_is_invalid_everywhere():
     assert lib.mhc_pre_coeffs_flush(z, z) == 1
     assert lib.mhc_first(z, z, z, 0.0, 1, z, z, z, z, z) == 1
     assert lib.mhc_collapse_norm(z, z, z, z, 0.0, 1, z, z, z, z) == 1
+    assert lib.mhc_boundary_coeffs(z, z, 1, z, z, z, z, z, 0.0, 1, z, z, z, z, None, z) == 1
+    assert lib.mhc_finalize_coeffs(z, z, 1, z, z, z, z, z, z, z, z, 0.0, 1, z, z, z, z, None,
+                                   z) == 1
+
+
+def test_coeff_args_struct_matches_the_header(tmp_path):
+    """The binding's ctypes mirror of mhc_coeff_args has the C struct's size and field
+    offsets (a small C program compiled against include/mhc.h prints them)."""
+    fields = [f for f, _ in binding.CoeffArgs._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include "mhc.h"\n#include <stddef.h>\n#include <stdio.h>\nint main(void) {\n'
+        '  printf("%zu\\n", sizeof(mhc_coeff_args));\n'
+        + "".join(f'  printf("%zu\\n", offsetof(mhc_coeff_args, {f}));\n' for f in fields)
+        + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(binding.HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(binding.CoeffArgs)] + [getattr(binding.CoeffArgs, f).offset
+                                                 for f in fields]
+    assert got == want
+
+
+class _StubHandle:
+    """Just the sizes the binding reads; every case below fails before the library is called."""
+    hidden, hc_mult, top_k = 64, 4, 8
+    ptr = None
+
+
+def _fused_args(rows=3, hidden=64, fn_rows=None, scale_len=3):
+    import torch
+    n, nc = 4, 24
+    d = dict(
+        x=torch.zeros((2, rows, hidden), dtype=torch.bfloat16),
+        s=torch.zeros((rows, n, hidden), dtype=torch.bfloat16),
+        post=torch.zeros((rows, n)), comb=torch.zeros((rows, n, n)), pre=torch.zeros((rows, n)),
+        w=torch.zeros((hidden,), dtype=torch.bfloat16))
+    nxt = {"fn": torch.zeros((fn_rows or n * hidden, nc), dtype=torch.bfloat16),
+           "scale": torch.zeros((scale_len,)), "base": torch.zeros((nc,)), "rms_eps": 1e-6,
+           "pre_eps": 1e-6, "sinkhorn_eps": 1e-6, "post_alpha": 2.0, "sinkhorn_iters": 20}
+    return d, nxt
+
+
+@pytest.mark.parametrize("case", ["no_pre", "fn_shape", "scale_len", "next_out_shape",
+                                  "streams_hidden"])
+def test_fused_binding_rejects_bad_arguments(case):
+    import torch
+    h = _StubHandle()
+    d, nxt = _fused_args(fn_rows=8 if case == "fn_shape" else None,
+                         scale_len=4 if case == "scale_len" else 3)
+    pre = None if case == "no_pre" else d["pre"]
+    if case == "streams_hidden":
+        d["s"] = torch.zeros((3, 4, 32), dtype=torch.bfloat16)
+    next_out = None
+    if case == "next_out_shape":
+        next_out = (torch.zeros((3, 4)), torch.zeros((3, 4)), torch.zeros((3, 16)))
+    with pytest.raises(ValueError):
+        binding.boundary_coeffs(h, d["x"], d["s"], d["post"], d["comb"], pre, d["w"], 1e-6, nxt,
+                                next_out=next_out)
