@@ -229,6 +229,16 @@ def main():
                     "(mhc_boundary_coeffs / mhc_finalize_coeffs)"}
         log(f"  chain (fused) {out['chain_decode_step']}")
         del s4
+        s5 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, fused=True,
+                                   deferred=True)
+        e5, g5 = time_calls(torch, [s5.run], k, 2)
+        out["chain_decode_step_fused_deferred"] = {
+            "us_per_step": round(g5, 1), "us_per_step_eager": None if e5 is None else round(e5, 1),
+            "gb_per_s": round(s5.algorithmic_bytes() / g5 / 1e3, 1),
+            "note": "fused calls that leave the next coefficients as partial sums, finished "
+                    "by the next fused call's kernel (mhc_coeff_args.deferred)"}
+        log(f"  chain (fused, deferred) {out['chain_decode_step_fused_deferred']}")
+        del s5
         us_e, us_g = time_calls(torch, [step.run], k, 2)
         out["chain_decode_step_unfused"] = {
             "us_per_step": round(us_g, 1),

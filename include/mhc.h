@@ -295,7 +295,13 @@ int mhc_pre_coeffs_flush(mhc_handle h, mhc_stream_t stream);
 /*
  * The arguments of a coefficient call (as mhc_pre_coeffs) carried by the fused calls
  * below. A host struct, read during the call only; the pointers are device pointers
- * with mhc_pre_coeffs's layouts and alignments.
+ * with mhc_pre_coeffs's layouts and alignments. deferred = 1 makes the coefficient call
+ * a deferred one (as mhc_pre_coeffs_deferred): the fused kernel leaves the coefficients
+ * as partial sums in the handle and the call stays pending; its outputs are written by
+ * the next call that consumes them (a boundary, finalize, residual-only or fused call
+ * whose post and comb, and pre if it takes one, are these outputs, for the same rows),
+ * by the epilogue that any other call enqueues first, or by mhc_pre_coeffs_flush. Other
+ * values than 0 and 1 give MHC_ERR_INVALID_ARG.
  */
 typedef struct mhc_coeff_args {
   const uint16_t* fn;       /* [n*H, 2n + n*n] bf16 row-major, 16-byte aligned */
@@ -303,6 +309,7 @@ typedef struct mhc_coeff_args {
   const float* base;        /* [2n + n*n] */
   float rms_eps, pre_eps, sinkhorn_eps, post_alpha;
   int sinkhorn_iters;       /* [0, 1000] */
+  int deferred;             /* 0 or 1: leave the coefficients pending (see below) */
   float* pre_out;           /* [R, n] */
   float* post_out;          /* [R, n] */
   float* comb_out;          /* [R, n, n] */
@@ -331,7 +338,10 @@ typedef struct mhc_coeff_args {
  * argument. The single kernel runs when rows <= min(max_rows, 1024), post, comb and pre
  * are 16-byte aligned and a row's 256-element pieces fit the workgroups one XCD holds at
  * once (H <= 8192 on MI355X); otherwise the call runs the two calls (same results as
- * above). A pending deferred coefficient call is enqueued first.
+ * above). A pending deferred coefficient call whose outputs are this call's post, comb and
+ * pre (same rows) is finished inside the kernel when this call is deferred too and the
+ * pending call was a fused one (its partial sums are the fused kernel's); in the two-call
+ * form the boundary kernel finishes it; otherwise its epilogue is enqueued first.
  * Concurrency: the single kernel may occupy every resident slot of an XCD for its tile's
  * workgroups, which wait on one another. Kernels of other streams only delay it, but two
  * of these calls running at the same time on different streams can each hold part of an

@@ -34,7 +34,7 @@ class CoeffArgs(ctypes.Structure):
     """``mhc_coeff_args``: a coefficient call's arguments, for the fused calls."""
     _fields_ = [("fn", _vp), ("scale", _vp), ("base", _vp), ("rms_eps", _f), ("pre_eps", _f),
                 ("sinkhorn_eps", _f), ("post_alpha", _f), ("sinkhorn_iters", _i),
-                ("pre_out", _vp), ("post_out", _vp), ("comb_out", _vp)]
+                ("deferred", _i), ("pre_out", _vp), ("post_out", _vp), ("comb_out", _vp)]
 
 
 _SIGS = {
@@ -394,7 +394,7 @@ def pre_coeffs_flush(h, stream=None):
     _check(load_library().mhc_pre_coeffs_flush(h.ptr, _stream(stream)), "mhc_pre_coeffs_flush")
 
 
-def _coeff_args(h, rows, dev, nxt, out):
+def _coeff_args(h, rows, dev, nxt, out, deferred):
     """Check a coefficient call's arguments (a dict with fn, scale, base, rms_eps, pre_eps,
     sinkhorn_eps, post_alpha, sinkhorn_iters) and its outputs; -> (CoeffArgs, outputs)."""
     n, hidden = h.hc_mult, h.hidden
@@ -412,16 +412,18 @@ def _coeff_args(h, rows, dev, nxt, out):
     _need(comb, "next comb_out", torch.float32, (rows, n, n), dev)
     a = CoeffArgs(_ptr(nxt["fn"]), _ptr(nxt["scale"]), _ptr(nxt["base"]), float(nxt["rms_eps"]),
                   float(nxt["pre_eps"]), float(nxt["sinkhorn_eps"]), float(nxt["post_alpha"]),
-                  int(nxt["sinkhorn_iters"]), _ptr(pre), _ptr(post), _ptr(comb))
+                  int(nxt["sinkhorn_iters"]), 1 if deferred else 0, _ptr(pre), _ptr(post),
+                  _ptr(comb))
     return a, out
 
 
 def boundary_coeffs(h, x_partials, residual, post, comb, pre, norm_weight, eps, nxt,
                     mxfp8=False, residual_out=None, layer_input_out=None, mx_out=None,
-                    next_out=None, stream=None):
+                    next_out=None, deferred=False, stream=None):
     """``mhc_boundary_coeffs``: :func:`boundary` and then :func:`pre_coeffs` on its new streams
     with the arguments in ``nxt`` (a dict), in one kernel. Returns boundary's dict plus
-    ``next`` = (pre, post, comb) of the next sublayer."""
+    ``next`` = (pre, post, comb) of the next sublayer. ``deferred``: the next coefficients
+    stay pending, as after :func:`pre_coeffs_deferred`."""
     rows, n, hidden, dev = _check_mix_inputs(h, residual, post, comb)
     if x_partials.dim() != 3:
         raise ValueError("x_partials must be [tp, rows, hidden]")
@@ -431,7 +433,7 @@ def boundary_coeffs(h, x_partials, residual, post, comb, pre, norm_weight, eps, 
         raise ValueError("the fused call writes a layer input: pre is required")
     ro, li, md, ms = _mix_outputs(h, residual, pre, norm_weight, mxfp8, residual_out,
                                   layer_input_out, mx_out)
-    a, nout = _coeff_args(h, rows, dev, nxt, next_out)
+    a, nout = _coeff_args(h, rows, dev, nxt, next_out, deferred)
     st = load_library().mhc_boundary_coeffs(h.ptr, _ptr(x_partials), tp, _ptr(residual),
                                             _ptr(post), _ptr(comb), _ptr(pre),
                                             _ptr(norm_weight), float(eps), rows, _ptr(ro),
@@ -446,9 +448,9 @@ def boundary_coeffs(h, x_partials, residual, post, comb, pre, norm_weight, eps, 
 def finalize_coeffs(h, gemm2_permuted, expert_weights, expanded_idx_to_permuted_idx,
                     shared_output, residual, post, comb, pre, norm_weight, eps, nxt,
                     mxfp8=False, residual_out=None, layer_input_out=None, mx_out=None,
-                    next_out=None, stream=None):
+                    next_out=None, deferred=False, stream=None):
     """``mhc_finalize_coeffs``: :func:`finalize` and then :func:`pre_coeffs` on its new
-    streams, in one kernel; returns as :func:`boundary_coeffs`."""
+    streams, in one kernel; returns and defers as :func:`boundary_coeffs`."""
     rows, n, hidden, dev = _check_mix_inputs(h, residual, post, comb)
     if gemm2_permuted.dim() != 2:
         raise ValueError("gemm2_permuted must be [num_permuted, hidden]")
@@ -462,7 +464,7 @@ def finalize_coeffs(h, gemm2_permuted, expert_weights, expanded_idx_to_permuted_
         raise ValueError("the fused call writes a layer input: pre is required")
     ro, li, md, ms = _mix_outputs(h, residual, pre, norm_weight, mxfp8, residual_out,
                                   layer_input_out, mx_out)
-    a, nout = _coeff_args(h, rows, dev, nxt, next_out)
+    a, nout = _coeff_args(h, rows, dev, nxt, next_out, deferred)
     st = load_library().mhc_finalize_coeffs(h.ptr, _ptr(gemm2_permuted), P, _ptr(expert_weights),
                                             _ptr(expanded_idx_to_permuted_idx),
                                             _ptr(shared_output), _ptr(residual), _ptr(post),

@@ -30,7 +30,9 @@ result unused), so that the overlap has something to hide under.
 Fused (``fused=True``): each boundary that is followed by a coefficient call runs as one
 call with it (``mhc_boundary_coeffs`` / ``mhc_finalize_coeffs``), which reads the current
 coefficients and writes the next ones in the same kernel, so the step alternates between
-two coefficient buffer sets.
+two coefficient buffer sets. With ``deferred=True`` as well, each fused call leaves the next
+coefficients as partial sums, and the next fused call finishes them in its own kernel while
+its loads are in flight (``mhc_coeff_args.deferred``).
 """
 
 import torch
@@ -64,8 +66,8 @@ class DecodeChain:
         self.fused = fused
         self.sets = [(self.pre, self.post, self.comb)]
         if fused:
-            if deferred or side_stream:
-                raise ValueError("fused boundaries take neither deferred nor side-stream calls")
+            if side_stream:
+                raise ValueError("fused boundaries take no side-stream calls")
             self.sets.append((torch.empty_like(self.pre), torch.empty_like(self.post),
                               torch.empty_like(self.comb)))
         self.next_args = [None if i + 1 == len(sublayers) else {
@@ -180,7 +182,8 @@ class DecodeChain:
             if self.record is not None:
                 self.record(i, "before", self)
             if self.fused and not last:
-                kw.update(residual_out=self.streams, next_out=self.sets[1 - cur])
+                kw.update(residual_out=self.streams, next_out=self.sets[1 - cur],
+                          deferred=self.deferred)
                 if "partials" in s:
                     binding.boundary_coeffs(h, s["partials"], self.streams, self.post, self.comb,
                                             nxt=self.next_args[i], **kw)

@@ -43,6 +43,8 @@ struct mhc_ctx {
   unsigned* epoch;
   unsigned* errors;
   unsigned long long* tile_words;  // the fused kernel's tagged partials
+  float* tile_part[2];     // a deferred fused call's coefficient partials (used in turn)
+  int tile_part_next;      // the buffer the next deferred fused call writes
   size_t zero_words;       // 32-bit words up to pre_part (cleared by mhc_reset)
   // a deferred coefficient call whose epilogue has not been enqueued yet
   bool pending;
@@ -254,7 +256,11 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   const size_t err_bytes = 256;
   const size_t tile_bytes = round_up(mhc::boundary_tile_words(h->tile_rows, hidden) * 8, 256);
   const size_t pre_bytes = round_up(pre_floats * sizeof(float), 256);
-  const size_t total = slot_bytes + epoch_bytes + err_bytes + tile_bytes + pre_bytes;
+  const size_t part_bytes =
+      round_up((size_t)h->tile_rows * 25 * mhc::boundary_tile_part_ks(hidden) * sizeof(float),
+               256);
+  const size_t total =
+      slot_bytes + epoch_bytes + err_bytes + tile_bytes + pre_bytes + 2 * part_bytes;
   void* base = nullptr;
   if (hipMalloc(&base, total) != hipSuccess) {
     delete h;
@@ -270,6 +276,10 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
       reinterpret_cast<unsigned long long*>(b + slot_bytes + epoch_bytes + err_bytes);
   h->pre_part =
       reinterpret_cast<float*>(b + slot_bytes + epoch_bytes + err_bytes + tile_bytes);
+  char* parts = b + slot_bytes + epoch_bytes + err_bytes + tile_bytes + pre_bytes;
+  h->tile_part[0] = reinterpret_cast<float*>(parts);
+  h->tile_part[1] = reinterpret_cast<float*>(parts + part_bytes);
+  h->tile_part_next = 0;
   h->zero_words = (slot_bytes + epoch_bytes + err_bytes + tile_bytes) / 4;
   hipError_t e = mhc::launch_fill_u32(reinterpret_cast<unsigned*>(base), total / 4, 0u, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -474,6 +484,7 @@ int check_coeff_args(const mhc_coeff_args* a) {
   if (!a) return MHC_ERR_INVALID_ARG;
   if (a->sinkhorn_iters < 0 || a->sinkhorn_iters > kMaxSinkhornIters) return MHC_ERR_SHAPE;
   if (!(a->rms_eps >= 0.0f) || !(a->sinkhorn_eps >= 0.0f)) return MHC_ERR_SHAPE;
+  if (a->deferred != 0 && a->deferred != 1) return MHC_ERR_INVALID_ARG;
   if (!a->fn || !a->scale || !a->base || !a->pre_out || !a->post_out || !a->comb_out)
     return MHC_ERR_INVALID_ARG;
   if (!aligned(a->fn, 16) || !aligned(a->scale, 4) || !aligned(a->base, 4) ||
@@ -486,16 +497,27 @@ int check_coeff_args(const mhc_coeff_args* a) {
 // the fused form applies, else the two calls. L is the boundary's launch, already filled.
 int boundary_then_coeffs(mhc_ctx* h, mhc::BoundaryLaunch& L, const mhc_coeff_args* a,
                          hipStream_t s) {
-  int st = flush_pending(h, s);
-  if (st != MHC_OK) return st;
   const bool fused = h->tile_rows >= L.rows && aligned(L.post, 16) && aligned(L.comb, 16) &&
                      aligned(L.pre, 16);
+  // a pending call whose outputs are this call's post, comb and pre is finished inside the
+  // kernel: the fused kernel takes it when this call is deferred too and the pending
+  // partial sums are a fused kernel's; the boundary kernel of the two-call form takes any
+  bool defer_in = false;
+  int st = MHC_OK;
+  if (fused) {
+    defer_in = h->pending && a->deferred && h->pend.ks_count > 0 && L.post == h->pend.post_out &&
+               L.comb == h->pend.comb_out && L.pre == h->pend.pre_out && L.rows == h->pend.rows;
+    st = defer_in ? MHC_OK : flush_pending(h, s);
+  } else {
+    st = take_pending(h, L, L.post, L.comb, L.pre, L.rows, s);
+  }
+  if (st != MHC_OK) return st;
   if (!fused) {
     st = launch_status(mhc::launch_boundary(L, s));
     if (st != MHC_OK) return st;
-    return mhc_pre_coeffs(h, L.residual_out, a->fn, a->scale, a->base, a->rms_eps, a->pre_eps,
-                          a->sinkhorn_eps, a->post_alpha, a->sinkhorn_iters, L.rows, a->pre_out,
-                          a->post_out, a->comb_out, s);
+    return (a->deferred ? mhc_pre_coeffs_deferred : mhc_pre_coeffs)(
+        h, L.residual_out, a->fn, a->scale, a->base, a->rms_eps, a->pre_eps, a->sinkhorn_eps,
+        a->post_alpha, a->sinkhorn_iters, L.rows, a->pre_out, a->post_out, a->comb_out, s);
   }
   mhc::TileLaunch T;
   T.b = L;
@@ -512,10 +534,41 @@ int boundary_then_coeffs(mhc_ctx* h, mhc::BoundaryLaunch& L, const mhc_coeff_arg
   T.next_pre = a->pre_out;
   T.next_post = a->post_out;
   T.next_comb = a->comb_out;
+  T.part_out = nullptr;
+  T.defer_in = defer_in;
+  T.in_coef = defer_in ? mhc::pre_epilogue_args(h->pend) : mhc::CoeffEpilogue{};
   T.words = h->tile_words;
   T.tile_rows = h->tile_rows;
   T.wgs_per_xcd = h->tile_wgs_per_xcd;
-  return launch_status(mhc::launch_boundary_tile(T, s));
+  if (!a->deferred) return launch_status(mhc::launch_boundary_tile(T, s));
+  // deferred: the kernel leaves the next coefficients as partials; the call is pending
+  // until a consumer or a flush finishes them
+  float* part = h->tile_part[h->tile_part_next];  // not the pending call's
+  T.part_out = part;
+  h->pending = false;  // taken (defer_in) or flushed above
+  st = launch_status(mhc::launch_boundary_tile(T, s));
+  if (st != MHC_OK) return st;
+  h->tile_part_next ^= 1;
+  mhc::PreLaunch P = {};
+  P.residual = L.residual_out;
+  P.fn = a->fn;
+  P.scale = a->scale;
+  P.base = a->base;
+  P.rms_eps = a->rms_eps;
+  P.pre_eps = a->pre_eps;
+  P.sinkhorn_eps = a->sinkhorn_eps;
+  P.post_alpha = a->post_alpha;
+  P.sinkhorn_iters = a->sinkhorn_iters;
+  P.rows = L.rows;
+  P.hidden = h->hidden;
+  P.pre_out = a->pre_out;
+  P.post_out = a->post_out;
+  P.comb_out = a->comb_out;
+  P.part = part;
+  P.ks_count = mhc::boundary_tile_part_ks(h->hidden);
+  h->pending = true;
+  h->pend = P;
+  return MHC_OK;
 }
 
 }  // namespace
@@ -601,7 +654,7 @@ int pre_coeffs_common(mhc_handle h, const uint16_t* residual, const uint16_t* fn
     return MHC_ERR_ALIGN;
   int st = check_device(h);
   if (st != MHC_OK) return st;
-  mhc::PreLaunch L;
+  mhc::PreLaunch L = {};
   L.residual = residual;
   L.fn = fn;
   L.scale = scale;

@@ -97,7 +97,10 @@ struct TileParams {
   const float* base;        // [24]
   float rms_eps, pre_eps, sk_eps, alpha;
   int iters;
-  float* next_pre;          // [rows][4]
+  union {
+    float* next_pre;        // [rows][4]
+    float* part_out;        // DEFER_OUT: [rows][25][part_ks] partials of the next call
+  };
   float* next_post;         // [rows][4]
   float* next_comb;         // [rows][16]
   // handoff
@@ -135,18 +138,74 @@ __device__ __forceinline__ float half_wave_sum(float v) {
   return v + __shfl_xor(v, 16, kWave);
 }
 
+// A pending coefficient call finished in this kernel: its epilogue arguments, with `part`
+// its per-chunk partial sums ([rows][25][ks_count], ks_count <= 32) written by the previous
+// fused kernel. A kernel argument of those variants only.
+struct TileDeferIn {
+  CoeffEpilogue coef;
+};
+
+// The coefficient epilogue of two rows in one wave: half h (lanes 32h .. 32h + 31) holds
+// row h's sums (lane 32h + l: value l, as coeff_from_sums's lane l), and row h's comb sits
+// in the upper DPP row of its half (lanes 32h + 16 .. 32h + 31), so the Sinkhorn steps
+// of both rows run in the same instructions. Per value, the operations and their order
+// are coeff_from_sums's, so the results are bit-identical. Returns this lane's value and
+// sets *slot (0..3 pre, 4..7 post, 8..23 comb of the half's row, -1 none).
+__device__ __forceinline__ float coeff_two_rows(const CoeffEpilogue& e, int L, float acc,
+                                                float sc_l, float base_l, int* slot) {
+  const int l = L & 31, hb = L & 32;
+  const float ss = __shfl(acc, hb + kCoefNC, kWave);
+  const float inv = 1.0f / sqrtf(ss / (float)e.K + e.rms_eps);
+  float lp = 0.f;
+  if (l < kCoefNC) lp = (acc * inv) * sc_l + base_l;
+  float out = 0.f;
+  *slot = -1;
+  if (l < kCoefN) {
+    out = 1.0f / (1.0f + expf(-lp)) + e.pre_eps;
+    *slot = l;
+  } else if (l < 2 * kCoefN) {
+    out = e.alpha * (1.0f / (1.0f + expf(-lp)));
+    *slot = l;
+  }
+  const int ce = l - 16;  // comb entry (i, j) = 4i + j at lane 32h + 16 + 4i + j
+  float a = __shfl(lp, hb + 2 * kCoefN + (ce & 15), kWave);
+  float mx = fmaxf(a, dpp_f32<kDppQuadXor1>(a));
+  mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
+  a = expf(a - mx);
+  for (int it = 0; it < e.iters; ++it) {
+    float rs = a + dpp_f32<kDppQuadXor1>(a);
+    rs = rs + dpp_f32<kDppQuadXor2>(rs);
+    a = a * __builtin_amdgcn_rcpf(rs + e.sk_eps);
+    float cs = a + dpp_f32<kDppRowRor4>(a);
+    cs = cs + dpp_f32<kDppRowRor8>(cs);
+    a = a * __builtin_amdgcn_rcpf(cs + e.sk_eps);
+  }
+  if (ce >= 0) {
+    out = a;
+    *slot = 2 * kCoefN + ce;
+  }
+  return out;
+}
+
 struct TileShared {
   uint16_t fnT[kCoefNC][kFnLd];                 // fn^T of the chunk, [logit][k]
   uint4 sT[kN][kTileRows][kTileVecs + 1];       // new streams, bf16, padded rows
   float red[kTileWaves][kTileRows][kCoefNC];    // per-wave partial logits
   float rowsum[kTileRows][2];                   // per-row sum of y^2, of v^2
   unsigned want[kTileRows];
+  float4 cf[kTileRows][kCoefNC / 4];            // a pending call's coefficients (pre|post|comb)
 };
 
-template <bool FINALIZE, bool MXFP8>
+// DEFER: 0 the next coefficients finished in the kernel; 1 left as partial sums (DEFER_OUT);
+// 2 also this call's post, comb and pre finished here from the pending call's partial sums
+// (DEFER_IN) instead of read.
+template <bool FINALIZE, bool MXFP8, int DEFER>
 __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilogue& coef,
-                                          int tile, int c, TileShared& S, float sc_l,
-                                          float base_l) {
+                                          const TileDeferIn* din, int tile, int c,
+                                          TileShared& S, float sc_l, float base_l, float dsc_l,
+                                          float dbase_l) {
+  constexpr bool DEFER_OUT = DEFER >= 1;
+  constexpr bool DEFER_IN = DEFER == 2;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -168,6 +227,18 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   const unsigned epoch_now = __hip_atomic_load(p.epoch + min(row0 + (tid & 15), p.rows - 1),
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
+  // --- DEFER_IN: the pending call's partial sums of this lane's row (the half wave's), value
+  // vl (lanes past 24 repeat value 24), first: their wait then leaves the loads below in flight
+  float4 dpart[kFinishBatch / 4];
+  if constexpr (DEFER_IN) {
+    const CoeffEpilogue& e = din->coef;
+    const float4* src = reinterpret_cast<const float4*>(
+        e.part + ((size_t)rl * kCoefPartW + min(vl, kCoefPartW - 1)) * e.ks_count);
+    const int last = e.ks_count / 4 - 1;  // past it: in-bounds repeats, never added
+#pragma unroll
+    for (int u = 0; u < kFinishBatch / 4; ++u) dpart[u] = src[u < last ? u : last];
+  }
+
   // --- loads: fn slice (mostly L2 hits), the row's mixes, norm weight, streams, sublayer
   uint4 fv[kFnVecs];
 #pragma unroll
@@ -178,11 +249,41 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
     const int h = min(c * kTileH + kk, (p.hv * 8) - 1);  // past the end: zeroed below
     fv[j] = p.fn[((size_t)i * (p.hv * 8) + h) * 3 + part];
   }
-  const float4 pst4 = p.post[rl];
-  float4 cmb4[kN];
+  float4 pst4, cmb4[kN], pr4;
+  if constexpr (!DEFER_IN) {
+    pst4 = p.post[rl];
 #pragma unroll
-  for (int i = 0; i < kN; ++i) cmb4[i] = p.comb[rl * kN + i];
-  const float4 pr4 = p.pre[rl];
+    for (int i = 0; i < kN; ++i) cmb4[i] = p.comb[rl * kN + i];
+    pr4 = p.pre[rl];
+  }
+  // DEFER_IN: the pending call's coefficients of rows 2 wave and 2 wave + 1 (this wave's
+  // halves), from their partial sums added in chunk order; into LDS, from which each half
+  // reads its row's (wave-local: no barrier), and out to the pending call's outputs
+  // (chunk 0). Run while this item's loads are in flight.
+  auto finish_pending = [&]() {
+    const CoeffEpilogue& e = din->coef;
+    const int n4 = e.ks_count / 4;
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < kFinishBatch / 4; ++u)
+      if (u < n4) acc = (((acc + dpart[u].x) + dpart[u].y) + dpart[u].z) + dpart[u].w;
+    int slot;
+    const float val = coeff_two_rows(e, lane, acc, dsc_l, dbase_l, &slot);
+    float* cf = reinterpret_cast<float*>(&S.cf[m][0]);
+    if (slot >= 0) cf[slot] = val;
+    if (c == 0 && row_ok && slot >= 0) {
+      if (slot < kN) const_cast<float*>(&p.pre[r].x)[slot] = val;
+      else if (slot < 2 * kN) const_cast<float*>(&p.post[r].x)[slot - kN] = val;
+      else const_cast<float*>(&p.comb[r * kN].x)[slot - 2 * kN] = val;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    pr4 = S.cf[m][0];
+    pst4 = S.cf[m][1];
+#pragma unroll
+    for (int i = 0; i < kN; ++i) cmb4[i] = S.cf[m][2 + i];
+  };
   int pk[8];
   float wk[8];
   if constexpr (FINALIZE) {
@@ -207,11 +308,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
     // t ascending
     const uint4* src = p.xp + (size_t)rl * p.hv + va;
     const size_t slice = (size_t)p.rows * p.hv;
-    for (int t0 = 0; t0 < p.tp; t0 += 8) {
-      uint4 xv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (t0 + u < p.tp) xv[u] = load_nt(src + (size_t)(t0 + u) * slice);
+    auto add_batch = [&](int t0, const uint4* xv) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (t0 + u < p.tp) {
@@ -221,6 +318,24 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
           for (int e = 0; e < 8; ++e) x[e] += f[e];
         }
       }
+    };
+    int t_first = 0;
+    if constexpr (DEFER_IN) {
+      // the first slices' loads go out before the pending coefficients are finished
+      uint4 xv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u < p.tp) xv[u] = load_nt(src + (size_t)u * slice);
+      finish_pending();
+      add_batch(0, xv);
+      t_first = 8;
+    }
+    for (int t0 = t_first; t0 < p.tp; t0 += 8) {
+      uint4 xv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (t0 + u < p.tp) xv[u] = load_nt(src + (size_t)(t0 + u) * slice);
+      add_batch(t0, xv);
     }
   } else {
     // k ascending, then the shared row
@@ -234,6 +349,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
         if (!ok) wk[u] = 0.f;
       }
     }
+    if constexpr (DEFER_IN) finish_pending();
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (u < p.top_k) {
@@ -360,8 +476,27 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
 
   __syncthreads();  // red complete
   // --- the coefficient partials of this chunk (waves added in order), out before the
-  // handoff wait so that they travel while it runs
-  if (tid < kTileRows * kCoefPartW) {
+  // handoff wait so that they travel while it runs; deferred: as plain floats, in the split
+  // layout of the coefficient epilogue ([row][25][split], split = chunk, splits padded to a
+  // multiple of 4 with zeros that chunk 0 writes), read after this kernel has completed
+  if (DEFER_OUT && tid < kTileRows * kCoefPartW) {
+    const int rr = tid / kCoefPartW, vv = tid % kCoefPartW;
+    if (row0 + rr < p.rows) {
+      float t = 0.f;
+      if (vv < kCoefNC) {
+#pragma unroll
+        for (int w = 0; w < kTileWaves; ++w) t += S.red[w][rr][vv];
+      } else {
+        t = S.rowsum[rr][1];
+      }
+      const int ks = (p.chunks + 3) & ~3;
+      float* dst = p.part_out + ((size_t)(row0 + rr) * kCoefPartW + vv) * ks;
+      dst[c] = t;
+      if (c == 0)
+        for (int z = p.chunks; z < ks; ++z) dst[z] = 0.f;
+    }
+  }
+  if (!DEFER_OUT && tid < kTileRows * kCoefPartW) {
     const int rr = tid / kCoefPartW, vv = tid % kCoefPartW;
     if (row0 + rr < p.rows) {
       float t = 0.f;
@@ -407,7 +542,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   // wave's layer-input stores so that its wait for the words does not wait for them; lane
   // L < 25 adds value L of every chunk in chunk order
   int j = 0;
-  for (int rt = c; rt < kTileRows; rt += p.chunks, ++j) {
+  for (int rt = c; !DEFER_OUT && rt < kTileRows; rt += p.chunks, ++j) {
     if (j % kTileWaves != wave) continue;  // wave-uniform
     const int rc = row0 + rt;
     if (rc >= p.rows) continue;
@@ -477,8 +612,8 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   }
 }
 
-template <bool FINALIZE, bool MXFP8>
-__global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_kernel(const TileParams p) {
+template <bool FINALIZE, bool MXFP8, int DEFER>
+__device__ __forceinline__ void tile_kernel_body(const TileParams& p, const TileDeferIn* din) {
   __shared__ __attribute__((aligned(16))) TileShared S;
   // the coefficient epilogue's arguments (kept out of the kernel argument block, which
   // stays within 256 bytes)
@@ -495,6 +630,8 @@ __global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_kernel(const Ti
   coef.iters = p.iters;
   float sc_l, base_l;
   coeff_lane_scale_base(coef, threadIdx.x & (kWave - 1), &sc_l, &base_l);
+  float dsc_l = 0.f, dbase_l = 0.f;  // the pending call's, by lane of the half wave
+  if constexpr (DEFER == 2) coeff_lane_scale_base(din->coef, threadIdx.x & 31, &dsc_l, &dbase_l);
   const int wg = blockIdx.x;
   const int xcd = wg % kXcd;
   const int local = wg / kXcd;
@@ -504,28 +641,65 @@ __global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_kernel(const Ti
     const int tile = (round * p.tiles_per_round + jt) * kXcd + xcd;
     if (tile * kTileRows >= p.rows) break;  // uniform per workgroup; later rounds go higher
     if (round > 0) __syncthreads();          // LDS reused
-    tile_item<FINALIZE, MXFP8>(p, coef, tile, c, S, sc_l, base_l);
+    tile_item<FINALIZE, MXFP8, DEFER>(p, coef, din, tile, c, S, sc_l, base_l, dsc_l, dbase_l);
   }
 }
 
-template <bool FIN, bool MX>
+// DEFER 0 or 1: the argument block is TileParams alone (256 bytes; a larger one costs
+// launch time). DEFER 2 takes the pending call's arguments as well.
+template <bool FINALIZE, bool MXFP8, int DEFER>
+__global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_kernel(const TileParams p) {
+  tile_kernel_body<FINALIZE, MXFP8, DEFER>(p, nullptr);
+}
+
+template <bool FINALIZE, bool MXFP8>
+__global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_in_kernel(const TileParams p,
+                                                                           const TileDeferIn d) {
+  tile_kernel_body<FINALIZE, MXFP8, 2>(p, &d);
+}
+
+template <bool FIN, bool MX, int DEFER>
 int occupancy_tile() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, boundary_tile_kernel<FIN, MX>,
-                                                   kTileThreads, 0) != hipSuccess)
-    return 0;
-  return n;
+  hipError_t e;
+  if constexpr (DEFER == 2)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, boundary_tile_in_kernel<FIN, MX>,
+                                                     kTileThreads, 0);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, boundary_tile_kernel<FIN, MX, DEFER>,
+                                                     kTileThreads, 0);
+  return e == hipSuccess ? n : 0;
+}
+
+template <bool FIN, bool MX>
+void launch_tile(const TileParams& p, const TileDeferIn* din, int defer, int grid,
+                 hipStream_t stream) {
+  if (defer == 2)
+    hipLaunchKernelGGL((boundary_tile_in_kernel<FIN, MX>), dim3(grid), dim3(kTileThreads), 0,
+                       stream, p, *din);
+  else if (defer == 1)
+    hipLaunchKernelGGL((boundary_tile_kernel<FIN, MX, 1>), dim3(grid), dim3(kTileThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((boundary_tile_kernel<FIN, MX, 0>), dim3(grid), dim3(kTileThreads), 0,
+                       stream, p);
+}
+
+template <int DEFER>
+int occupancy_tile_all() {
+  int n = occupancy_tile<false, false, DEFER>();
+  n = min(n, occupancy_tile<false, true, DEFER>());
+  n = min(n, occupancy_tile<true, false, DEFER>());
+  return min(n, occupancy_tile<true, true, DEFER>());
 }
 
 }  // namespace
 
 int boundary_tile_resident_wgs_per_cu() {
-  int n = occupancy_tile<false, false>();
-  n = min(n, occupancy_tile<false, true>());
-  n = min(n, occupancy_tile<true, false>());
-  n = min(n, occupancy_tile<true, true>());
-  return n;
+  return min(occupancy_tile_all<0>(), min(occupancy_tile_all<1>(), occupancy_tile_all<2>()));
 }
+
+int boundary_tile_part_ks(int hidden) { return (boundary_tile_chunks(hidden) + 3) & ~3; }
 
 int boundary_tile_chunks(int hidden) { return (hidden + kTileH - 1) / kTileH; }
 
@@ -571,7 +745,11 @@ hipError_t launch_boundary_tile(const TileLaunch& T, hipStream_t stream) {
   p.sk_eps = T.coef.sk_eps;
   p.alpha = T.coef.alpha;
   p.iters = T.coef.iters;
-  p.next_pre = T.next_pre;
+  const bool defer_out = T.part_out != nullptr;
+  if (defer_out)
+    p.part_out = T.part_out;
+  else
+    p.next_pre = T.next_pre;
   p.next_post = T.next_post;
   p.next_comb = T.next_comb;
   p.words = T.words;
@@ -594,13 +772,16 @@ hipError_t launch_boundary_tile(const TileLaunch& T, hipStream_t stream) {
   const int grid = kXcd * tpr * p.chunks;
   const bool fin = L.gemm2_permuted != nullptr;
   const bool mx = L.mx_data_out != nullptr;
-  if (fin) {
-    if (mx) hipLaunchKernelGGL((boundary_tile_kernel<true, true>), dim3(grid), dim3(kTileThreads), 0, stream, p);
-    else hipLaunchKernelGGL((boundary_tile_kernel<true, false>), dim3(grid), dim3(kTileThreads), 0, stream, p);
-  } else {
-    if (mx) hipLaunchKernelGGL((boundary_tile_kernel<false, true>), dim3(grid), dim3(kTileThreads), 0, stream, p);
-    else hipLaunchKernelGGL((boundary_tile_kernel<false, false>), dim3(grid), dim3(kTileThreads), 0, stream, p);
-  }
+  TileDeferIn din;
+  din.coef = T.in_coef;
+  const int defer = T.defer_in ? 2 : (defer_out ? 1 : 0);
+  if (T.defer_in && (!defer_out || T.in_coef.ks_count < 4 || T.in_coef.ks_count > kFinishBatch ||
+                     T.in_coef.ks_count % 4 != 0))
+    return hipErrorInvalidConfiguration;
+  if (fin) mx ? launch_tile<true, true>(p, &din, defer, grid, stream)
+              : launch_tile<true, false>(p, &din, defer, grid, stream);
+  else mx ? launch_tile<false, true>(p, &din, defer, grid, stream)
+          : launch_tile<false, false>(p, &din, defer, grid, stream);
   return hipGetLastError();
 }
 

@@ -69,6 +69,8 @@ struct PreLaunch {
   float* post_out;
   float* comb_out;
   float* part;                  // pre_scratch_floats(max_rows, hidden) floats
+  int ks_count;                 // splits of `part`: 0 for the split-K plan's, else a multiple
+                                // of 4 (partials written by the fused boundary)
 };
 
 // The boundary fused with the next coefficient call (boundary_tile.hip): the boundary's
@@ -80,6 +82,12 @@ struct TileLaunch {
   float* next_pre;
   float* next_post;
   float* next_comb;
+  float* part_out;              // non-NULL: write the next coefficients' partials here
+                                // ([rows][25][boundary_tile_part_ks(hidden)]) and finish none
+  bool defer_in;                // b.post, b.comb and b.pre are a pending call's outputs: finish
+                                // them from in_coef.part (another fused kernel's part_out;
+                                // requires part_out) and write them, instead of reading them
+  CoeffEpilogue in_coef;
   unsigned long long* words;    // boundary_tile_words(tile_rows, hidden) tagged partials
   int tile_rows;                // rows the words cover (the handle's), >= the call's rows
   int wgs_per_xcd;              // resident workgroups of the tile kernel on one XCD
@@ -87,6 +95,7 @@ struct TileLaunch {
 int boundary_tile_resident_wgs_per_cu();
 int boundary_tile_chunks(int hidden);
 size_t boundary_tile_words(int rows, int hidden);
+int boundary_tile_part_ks(int hidden);
 bool boundary_tile_fits(int hidden, int wgs_per_xcd);
 hipError_t launch_boundary_tile(const TileLaunch& T, hipStream_t stream);
 

@@ -192,7 +192,7 @@ CoeffEpilogue pre_epilogue_args(const PreLaunch& L) {
   e.part = L.part;
   e.scale = L.scale;
   e.base = L.base;
-  e.ks_count = ks;
+  e.ks_count = L.ks_count > 0 ? L.ks_count : ks;
   e.K = kN * L.hidden;
   e.rms_eps = L.rms_eps;
   e.pre_eps = L.pre_eps;

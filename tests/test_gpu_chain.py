@@ -224,3 +224,44 @@ def test_fused_chain_61_layers_sampled_steps():
     n = len(step.subs)
     _teacher_forced_checks(step, {0, 1, 2, n // 2 - 1, n // 2, n - 2, n - 1})
     assert step.h.errors() == 0
+
+
+def test_fused_deferred_chain_equals_fused_chain():
+    """Fused calls that also defer their coefficients (each finished by the next fused call's
+    kernel, the last by the residual-only boundary): the step's mean, streams and final
+    coefficients equal the fused step's bit for bit, eager and under graph replay, at 3 and
+    at 61 layers."""
+    for layers in (3, 61):
+        say(f"case: chained step, {layers} layers: fused + deferred vs fused")
+        fused = chain.DecodeChain.from_synth(DEV, layers=layers, fused=True)
+        want = N(fused.run())
+        torch.cuda.synchronize()
+        want_streams = N(fused.streams)
+        want_coeffs = [N(fused.pre), N(fused.post), N(fused.comb)]
+        both = chain.DecodeChain(fused.h, fused.emb, fused.subs, fused.p, DEV, fused=True,
+                                 deferred=True)
+        got = N(both.run())
+        torch.cuda.synchronize()
+        assert np.array_equal(got, want), f"{layers} layers: mean differs"
+        assert np.array_equal(N(both.streams), want_streams), f"{layers} layers: streams differ"
+        for a, b in zip((both.pre, both.post, both.comb), want_coeffs):
+            assert np.array_equal(N(a), b), f"{layers} layers: coefficients differ"
+        if layers == 3:
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                both.run()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                out = both.run()
+            for rep in range(2):
+                out.zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                assert np.array_equal(N(out), want), f"replay {rep}"
+                fused.run()
+                torch.cuda.synchronize()
+        assert fused.h.errors() == 0
+        del fused, both

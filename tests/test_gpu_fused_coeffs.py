@@ -250,8 +250,10 @@ def test_fused_argument_checks():
     li = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
     outs = [torch.empty((R, 4), device="cuda"), torch.empty((R, 4), device="cuda"),
             torch.empty((R, 4, 4), device="cuda")]
-    a = binding.CoeffArgs(p(nxt["fn"]), p(nxt["scale"]), p(nxt["base"]), 1e-6, 1e-6, 1e-6, 2.0,
-                          20, p(outs[0]), p(outs[1]), p(outs[2]))
+    a = binding.CoeffArgs(fn=p(nxt["fn"]), scale=p(nxt["scale"]), base=p(nxt["base"]),
+                          rms_eps=1e-6, pre_eps=1e-6, sinkhorn_eps=1e-6, post_alpha=2.0,
+                          sinkhorn_iters=20, deferred=0, pre_out=p(outs[0]),
+                          post_out=p(outs[1]), comb_out=p(outs[2]))
 
     def call(args, pre=dv["pre"], rows=R):
         return lib.mhc_boundary_coeffs(h.ptr, p(dv["x_partials"]), 2, p(dv["residual"]),
@@ -269,6 +271,9 @@ def test_fused_argument_checks():
     assert call(ctypes.byref(bad)) == 2
     bad = binding.CoeffArgs.from_buffer_copy(a)
     bad.comb_out = None
+    assert call(ctypes.byref(bad)) == 1
+    bad = binding.CoeffArgs.from_buffer_copy(a)
+    bad.deferred = 2                                  # only 0 and 1
     assert call(ctypes.byref(bad)) == 1
     assert call(ctypes.byref(a), rows=R + 1) == 4
     assert lib.mhc_finalize_coeffs(h.ptr, None, 1, None, None, None, p(dv["residual"]),
