@@ -219,26 +219,26 @@ def main():
         log(f"  inputs ready in {time.time() - t0:.1f} s ({step.input_bytes() / 1e9:.2f} GB)")
         k = max(3, args.steps // 40)
         out = {}
-        s4 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, fused=True)
-        e4, g4 = time_calls(torch, [s4.run], k, 2)
-        out["chain_decode_step"] = {
-            "us_per_step": round(g4, 1), "us_per_step_eager": None if e4 is None else round(e4, 1),
-            "algorithmic_bytes": int(s4.algorithmic_bytes()),
-            "gb_per_s": round(s4.algorithmic_bytes() / g4 / 1e3, 1),
-            "note": "each boundary and the coefficient call after it in one kernel "
-                    "(mhc_boundary_coeffs / mhc_finalize_coeffs)"}
-        log(f"  chain (fused) {out['chain_decode_step']}")
-        del s4
         s5 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, fused=True,
                                    deferred=True)
         e5, g5 = time_calls(torch, [s5.run], k, 2)
-        out["chain_decode_step_fused_deferred"] = {
+        out["chain_decode_step"] = {
             "us_per_step": round(g5, 1), "us_per_step_eager": None if e5 is None else round(e5, 1),
+            "algorithmic_bytes": int(s5.algorithmic_bytes()),
             "gb_per_s": round(s5.algorithmic_bytes() / g5 / 1e3, 1),
-            "note": "fused calls that leave the next coefficients as partial sums, finished "
-                    "by the next fused call's kernel (mhc_coeff_args.deferred)"}
-        log(f"  chain (fused, deferred) {out['chain_decode_step_fused_deferred']}")
+            "note": "each boundary and the coefficient call after it in one kernel, which "
+                    "leaves the coefficients as partial sums for the next one to finish "
+                    "(mhc_boundary_coeffs / mhc_finalize_coeffs, deferred)"}
+        log(f"  chain (fused, deferred) {out['chain_decode_step']}")
         del s5
+        s4 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, fused=True)
+        e4, g4 = time_calls(torch, [s4.run], k, 2)
+        out["chain_decode_step_fused"] = {
+            "us_per_step": round(g4, 1), "us_per_step_eager": None if e4 is None else round(e4, 1),
+            "gb_per_s": round(s4.algorithmic_bytes() / g4 / 1e3, 1),
+            "note": "fused calls that finish the next coefficients themselves"}
+        log(f"  chain (fused) {out['chain_decode_step_fused']}")
+        del s4
         us_e, us_g = time_calls(torch, [step.run], k, 2)
         out["chain_decode_step_unfused"] = {
             "us_per_step": round(us_g, 1),
@@ -348,6 +348,35 @@ def main():
             out[name2] = row_entry(name2, nb + extra + Rc * 4 * H * 2, e, g, ns)
             out[name2]["note"] = "the same work as two calls (boundary, then mhc_pre_coeffs)"
             log(f"  {name2} {out[name2]}")
+
+            # deferred and chained: call i takes call i-1's coefficients (finishing them in
+            # its kernel) and leaves its own as partial sums
+            for b in bufs:
+                for t, src_t in zip(b["nx"], (co["pre"], co["post"], co["comb"])):
+                    t.copy_(src_t)
+
+            def chained(i):
+                b, (pp, qq, cc) = bufs[i], bufs[i - 1]["nx"]
+                kw = dict(mxfp8=mx, residual_out=b["s"], layer_input_out=b["li"],
+                          mx_out=b["mx"], next_out=b["nx"], deferred=True)
+                if kind == "boundary":
+                    return binding.boundary_coeffs(h, b["x_partials"], b["s"], qq, cc, pp,
+                                                   co["norm_weight"], d["eps"], nxt, **kw)
+                return binding.finalize_coeffs(h, b["gemm2_permuted"], small["expert_weights"],
+                                               small["expanded_idx_to_permuted_idx"],
+                                               b["shared_output"], b["s"], qq, cc, pp,
+                                               co["norm_weight"], d["eps"], nxt, **kw)
+
+            e, g = time_calls(torch, [(lambda i=i: chained(i)) for i in range(ns)],
+                              args.steps, args.warmup)
+            binding.pre_coeffs_flush(h)  # the last call's coefficients, before the buffers go
+            torch.cuda.synchronize()
+            name3 = f"{kind}_coeffs_deferred_r128" + ("_mxfp8" if mx else "")
+            out[name3] = row_entry(name3, nb + extra, e, g, ns)
+            out[name3]["note"] = ("as " + name + ", chained: each call finishes the previous "
+                                  "call's coefficients in its kernel and leaves its own as "
+                                  "partial sums (mhc_coeff_args.deferred)")
+            log(f"  {name3} {out[name3]}")
             del bufs
         return out
 

@@ -258,8 +258,9 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   }
   // DEFER_IN: the pending call's coefficients of rows 2 wave and 2 wave + 1 (this wave's
   // halves), from their partial sums added in chunk order; into LDS, from which each half
-  // reads its row's (wave-local: no barrier), and out to the pending call's outputs
-  // (chunk 0). Run while this item's loads are in flight.
+  // reads its row's (wave-local: no barrier). Run while this item's loads are in flight.
+  // Chunk 0 writes them to the pending call's outputs at the end of the item (a store
+  // here would hold up every later wait for loads).
   auto finish_pending = [&]() {
     const CoeffEpilogue& e = din->coef;
     const int n4 = e.ks_count / 4;
@@ -271,11 +272,6 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
     const float val = coeff_two_rows(e, lane, acc, dsc_l, dbase_l, &slot);
     float* cf = reinterpret_cast<float*>(&S.cf[m][0]);
     if (slot >= 0) cf[slot] = val;
-    if (c == 0 && row_ok && slot >= 0) {
-      if (slot < kN) const_cast<float*>(&p.pre[r].x)[slot] = val;
-      else if (slot < 2 * kN) const_cast<float*>(&p.post[r].x)[slot - kN] = val;
-      else const_cast<float*>(&p.comb[r * kN].x)[slot - 2 * kN] = val;
-    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -608,6 +604,16 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
         p.mx_data[(size_t)r * p.hv + v] = make_uint2(lo, hi);
         if ((v & 3) == 0) p.mx_scale[(size_t)r * ((p.hv * 8) / 32) + (v >> 2)] = (uint8_t)(ex + 127);
       }
+    }
+  }
+
+  // --- DEFER_IN: the pending call's outputs of this row (lane vl: slot vl), from LDS
+  if constexpr (DEFER_IN) {
+    if (c == 0 && row_ok && vl < kCoefNC) {
+      const float val = reinterpret_cast<const float*>(&S.cf[m][0])[vl];
+      if (vl < kN) const_cast<float*>(&p.pre[r].x)[vl] = val;
+      else if (vl < 2 * kN) const_cast<float*>(&p.post[r].x)[vl - kN] = val;
+      else const_cast<float*>(&p.comb[r * kN].x)[vl - 2 * kN] = val;
     }
   }
 }
