@@ -618,8 +618,16 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   }
 }
 
-template <bool FINALIZE, bool MXFP8, int DEFER>
-__device__ __forceinline__ void tile_kernel_body(const TileParams& p, const TileDeferIn* din) {
+// DEFER 0 or 1: the argument block is TileParams alone (256 bytes; a larger one costs
+// launch time). DEFER 2 takes the pending call's arguments as well (Extra = TileDeferIn).
+// One kernel template holds the body: with the body in a device function that two kernels
+// call, the compiler's allocation of the DEFER 0 kernels took 40 to 50 more scalar spills.
+template <bool FINALIZE, bool MXFP8, int DEFER, typename... Extra>
+__global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_kernel(const TileParams p,
+                                                                        const Extra... d) {
+  const TileDeferIn* din = nullptr;
+  if constexpr (sizeof...(Extra) > 0) ((din = &d), ...);
+
   __shared__ __attribute__((aligned(16))) TileShared S;
   // the coefficient epilogue's arguments (kept out of the kernel argument block, which
   // stays within 256 bytes)
@@ -651,26 +659,13 @@ __device__ __forceinline__ void tile_kernel_body(const TileParams& p, const Tile
   }
 }
 
-// DEFER 0 or 1: the argument block is TileParams alone (256 bytes; a larger one costs
-// launch time). DEFER 2 takes the pending call's arguments as well.
-template <bool FINALIZE, bool MXFP8, int DEFER>
-__global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_kernel(const TileParams p) {
-  tile_kernel_body<FINALIZE, MXFP8, DEFER>(p, nullptr);
-}
-
-template <bool FINALIZE, bool MXFP8>
-__global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_in_kernel(const TileParams p,
-                                                                           const TileDeferIn d) {
-  tile_kernel_body<FINALIZE, MXFP8, 2>(p, &d);
-}
-
 template <bool FIN, bool MX, int DEFER>
 int occupancy_tile() {
   int n = 0;
   hipError_t e;
   if constexpr (DEFER == 2)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, boundary_tile_in_kernel<FIN, MX>,
-                                                     kTileThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &n, boundary_tile_kernel<FIN, MX, 2, TileDeferIn>, kTileThreads, 0);
   else
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, boundary_tile_kernel<FIN, MX, DEFER>,
                                                      kTileThreads, 0);
@@ -681,8 +676,8 @@ template <bool FIN, bool MX>
 void launch_tile(const TileParams& p, const TileDeferIn* din, int defer, int grid,
                  hipStream_t stream) {
   if (defer == 2)
-    hipLaunchKernelGGL((boundary_tile_in_kernel<FIN, MX>), dim3(grid), dim3(kTileThreads), 0,
-                       stream, p, *din);
+    hipLaunchKernelGGL((boundary_tile_kernel<FIN, MX, 2, TileDeferIn>), dim3(grid),
+                       dim3(kTileThreads), 0, stream, p, *din);
   else if (defer == 1)
     hipLaunchKernelGGL((boundary_tile_kernel<FIN, MX, 1>), dim3(grid), dim3(kTileThreads), 0,
                        stream, p);
