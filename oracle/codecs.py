@@ -123,3 +123,27 @@ def mxfp8_quantize(layer_input_bits, block=32):
     scaled = xb * np.ldexp(1.0, -e)[:, :, None]
     codes = e4m3_encode(scaled).reshape(rows, hidden)
     return codes, (e + 127).astype(np.uint8)
+
+
+def mxfp8_scales_swizzled_128x4(scales, fill=0):
+    """Row-major E8M0 scales [rows, blocks] -> the swizzled 128x4 byte vector.
+
+    The boundary page gives its MXFP8 layer input FlashInfer's swizzled 128x4
+    scale layout (section ``empty_quantized_layer_input``) without spelling it
+    out; this is that layout as the block-scaled GEMM interfaces publish it.
+    Rows are padded to a multiple of 128 and blocks to a multiple of 4 (the
+    padding holds ``fill``). The padded matrix is cut into 128 x 4 tiles stored
+    one after another in row-major tile order, 512 bytes each. Inside a tile,
+    row t = 32 * a + b (a in 0..3, b in 0..31) and block c (0..3) sit at byte
+    16 * b + 4 * a + c: the 32 row groups of 16 bytes each hold rows b, b+32,
+    b+64, b+96, four blocks per row.
+    """
+    s = np.asarray(scales, dtype=np.uint8)
+    rows, blocks = s.shape
+    rp = -(-rows // 128) * 128
+    bp = -(-blocks // 4) * 4
+    padded = np.full((rp, bp), fill, dtype=np.uint8)
+    padded[:rows, :blocks] = s
+    # axes: (row tile, a, b, block tile, c) -> (row tile, block tile, b, a, c)
+    t = padded.reshape(rp // 128, 4, 32, bp // 4, 4)
+    return np.ascontiguousarray(t.transpose(0, 3, 2, 1, 4)).reshape(-1)

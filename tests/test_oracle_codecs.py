@@ -161,3 +161,59 @@ def test_mxfp8_zero_block_and_layout():
     assert list(scales[0]) == [0, 0] and scales[1, 0] == 0
     assert scales[1, 1] == 127 - 7  # 3.0 <= 448 * 2**-7 = 3.5
     assert np.all(codes[1, 32:] == codecs.e4m3_encode(np.array([3.0 * 2 ** 7]))[0])
+
+
+# ---------------------------------------------------------------------------
+# the swizzled 128x4 scale layout
+# ---------------------------------------------------------------------------
+
+def _swizzle_ids(rows, blocks):
+    """Swizzle the element ids r * blocks + b (as two byte planes) and decode them back;
+    padding (fill 255 in the high plane) decodes to -1."""
+    ids = np.arange(rows * blocks, dtype=np.int64).reshape(rows, blocks)
+    assert rows * blocks < 255 * 256
+    lo = codecs.mxfp8_scales_swizzled_128x4((ids & 0xFF).astype(np.uint8), fill=0)
+    hi = codecs.mxfp8_scales_swizzled_128x4((ids >> 8).astype(np.uint8), fill=255)
+    out = lo.astype(np.int64) | (hi.astype(np.int64) << 8)
+    return np.where(hi == 255, -1, out)
+
+
+def test_scale_swizzle_golden_offsets(golden_dir):
+    g = _load(golden_dir, "scale_swizzle_128x4.json")
+    got = _swizzle_ids(g["rows"], g["blocks"])
+    assert got.size == g["total_bytes"]
+    for p in g["points"]:
+        assert got[p["offset"]] == p["row"] * g["blocks"] + p["block"], p
+    for p in g["padding"]:
+        assert got[p["offset"]] == -1, p
+
+
+@pytest.mark.parametrize("rows,blocks", [(1, 1), (128, 4), (130, 6), (64, 33), (300, 201)])
+def test_scale_swizzle_is_a_padded_permutation(rows, blocks):
+    got = _swizzle_ids(rows, blocks)
+    rp, bp = -(-rows // 128) * 128, -(-blocks // 4) * 4
+    assert got.size == rp * bp
+    real = got[got >= 0]
+    assert np.array_equal(np.sort(real), np.arange(rows * blocks))  # each scale exactly once
+    assert np.count_nonzero(got < 0) == rp * bp - rows * blocks
+
+
+@pytest.mark.parametrize("rows,blocks", [(130, 6), (300, 201)])
+def test_scale_swizzle_tiles_and_row_groups(rows, blocks):
+    """Tile i (512 bytes, row-major over the padded tile grid) holds exactly its 128 x 4
+    block; its 16-byte group b holds rows b, b+32, b+64, b+96, four consecutive blocks
+    each."""
+    got = _swizzle_ids(rows, blocks)
+    bp = -(-blocks // 4) * 4
+    kt = bp // 4
+    for tile in range(got.size // 512):
+        tr, tk = divmod(tile, kt)
+        t = got[tile * 512:(tile + 1) * 512]
+        for b in range(32):
+            grp = t[16 * b:16 * b + 16]
+            for a in range(4):
+                r = 128 * tr + 32 * a + b
+                for c in range(4):
+                    k = 4 * tk + c
+                    want = r * blocks + k if (r < rows and k < blocks) else -1
+                    assert grp[4 * a + c] == want, (tile, b, a, c)
