@@ -87,9 +87,10 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
                mhc_handle* out);
 
 /*
- * mhc_set_option -- knobs of a handle. Results do not depend on them (except
- * that a spin limit too small to cover the row handoff makes it give up, see
- * above). Takes effect for calls issued afterwards.
+ * mhc_set_option -- knobs of a handle. Results do not depend on the first two
+ * (except that a spin limit too small to cover the row handoff makes it give up,
+ * see above); the third chooses where the MXFP8 scale bytes go. Takes effect for
+ * calls issued afterwards.
  *   MHC_OPT_BOUNDARY_BLOCK: threads per workgroup of the boundary kernels that write a
  *     layer input, 128, 256 or 512, for every call and row count (default: chosen
  *     per call from the row count, see mhc_create). Each thread owns 8 hidden
@@ -100,10 +101,37 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
  *     Other values: MHC_ERR_SHAPE.
  *   MHC_OPT_SPIN_LIMIT: polls (each followed by a short sleep) before a row-handoff
  *     wait gives up; >= 0, default 2^20. Negative: MHC_ERR_SHAPE.
+ *   MHC_OPT_SCALE_LAYOUT: the layout of mx_scale_out in every call that writes an
+ *     MXFP8 layer input (mhc_boundary, mhc_finalize, mhc_first, mhc_collapse_norm,
+ *     mhc_boundary_coeffs, mhc_finalize_coeffs); the E4M3 data stays [R, H]:
+ *       MHC_SCALE_ROW_MAJOR (default): [R, H/32], byte (r, b) at r * (H/32) + b.
+ *       MHC_SCALE_SWIZZLED_128X4: the swizzled 128x4 layout the boundary page gives its
+ *         MXFP8 layer input (empty_quantized_layer_input: FlashInfer's layout, the
+ *         block-scale operand layout of block-scaled GEMMs). Rows are padded to a
+ *         multiple of 128 and the H/32 blocks to a multiple of 4; with KT = padded
+ *         blocks / 4, byte (r, b) is at
+ *           ((r / 128) * KT + b / 4) * 512 + (r % 32) * 16 + ((r / 32) % 4) * 4 + b % 4,
+ *         i.e. one 512-byte tile per 128 rows x 4 blocks, tiles row-major. The buffer
+ *         holds mhc_mxfp8_scale_bytes(R, H, MHC_SCALE_SWIZZLED_128X4) bytes; the
+ *         padding bytes (rows >= R, blocks >= H/32) are not written.
+ *     Other values: MHC_ERR_SHAPE.
  * Unknown options: MHC_ERR_INVALID_ARG.
  */
-enum mhc_option { MHC_OPT_BOUNDARY_BLOCK = 1, MHC_OPT_SPIN_LIMIT = 2 };
+enum mhc_option { MHC_OPT_BOUNDARY_BLOCK = 1, MHC_OPT_SPIN_LIMIT = 2, MHC_OPT_SCALE_LAYOUT = 3 };
+enum mhc_scale_layout { MHC_SCALE_ROW_MAJOR = 0, MHC_SCALE_SWIZZLED_128X4 = 1 };
 int mhc_set_option(mhc_handle h, int option, int value);
+
+/*
+ * mhc_mxfp8_scale_bytes -- the size in bytes of mx_scale_out for `rows` rows of `hidden`
+ * elements in a scale layout (see MHC_OPT_SCALE_LAYOUT): rows * hidden/32 row-major,
+ * roundup(rows, 128) * roundup(hidden/32, 4) swizzled. Host only (no device work).
+ * boundary page, empty_quantized_layer_input: the scale buffer of an MXFP8 layer input
+ * is sized from the token count and hidden size.
+ *   rows >= 0, hidden > 0 and a multiple of 32  else MHC_ERR_SHAPE
+ *   layout a mhc_scale_layout                   else MHC_ERR_SHAPE
+ *   bytes  a host pointer                       else MHC_ERR_INVALID_ARG
+ */
+int mhc_mxfp8_scale_bytes(int rows, int hidden, int layout, uint64_t* bytes);
 
 /*
  * mhc_get_errors -- the number of row-handoff waits that gave up since the
@@ -150,8 +178,9 @@ int mhc_reset(mhc_handle h, mhc_stream_t stream);
  *   norm_weight     [H] bf16;  norm_eps >= 0
  *   residual_out    [R, n, H] bf16, may equal residual
  *   layer_input_out [R, H] bf16
- *   mx_data_out     [R, H] E4M3 bytes and mx_scale_out [R, H/32] E8M0 bytes, both
- *                   NULL (no MXFP8) or both set (needs pre and H % 32 == 0)
+ *   mx_data_out     [R, H] E4M3 bytes and mx_scale_out [R, H/32] E8M0 bytes (or the
+ *                   swizzled layout, see MHC_OPT_SCALE_LAYOUT), both NULL (no MXFP8)
+ *                   or both set (needs pre and H % 32 == 0)
  */
 int mhc_boundary(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_t* residual,
                  const float* post, const float* comb, const float* pre,

@@ -22,6 +22,9 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "mhc.h")
 MHC_OK = 0
 MHC_OPT_BOUNDARY_BLOCK = 1
 MHC_OPT_SPIN_LIMIT = 2
+MHC_OPT_SCALE_LAYOUT = 3
+MHC_SCALE_ROW_MAJOR = 0
+MHC_SCALE_SWIZZLED_128X4 = 1
 _VALUE_ERRORS = {1, 2, 3, 4, 5}
 
 _lib = None
@@ -41,6 +44,7 @@ _SIGS = {
     "mhc_status_string": ([_i], ctypes.c_char_p),
     "mhc_create": ([_i, _i, _i, _i, _i, _i, ctypes.POINTER(_vp)], _i),
     "mhc_set_option": ([_vp, _i, _i], _i),
+    "mhc_mxfp8_scale_bytes": ([_i, _i, _i, ctypes.POINTER(ctypes.c_uint64)], _i),
     "mhc_get_errors": ([_vp, ctypes.POINTER(ctypes.c_uint), _i, _vp], _i),
     "mhc_destroy": ([_vp], _i),
     "mhc_reset": ([_vp, _vp], _i),
@@ -132,6 +136,7 @@ class Handle:
         dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
         self.hidden, self.hc_mult, self.max_rows = hidden, hc_mult, max_rows
         self.max_tp, self.top_k, self.device = max_tp, top_k, dev
+        self.scale_layout = MHC_SCALE_ROW_MAJOR
         h = _vp()
         with torch.cuda.device(dev):
             _check(lib.mhc_create(hidden, hc_mult, max_rows, max_tp, top_k, dev.index,
@@ -146,6 +151,8 @@ class Handle:
 
     def set_option(self, option, value):
         _check(load_library().mhc_set_option(self.ptr, option, value), "mhc_set_option")
+        if option == MHC_OPT_SCALE_LAYOUT:
+            self.scale_layout = value
 
     def errors(self, clear=False, stream=None):
         """Row-handoff waits that gave up (``mhc_get_errors``); waits for the stream."""
@@ -175,6 +182,31 @@ class Handle:
         self.close()
 
 
+def mxfp8_scale_bytes(rows, hidden, layout=MHC_SCALE_ROW_MAJOR):
+    """``mhc_mxfp8_scale_bytes``: bytes of an MXFP8 scale buffer in a scale layout."""
+    n = ctypes.c_uint64(0)
+    _check(load_library().mhc_mxfp8_scale_bytes(rows, hidden, layout, ctypes.byref(n)),
+           "mhc_mxfp8_scale_bytes")
+    return n.value
+
+
+def _mx_outputs(h, rows, hidden, dev, mx_out):
+    """The E4M3 data [rows, hidden] and the scale bytes: [rows, hidden // 32] row-major, or
+    the swizzled 128x4 layout's padded byte vector (allocated zeroed, so that the padding
+    the kernels leave alone reads as zero)."""
+    swizzled = getattr(h, "scale_layout", MHC_SCALE_ROW_MAJOR) == MHC_SCALE_SWIZZLED_128X4
+    scale_shape = ((mxfp8_scale_bytes(rows, hidden, MHC_SCALE_SWIZZLED_128X4),) if swizzled
+                   else (rows, hidden // 32))
+    if mx_out is None:
+        alloc = torch.zeros if swizzled else torch.empty
+        mx_out = (torch.empty((rows, hidden), dtype=torch.uint8, device=dev),
+                  alloc(scale_shape, dtype=torch.uint8, device=dev))
+    mx_data, mx_scale = mx_out
+    _need(mx_data, "mx_data_out", torch.uint8, (rows, hidden), dev)
+    _need(mx_scale, "mx_scale_out", torch.uint8, scale_shape, dev)
+    return mx_data, mx_scale
+
+
 def _mix_outputs(h, residual, pre, norm_weight, mxfp8, residual_out, layer_input_out, mx_out):
     rows, n, hidden = residual.shape
     dev = residual.device
@@ -192,12 +224,7 @@ def _mix_outputs(h, residual, pre, norm_weight, mxfp8, residual_out, layer_input
     _need(layer_input_out, "layer_input_out", torch.bfloat16, (rows, hidden), dev)
     mx_data = mx_scale = None
     if mxfp8:
-        if mx_out is None:
-            mx_out = (torch.empty((rows, hidden), dtype=torch.uint8, device=dev),
-                      torch.empty((rows, hidden // 32), dtype=torch.uint8, device=dev))
-        mx_data, mx_scale = mx_out
-        _need(mx_data, "mx_data_out", torch.uint8, (rows, hidden), dev)
-        _need(mx_scale, "mx_scale_out", torch.uint8, (rows, hidden // 32), dev)
+        mx_data, mx_scale = _mx_outputs(h, rows, hidden, dev, mx_out)
     return residual_out, layer_input_out, mx_data, mx_scale
 
 
@@ -301,12 +328,7 @@ def _layer_outputs(h, rows, dev, mxfp8, layer_input_out, mx_out):
     _need(layer_input_out, "layer_input_out", torch.bfloat16, (rows, hidden), dev)
     mx_data = mx_scale = None
     if mxfp8:
-        if mx_out is None:
-            mx_out = (torch.empty((rows, hidden), dtype=torch.uint8, device=dev),
-                      torch.empty((rows, hidden // 32), dtype=torch.uint8, device=dev))
-        mx_data, mx_scale = mx_out
-        _need(mx_data, "mx_data_out", torch.uint8, (rows, hidden), dev)
-        _need(mx_scale, "mx_scale_out", torch.uint8, (rows, hidden // 32), dev)
+        mx_data, mx_scale = _mx_outputs(h, rows, hidden, dev, mx_out)
     elif mx_out is not None:
         raise ValueError("mx_out given without mxfp8=True")
     return layer_input_out, mx_data, mx_scale

@@ -33,6 +33,7 @@ struct mhc_ctx {
   int block_many;          // ... for more rows (auto)
   int block_set;           // the size MHC_OPT_BOUNDARY_BLOCK set, 0: automatic
   int spin_limit;          // polls before a handoff wait gives up
+  int scale_layout;        // MHC_SCALE_ROW_MAJOR or MHC_SCALE_SWIZZLED_128X4
   int wgs_per_xcd[3];      // resident layer-input workgroups per XCD at block 128 / 256 / 512
   int tile_wgs_per_xcd;    // resident workgroups of the fused boundary + coefficient kernel
   int tile_rows;           // rows the fused kernel's scratch covers (0: not available)
@@ -117,6 +118,7 @@ void fill_mix(const mhc_ctx* h, mhc::BoundaryLaunch& L, const uint16_t* residual
   L.layer_input_out = layer_input_out;
   L.mx_data_out = mx_data_out;
   L.mx_scale_out = mx_scale_out;
+  L.scale_kt = h->scale_layout == MHC_SCALE_SWIZZLED_128X4 ? (h->hidden / 32 + 3) / 4 : 0;
   L.slots = h->slots;
   L.epoch = h->epoch;
   L.errors = h->errors;
@@ -212,6 +214,7 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   h->device = device;
   h->block = kDefaultBlock;
   h->spin_limit = kDefaultSpinLimit;
+  h->scale_layout = MHC_SCALE_ROW_MAJOR;
   h->pending = false;
   h->slot_stride = mhc::boundary_chunks(hidden, kMinBlock, true);  // the most chunks per row
   int cus = 0;
@@ -305,8 +308,28 @@ int mhc_set_option(mhc_handle h, int option, int value) {
       if (value < 0) return MHC_ERR_SHAPE;
       h->spin_limit = value;
       return MHC_OK;
+    case MHC_OPT_SCALE_LAYOUT:
+      if (value != MHC_SCALE_ROW_MAJOR && value != MHC_SCALE_SWIZZLED_128X4) return MHC_ERR_SHAPE;
+      h->scale_layout = value;
+      return MHC_OK;
     default:
       return MHC_ERR_INVALID_ARG;
+  }
+}
+
+int mhc_mxfp8_scale_bytes(int rows, int hidden, int layout, uint64_t* bytes) {
+  if (!bytes) return MHC_ERR_INVALID_ARG;
+  if (rows < 0 || hidden <= 0 || hidden % 32 != 0) return MHC_ERR_SHAPE;
+  const uint64_t blocks = (uint64_t)(hidden / 32);
+  switch (layout) {
+    case MHC_SCALE_ROW_MAJOR:
+      *bytes = (uint64_t)rows * blocks;
+      return MHC_OK;
+    case MHC_SCALE_SWIZZLED_128X4:
+      *bytes = round_up((uint64_t)rows, 128) * round_up(blocks, 4);
+      return MHC_OK;
+    default:
+      return MHC_ERR_SHAPE;
   }
 }
 

@@ -61,6 +61,7 @@ struct BoundaryParams {
   // sublayer output: TP partials ...
   const uint4* xp;          // [tp][rows][hv]
   int tp;
+  int scale_kt;             // MXFP8 scale layout (mx_scale_offset): 0 row-major, else 128x4 tiles
   // ... or an unfinalized MoE output
   const uint4* g;           // [num_permuted][hv]
   const float* ew;          // [rows][top_k]
@@ -78,7 +79,7 @@ struct BoundaryParams {
   int rows, hv, hidden, chunks;
   uint4* layer_out;         // [rows][hv]
   uint2* mx_data;           // [rows][hv] (8 E4M3 codes per vector)
-  uint8_t* mx_scale;        // [rows][hidden / 32]
+  uint8_t* mx_scale;        // [rows][hidden / 32] or swizzled (scale_kt)
   // row-RMS handoff
   unsigned long long* slots;  // [max_rows][slot_stride]
   unsigned* epoch;            // [max_rows]
@@ -88,6 +89,9 @@ struct BoundaryParams {
   int rounds;
   int spin_limit;
 };
+// The argument block of the undeferred kernels stays within 256 bytes (a step in launch
+// cost was measured above it).
+static_assert(sizeof(BoundaryParams) == 192, "BoundaryParams grew");
 
 // Deferred coefficients: post, comb and pre come from a pending coefficient call's
 // split-K partials, finished in the kernel; each row's first workgroup writes them out.
@@ -520,7 +524,8 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     const uint32_t lo = cvt_pk4_e4m3(q[0] * sc, q[1] * sc, q[2] * sc, q[3] * sc);
     const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
     p.mx_data[(size_t)r * p.hv + v] = make_uint2(lo, hi);
-    if ((v & 3) == 0) p.mx_scale[(size_t)r * (p.hidden / 32) + (v >> 2)] = (uint8_t)(ex + 127);
+    if ((v & 3) == 0)
+      p.mx_scale[mx_scale_offset(r, v >> 2, p.hidden / 32, p.scale_kt)] = (uint8_t)(ex + 127);
   }
 }
 
@@ -688,6 +693,7 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   p.layer_out = reinterpret_cast<uint4*>(L.layer_input_out);
   p.mx_data = reinterpret_cast<uint2*>(L.mx_data_out);
   p.mx_scale = L.mx_scale_out;
+  p.scale_kt = L.scale_kt;
   p.slots = L.slots;
   p.epoch = L.epoch;
   p.errors = L.errors;

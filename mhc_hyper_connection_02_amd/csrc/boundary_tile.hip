@@ -73,6 +73,7 @@ struct TileParams {
   // sublayer output: TP partials ...
   const uint4* xp;          // [tp][rows][hv]
   int tp;
+  int scale_kt;             // MXFP8 scale layout (mx_scale_offset): 0 row-major, else 128x4 tiles
   // ... or an unfinalized MoE output
   const uint4* g;           // [num_permuted][hv]
   const float* ew;          // [rows][top_k]
@@ -90,7 +91,7 @@ struct TileParams {
   int rows, hv, chunks;     // hidden = 8 hv
   uint4* layer_out;         // [rows][hv]
   uint2* mx_data;           // [rows][hv]
-  uint8_t* mx_scale;        // [rows][hidden / 32]
+  uint8_t* mx_scale;        // [rows][hidden / 32] or swizzled (scale_kt)
   // the next coefficients
   const uint4* fn;          // [4 * hidden][24] bf16, 3 vectors per k row
   const float* scale;       // [3]
@@ -110,6 +111,9 @@ struct TileParams {
   unsigned* errors;
   int tile_cap, tiles_per_round, rounds, spin_limit;  // tile_cap: tiles of the scratch
 };
+// The whole argument block of the undeferred kernels: at most 256 bytes (a step in launch
+// cost was measured above it).
+static_assert(sizeof(TileParams) == 256, "TileParams grew");
 
 // Handoff words, tile-major: per (tile, chunk) the 16 rows' sums of y^2, then per (tile,
 // chunk, row) the 25 coefficient partials (24 logits, the sum of v^2). One workgroup's
@@ -602,7 +606,8 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
       const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
       if (active) {
         p.mx_data[(size_t)r * p.hv + v] = make_uint2(lo, hi);
-        if ((v & 3) == 0) p.mx_scale[(size_t)r * ((p.hv * 8) / 32) + (v >> 2)] = (uint8_t)(ex + 127);
+        if ((v & 3) == 0)
+          p.mx_scale[mx_scale_offset(r, v >> 2, p.hv / 4, p.scale_kt)] = (uint8_t)(ex + 127);
       }
     }
   }
@@ -738,6 +743,7 @@ hipError_t launch_boundary_tile(const TileLaunch& T, hipStream_t stream) {
   p.layer_out = reinterpret_cast<uint4*>(L.layer_input_out);
   p.mx_data = reinterpret_cast<uint2*>(L.mx_data_out);
   p.mx_scale = L.mx_scale_out;
+  p.scale_kt = L.scale_kt;
   p.fn = reinterpret_cast<const uint4*>(T.fn);
   p.scale = T.coef.scale;
   p.base = T.coef.base;

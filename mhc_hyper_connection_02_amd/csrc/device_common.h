@@ -76,6 +76,19 @@ __device__ __forceinline__ int e8m0_exponent(uint32_t amax_bits) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// Byte offset of the E8M0 scale of row r, 32-element block kb, in the MXFP8 scale
+// output. kt == 0: plain row-major [rows][kblocks]. kt > 0: the swizzled 128x4
+// layout that the boundary page names for its MXFP8 layer input (FlashInfer's, the
+// block-scale layout of the published block-scaled GEMM interfaces): rows padded to
+// 128, blocks to 4, one 512-byte tile per 128 rows x 4 blocks, tiles row-major with
+// kt = padded blocks / 4 tiles per tile row; inside a tile, byte
+// (r % 32) * 16 + ((r / 32) % 4) * 4 + kb % 4.
+__device__ __forceinline__ size_t mx_scale_offset(int r, int kb, int kblocks, int kt) {
+  if (kt == 0) return (size_t)r * kblocks + kb;
+  return (((size_t)(r >> 7) * kt + (kb >> 2)) << 9) + ((r & 31) << 4) + (((r >> 5) & 3) << 2) +
+         (kb & 3);
+}
+
 // Cross-lane moves on the DPP path (no LDS round trip). Quad permutations act
 // within each group of 4 lanes; row rotations within each row of 16 lanes.
 constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]

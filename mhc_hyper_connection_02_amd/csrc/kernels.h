@@ -31,6 +31,8 @@ struct BoundaryLaunch {
   uint16_t* layer_input_out;
   uint8_t* mx_data_out;         // NULL: no MXFP8
   uint8_t* mx_scale_out;
+  int scale_kt;                 // 0: scales row-major [rows][hidden/32]; else the swizzled
+                                // 128x4 layout with scale_kt tiles per 128 rows
   unsigned long long* slots;    // [max_rows][slot_stride] row-RMS handoff words
   unsigned* epoch;              // [max_rows]
   unsigned* errors;             // [1] handoff timeouts

@@ -20,7 +20,7 @@ def test_header_declares_the_entry_points():
                  "mhc_residual_only", "mhc_finalize", "mhc_collapse_mean", "mhc_pre_coeffs",
                  "mhc_status_string", "mhc_get_errors", "mhc_first", "mhc_collapse_norm",
                  "mhc_pre_coeffs_deferred", "mhc_pre_coeffs_flush", "mhc_boundary_coeffs",
-                 "mhc_finalize_coeffs"):
+                 "mhc_finalize_coeffs", "mhc_mxfp8_scale_bytes"):
         assert want in names
 
 
@@ -44,6 +44,22 @@ def test_status_strings():
         s = lib.mhc_status_string(code).decode()
         assert s.startswith("MHC")
     assert "unknown" in lib.mhc_status_string(99).decode()
+
+
+def test_mxfp8_scale_bytes_host_only():
+    """Scale-buffer sizes of both layouts (no device work): row-major rows * hidden/32;
+    swizzled 128x4 rows padded to 128 and blocks to 4."""
+    lib = binding.load_library()
+    n = ctypes.c_uint64(0)
+    cases = [((32, 7168, 0), 32 * 224), ((32, 7168, 1), 128 * 224), ((130, 1056, 1), 256 * 36),
+             ((0, 1056, 1), 0), ((1, 32, 1), 128 * 4), ((128, 128, 1), 128 * 4),
+             ((65536, 65536, 1), 65536 * 2048)]
+    for args, want in cases:
+        assert lib.mhc_mxfp8_scale_bytes(*args, ctypes.byref(n)) == 0, args
+        assert n.value == want, args
+    for args, code in [((4, 1000, 0), 2), ((-1, 1024, 0), 2), ((4, 0, 1), 2), ((4, 1024, 2), 2)]:
+        assert lib.mhc_mxfp8_scale_bytes(*args, ctypes.byref(n)) == code, args
+    assert lib.mhc_mxfp8_scale_bytes(4, 1024, 0, None) == 1
 
 
 def test_create_rejects_bad_sizes_before_any_device_call():
