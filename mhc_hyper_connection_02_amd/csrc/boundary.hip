@@ -271,7 +271,7 @@ __device__ __forceinline__ void boundary_item_quad(const BoundaryParams& p,
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(cq[d], f[e], o[e]);
   }
-  if (active) p.res_out[((size_t)r * kHC + q) * p.hv + v] = pack8_round(o);
+  if (active) store_nt(p.res_out + ((size_t)r * kHC + q) * p.hv + v, pack8_round(o));
   if constexpr (DEFER) __syncthreads();  // s_coef is rewritten for the next row
 }
 
@@ -420,7 +420,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     uint4* out = p.res_out + (size_t)r * kHC * p.hv + v;
 #pragma unroll
     for (int i = 0; i < kHC; ++i)
-      if (active) out[(size_t)i * p.hv] = xr;
+      if (active) store_nt(out + (size_t)i * p.hv, xr);
   } else if constexpr (MODE == kBoundaryHead) {
 #pragma unroll
     for (int j = 0; j < kHC; ++j) unpack8(sv[j], sn[j]);
@@ -439,7 +439,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
         sn[i][e] = a;
       }
       const uint4 o = pack8_round(sn[i]);
-      if (active) out[(size_t)i * p.hv] = o;  // the streams do not wait for the RMS
+      if (active) store_nt(out + (size_t)i * p.hv, o);  // the streams do not wait for the RMS
       if constexpr (HAS_PRE) unpack8(o, sn[i]);
     }
   }
@@ -508,7 +508,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = (y[e] * inv) * w[e];
   const uint4 ob = pack8_round(o);
-  p.layer_out[(size_t)r * p.hv + v] = ob;
+  store_nt(p.layer_out + (size_t)r * p.hv + v, ob);
   if constexpr (MXFP8) {
     // 32-element block = the quad of lanes holding vectors v & ~3 .. v | 3
     float q[8];
@@ -523,7 +523,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     // |q| * 2^-e <= 448 by the choice of e: in range, exact scaling
     const uint32_t lo = cvt_pk4_e4m3(q[0] * sc, q[1] * sc, q[2] * sc, q[3] * sc);
     const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
-    p.mx_data[(size_t)r * p.hv + v] = make_uint2(lo, hi);
+    store_nt(p.mx_data + (size_t)r * p.hv + v, make_uint2(lo, hi));
     if ((v & 3) == 0)
       p.mx_scale[mx_scale_offset(r, v >> 2, p.hidden / 32, p.scale_kt)] = (uint8_t)(ex + 127);
   }
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(256) void collapse_mean_kernel(const uint4* __restr
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] *= 0.25f;
-  out[i] = pack8_round(acc);
+  store_nt(out + i, pack8_round(acc));
 }
 
 // ---------------------------------------------------------------------------

@@ -398,7 +398,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
       sn[i][e] = a;
     }
     const uint4 o = pack8_round(sn[i]);
-    if (active) out[(size_t)i * p.hv] = o;
+    if (active) store_nt(out + (size_t)i * p.hv, o);
     S.sT[i][m][vl] = active ? o : make_uint4(0u, 0u, 0u, 0u);
     unpack8(o, sn[i]);
 #pragma unroll
@@ -590,7 +590,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (y[e] * inv) * w[e];
     const uint4 ob = pack8_round(o);
-    if (active) p.layer_out[(size_t)r * p.hv + v] = ob;
+    if (active) store_nt(p.layer_out + (size_t)r * p.hv + v, ob);
     if constexpr (MXFP8) {
       // 32-element block = the quad of lanes holding vectors v & ~3 .. v | 3
       float q[8];
@@ -605,7 +605,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
       const uint32_t lo = cvt_pk4_e4m3(q[0] * sc, q[1] * sc, q[2] * sc, q[3] * sc);
       const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
       if (active) {
-        p.mx_data[(size_t)r * p.hv + v] = make_uint2(lo, hi);
+        store_nt(p.mx_data + (size_t)r * p.hv + v, make_uint2(lo, hi));
         if ((v & 3) == 0)
           p.mx_scale[mx_scale_offset(r, v >> 2, p.hv / 4, p.scale_kt)] = (uint8_t)(ex + 127);
       }

