@@ -56,8 +56,13 @@ __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const Pr
   constexpr int kMaxFnVecs = kMaxStepsPerWg * kStepK * kNC / 8 / (kPreWaves * kWave);  // 12
 
   const int wg = blockIdx.x;
-  const int ks = wg % p.ks_count;  // ks_count % 8 == 0: a k range stays on one XCD
-  const int rb = wg / p.ks_count;
+  // (row block, split) pairs are dealt to the 8 XCDs in contiguous ranges (the grid,
+  // row blocks x ks_count, is a multiple of 8): the splits of a (row, logit), adjacent in
+  // `part`, are then written from one XCD's L2 (0.9 us less per 128-row call than dealing
+  // consecutive splits to consecutive XCDs; the same at 64 rows)
+  const int idx = (wg % 8) * ((int)gridDim.x / 8) + wg / 8;
+  const int ks = idx % p.ks_count;
+  const int rb = idx / p.ks_count;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
