@@ -115,9 +115,22 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
  *         holds mhc_mxfp8_scale_bytes(R, H, MHC_SCALE_SWIZZLED_128X4) bytes; the
  *         padding bytes (rows >= R, blocks >= H/32) are not written.
  *     Other values: MHC_ERR_SHAPE.
+ *   MHC_OPT_LANE_ELEMS: hidden elements per thread of the boundary and finalize kernels that
+ *     write a layer input (deferred coefficients or not): 8 (16-byte vectors) or 4 (default; 8-byte vectors at
+ *     twice the threads per workgroup, so a row keeps the same number of workgroups). 4 is
+ *     used only where the block size is chosen per call, the doubled workgroup fits the
+ *     co-residency limit and the call needs no more rounds than at 8; otherwise 8. The new
+ *     streams are identical either way (every element's arithmetic is the same); the row's
+ *     sum of squares is added in another order, so the layer input may differ in the last
+ *     bit of rare elements. Other values: MHC_ERR_SHAPE.
  * Unknown options: MHC_ERR_INVALID_ARG.
  */
-enum mhc_option { MHC_OPT_BOUNDARY_BLOCK = 1, MHC_OPT_SPIN_LIMIT = 2, MHC_OPT_SCALE_LAYOUT = 3 };
+enum mhc_option {
+  MHC_OPT_BOUNDARY_BLOCK = 1,
+  MHC_OPT_SPIN_LIMIT = 2,
+  MHC_OPT_SCALE_LAYOUT = 3,
+  MHC_OPT_LANE_ELEMS = 4
+};
 enum mhc_scale_layout { MHC_SCALE_ROW_MAJOR = 0, MHC_SCALE_SWIZZLED_128X4 = 1 };
 int mhc_set_option(mhc_handle h, int option, int value);
 

@@ -275,9 +275,10 @@ __device__ __forceinline__ void boundary_item_quad(const BoundaryParams& p,
   if constexpr (DEFER) __syncthreads();  // s_coef is rewritten for the next row
 }
 
-// One lane per 16-byte vector: lane owns 8 elements of the row and all four streams of
-// them (BS vectors per workgroup). Same dataflow and handoff as the quad layout above.
-template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8, int MODE, bool DEFER>
+// One lane per vector of EL consecutive elements (EL = 8: 16-byte vectors, EL = 4: 8-byte
+// vectors): the lane owns those elements of the row and all four streams of them (BS
+// vectors per workgroup). Same dataflow and handoff as the quad layout above.
+template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8, int MODE, bool DEFER, int EL>
 __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
                                                    const float* __restrict__ post,
                                                    const float* __restrict__ comb,
@@ -290,8 +291,18 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  static_assert(EL == 8 || EL == 4, "a lane holds 8 or 4 elements");
+  using Vec = typename std::conditional<EL == 8, uint4, uint2>::type;
+  const int nv = p.hv * (8 / EL);  // vectors per row
+  const Vec* xp = reinterpret_cast<const Vec*>(p.xp);
+  const Vec* gp = reinterpret_cast<const Vec*>(p.g);
+  const Vec* shp = reinterpret_cast<const Vec*>(p.shared);
+  const Vec* res_in = reinterpret_cast<const Vec*>(p.res_in);
+  Vec* res_out = reinterpret_cast<Vec*>(p.res_out);
+  const Vec* norm_w = reinterpret_cast<const Vec*>(p.norm_w);
+  Vec* layer_out = reinterpret_cast<Vec*>(p.layer_out);
   const int v = c * BS + tid;
-  const bool active = v < p.hv;
+  const bool active = v < nv;
   const int va = active ? v : 0;
 
   // the row's epoch (wave 0 runs the handoff), read by every wave without a branch, first,
@@ -300,9 +311,9 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   if constexpr (HAS_PRE)
     epoch_now = __hip_atomic_load(p.epoch + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  float x[8];
+  float x[EL];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  for (int e = 0; e < EL; ++e) x[e] = 0.f;
   int pk[8];
   float wk[8];
   if constexpr (FINALIZE) {
@@ -329,79 +340,79 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   }
   // the norm weight first: it is shared by every row, so it mostly hits in L2, and issued
   // ahead of the streaming loads it is back before them (measured: 0.2 us per call)
-  uint4 wv = make_uint4(0u, 0u, 0u, 0u);
-  if constexpr (HAS_PRE) wv = p.norm_w[va];
-  uint4 sv[kHC];
+  Vec wv = {};
+  if constexpr (HAS_PRE) wv = norm_w[va];
+  Vec sv[kHC];
   if constexpr (MODE != kBoundaryFirst) {
 #pragma unroll
-    for (int j = 0; j < kHC; ++j) sv[j] = load_nt(p.res_in + ((size_t)r * kHC + j) * p.hv + va);
+    for (int j = 0; j < kHC; ++j) sv[j] = load_nt(res_in + ((size_t)r * kHC + j) * nv + va);
   }
-  uint4 xr = make_uint4(0u, 0u, 0u, 0u);  // first: the embedding vector itself
+  Vec xr = {};  // first: the embedding vector itself
   CoeffPrefetch<kBoundaryPrefetch> cf;
   if constexpr (DEFER)
     if (wave == 0) coeff_row_prefetch<true>(dp.coef, r, lane, cf);
 
   if constexpr (MODE == kBoundaryFirst) {
-    xr = load_nt(p.xp + (size_t)r * p.hv + va);
-    unpack8(xr, x);
+    xr = load_nt(xp + (size_t)r * nv + va);
+    unpack_bf16(xr, x);
   } else if constexpr (MODE == kBoundaryHead) {
     // no sublayer output
   } else if constexpr (!FINALIZE) {
     // t ascending
-    const uint4* src = p.xp + (size_t)r * p.hv + va;
-    const size_t slice = (size_t)p.rows * p.hv;
+    const Vec* src = xp + (size_t)r * nv + va;
+    const size_t slice = (size_t)p.rows * nv;
     for (int t0 = 0; t0 < p.tp; t0 += 8) {
-      uint4 xv[8];
+      Vec xv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (t0 + u < p.tp) xv[u] = load_nt(src + (size_t)(t0 + u) * slice);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (t0 + u < p.tp) {
-          float f[8];
-          unpack8(xv[u], f);
+          float f[EL];
+          unpack_bf16(xv[u], f);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] += f[e];
+          for (int e = 0; e < EL; ++e) x[e] += f[e];
         }
       }
     }
   } else {
     // k ascending, then the shared row
-    const uint4 shv = load_nt(p.shared + (size_t)r * p.hv + va);
-    uint4 gv[8];
+    const Vec shv = load_nt(shp + (size_t)r * nv + va);
+    Vec gv[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (u < p.top_k) {
         const bool ok = pk[u] >= 0 && pk[u] < p.num_permuted;
-        gv[u] = load_nt(p.g + (size_t)(ok ? pk[u] : 0) * p.hv + va);
+        gv[u] = load_nt(gp + (size_t)(ok ? pk[u] : 0) * nv + va);
         if (!ok) wk[u] = 0.f;
       }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (u < p.top_k) {
-        float f[8];
-        unpack8(gv[u], f);
+        float f[EL];
+        unpack_bf16(gv[u], f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(wk[u], f[e], x[e]);
+        for (int e = 0; e < EL; ++e) x[e] = __builtin_fmaf(wk[u], f[e], x[e]);
       }
     }
     for (int k = 8; k < p.top_k; ++k) {  // slots beyond 8, in order
       const int pi = idx[r * p.top_k + k];
       const bool ok = pi >= 0 && pi < p.num_permuted;
       const float w = ok ? ew[r * p.top_k + k] : 0.f;
-      const uint4 g = load_nt(p.g + (size_t)(ok ? pi : 0) * p.hv + va);
-      float f[8];
-      unpack8(g, f);
+      const Vec g = load_nt(gp + (size_t)(ok ? pi : 0) * nv + va);
+      float f[EL];
+      unpack_bf16(g, f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(w, f[e], x[e]);
+      for (int e = 0; e < EL; ++e) x[e] = __builtin_fmaf(w, f[e], x[e]);
     }
-    float f[8];
-    unpack8(shv, f);
+    float f[EL];
+    unpack_bf16(shv, f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] += f[e];
+    for (int e = 0; e < EL; ++e) x[e] += f[e];
   }
-  if constexpr (MODE == kBoundaryMix) round8_bf16(x);  // the reduced output is a bf16 tensor
+  if constexpr (MODE == kBoundaryMix) round_bf16(x);  // the reduced output is a bf16 tensor
   if constexpr (DEFER) {
     if (wave == 0) deferred_finish(dp, r, c, cf, sc_l, base_l, s_coef);
     __syncthreads();
@@ -414,55 +425,55 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     for (int i = 0; i < kHC * kHC; ++i) cmb[i] = s_coef[2 * kHC + i];
   }
 
-  float sn[kHC][8];
+  float sn[kHC][EL];
   if constexpr (MODE == kBoundaryFirst) {
     // every stream is the embedding, bit for bit
-    uint4* out = p.res_out + (size_t)r * kHC * p.hv + v;
+    Vec* out = res_out + (size_t)r * kHC * nv + v;
 #pragma unroll
     for (int i = 0; i < kHC; ++i)
-      if (active) store_nt(out + (size_t)i * p.hv, xr);
+      if (active) store_nt(out + (size_t)i * nv, xr);
   } else if constexpr (MODE == kBoundaryHead) {
 #pragma unroll
-    for (int j = 0; j < kHC; ++j) unpack8(sv[j], sn[j]);
+    for (int j = 0; j < kHC; ++j) unpack_bf16(sv[j], sn[j]);
   } else {
-    uint4* out = p.res_out + (size_t)r * kHC * p.hv + v;
-    float s[kHC][8];
+    Vec* out = res_out + (size_t)r * kHC * nv + v;
+    float s[kHC][EL];
 #pragma unroll
-    for (int j = 0; j < kHC; ++j) unpack8(sv[j], s[j]);
+    for (int j = 0; j < kHC; ++j) unpack_bf16(sv[j], s[j]);
 #pragma unroll
     for (int i = 0; i < kHC; ++i) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < EL; ++e) {
         float a = pst[i] * x[e];
 #pragma unroll
         for (int j = 0; j < kHC; ++j) a = __builtin_fmaf(cmb[i * kHC + j], s[j][e], a);
         sn[i][e] = a;
       }
-      const uint4 o = pack8_round(sn[i]);
-      if (active) store_nt(out + (size_t)i * p.hv, o);  // the streams do not wait for the RMS
-      if constexpr (HAS_PRE) unpack8(o, sn[i]);
+      const Vec o = pack_bf16(sn[i]);
+      if (active) store_nt(out + (size_t)i * nv, o);  // the streams do not wait for the RMS
+      if constexpr (HAS_PRE) unpack_bf16(o, sn[i]);
     }
   }
   if constexpr (!HAS_PRE) return;
 
-  float y[8];
+  float y[EL];
   float sq = 0.f;
   if constexpr (MODE == kBoundaryFirst) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = x[e];  // the identity pre-mix
+    for (int e = 0; e < EL; ++e) y[e] = x[e];  // the identity pre-mix
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < EL; ++e) {
       float a = 0.f;
 #pragma unroll
       for (int j = 0; j < kHC; ++j) a = __builtin_fmaf(pr[j], sn[j][e], a);
       y[e] = a;
     }
     // the head's collapse is a bf16 tensor of its own before the norm
-    if constexpr (MODE == kBoundaryHead) round8_bf16(y);
+    if constexpr (MODE == kBoundaryHead) round_bf16(y);
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) sq = __builtin_fmaf(y[e], y[e], sq);
+  for (int e = 0; e < EL; ++e) sq = __builtin_fmaf(y[e], y[e], sq);
   if (!active) sq = 0.f;
   sq = wave_sum(sq);
   if (lane == 0) s_red[wave] = sq;
@@ -503,35 +514,43 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   __syncthreads();
   if (!active) return;
   const float inv = *s_inv;
-  float w[8], o[8];
-  unpack8(wv, w);
+  float w[EL], o[EL];
+  unpack_bf16(wv, w);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = (y[e] * inv) * w[e];
-  const uint4 ob = pack8_round(o);
-  store_nt(p.layer_out + (size_t)r * p.hv + v, ob);
+  for (int e = 0; e < EL; ++e) o[e] = (y[e] * inv) * w[e];
+  const Vec ob = pack_bf16(o);
+  store_nt(layer_out + (size_t)r * nv + v, ob);
   if constexpr (MXFP8) {
-    // 32-element block = the quad of lanes holding vectors v & ~3 .. v | 3
-    float q[8];
-    unpack8(ob, q);
+    // 32-element block = the 32 / EL consecutive lanes holding vectors v & ~(32/EL - 1) ..
+    // (a quad at EL = 8, two quads at EL = 4)
+    constexpr int kPerBlock = 32 / EL;
+    float q[EL];
+    unpack_bf16(ob, q);
     float amax = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(q[e]));
+    for (int e = 0; e < EL; ++e) amax = fmaxf(amax, fabsf(q[e]));
     amax = fmaxf(amax, dpp_f32<kDppQuadXor1>(amax));
     amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
+    if constexpr (EL == 4) amax = fmaxf(amax, swizzle_xor4(amax));
     const int ex = e8m0_exponent(__float_as_uint(amax));
     const float sc = __uint_as_float((uint32_t)(127 - ex) << 23);
     // |q| * 2^-e <= 448 by the choice of e: in range, exact scaling
     const uint32_t lo = cvt_pk4_e4m3(q[0] * sc, q[1] * sc, q[2] * sc, q[3] * sc);
-    const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
-    store_nt(p.mx_data + (size_t)r * p.hv + v, make_uint2(lo, hi));
-    if ((v & 3) == 0)
-      p.mx_scale[mx_scale_offset(r, v >> 2, p.hidden / 32, p.scale_kt)] = (uint8_t)(ex + 127);
+    if constexpr (EL == 8) {
+      const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
+      store_nt(p.mx_data + (size_t)r * p.hv + v, make_uint2(lo, hi));
+    } else {
+      store_nt(reinterpret_cast<uint32_t*>(p.mx_data) + (size_t)r * nv + v, lo);
+    }
+    if ((v & (kPerBlock - 1)) == 0)
+      p.mx_scale[mx_scale_offset(r, v / kPerBlock, p.hidden / 32, p.scale_kt)] =
+          (uint8_t)(ex + 127);
   }
 }
 
 // The deferred variants are held to at least 4 waves per SIMD (at most 128 VGPRs), as
 // the others are without a hint, so that a 128-row call keeps one round.
-template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8, int MODE, bool DEFER>
+template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8, int MODE, bool DEFER, int EL = 8>
 __global__ __launch_bounds__(BS, DEFER ? 4 : 1) void boundary_kernel(const BoundaryParams p,
                                                       const float* __restrict__ post,
                                                       const float* __restrict__ comb,
@@ -557,7 +576,7 @@ __global__ __launch_bounds__(BS, DEFER ? 4 : 1) void boundary_kernel(const Bound
     if constexpr (!HAS_PRE)
       boundary_item_quad<BS, FINALIZE, DEFER>(p, dp, r, c, s_coef, sc_l, base_l);
     else
-      boundary_item_lane<BS, FINALIZE, HAS_PRE, MXFP8, MODE, DEFER>(
+      boundary_item_lane<BS, FINALIZE, HAS_PRE, MXFP8, MODE, DEFER, EL>(
           p, post, comb, pre, idx, ew, dp, r, c, s_red, &s_inv, s_coef, sc_l, base_l);
   }
 }
@@ -591,19 +610,29 @@ __global__ __launch_bounds__(256) void collapse_mean_kernel(const uint4* __restr
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-template <int BS, bool FIN, bool PRE, bool MX, int MODE = kBoundaryMix, bool DEFER = false>
+template <int BS, bool FIN, bool PRE, bool MX, int MODE = kBoundaryMix, bool DEFER = false,
+          int EL = 8>
 static hipError_t launch_one(const BoundaryParams& p, const DeferParams& d, int grid,
                              hipStream_t st) {
   DeferArg<DEFER> dp;
   if constexpr (DEFER) dp = d;
-  hipLaunchKernelGGL((boundary_kernel<BS, FIN, PRE, MX, MODE, DEFER>), dim3(grid), dim3(BS), 0,
+  hipLaunchKernelGGL((boundary_kernel<BS, FIN, PRE, MX, MODE, DEFER, EL>), dim3(grid), dim3(BS), 0,
                      st, p, p.post, p.comb, p.pre, p.idx, p.ew, dp);
   return hipGetLastError();
 }
 
 template <int BS, bool DEFER>
 static hipError_t launch_mix(const BoundaryParams& p, const DeferParams& d, bool fin, bool pre,
-                             bool mx, int grid, hipStream_t st) {
+                             bool mx, int el, int grid, hipStream_t st) {
+  if constexpr (BS >= 256) {
+    if (el == 4 && pre) {  // four elements per lane (the layer-input kernels)
+      if (!fin)
+        return mx ? launch_one<BS, false, true, true, kBoundaryMix, DEFER, 4>(p, d, grid, st)
+                  : launch_one<BS, false, true, false, kBoundaryMix, DEFER, 4>(p, d, grid, st);
+      return mx ? launch_one<BS, true, true, true, kBoundaryMix, DEFER, 4>(p, d, grid, st)
+                : launch_one<BS, true, true, false, kBoundaryMix, DEFER, 4>(p, d, grid, st);
+    }
+  }
   if (!fin) {
     if (!pre) return launch_one<BS, false, false, false, kBoundaryMix, DEFER>(p, d, grid, st);
     return mx ? launch_one<BS, false, true, true, kBoundaryMix, DEFER>(p, d, grid, st)
@@ -616,22 +645,23 @@ static hipError_t launch_mix(const BoundaryParams& p, const DeferParams& d, bool
 
 template <int BS>
 static hipError_t launch_bs(const BoundaryParams& p, const DeferParams& d, bool fin, bool pre,
-                            bool mx, int mode, bool defer, int grid, hipStream_t st) {
+                            bool mx, int mode, bool defer, int el, int grid, hipStream_t st) {
   if (mode == kBoundaryFirst)
     return mx ? launch_one<BS, false, true, true, kBoundaryFirst>(p, d, grid, st)
               : launch_one<BS, false, true, false, kBoundaryFirst>(p, d, grid, st);
   if (mode == kBoundaryHead)
     return mx ? launch_one<BS, false, true, true, kBoundaryHead>(p, d, grid, st)
               : launch_one<BS, false, true, false, kBoundaryHead>(p, d, grid, st);
-  return defer ? launch_mix<BS, true>(p, d, fin, pre, mx, grid, st)
-               : launch_mix<BS, false>(p, d, fin, pre, mx, grid, st);
+  return defer ? launch_mix<BS, true>(p, d, fin, pre, mx, el, grid, st)
+               : launch_mix<BS, false>(p, d, fin, pre, mx, el, grid, st);
 }
 
-template <int BS, bool FIN, bool PRE, bool MX, int MODE = kBoundaryMix, bool DEFER = false>
+template <int BS, bool FIN, bool PRE, bool MX, int MODE = kBoundaryMix, bool DEFER = false,
+          int EL = 8>
 static int occupancy_one() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, boundary_kernel<BS, FIN, PRE, MX, MODE, DEFER>, BS, 0) != hipSuccess)
+          &n, boundary_kernel<BS, FIN, PRE, MX, MODE, DEFER, EL>, BS, 0) != hipSuccess)
     return 0;
   return n;
 }
@@ -649,6 +679,16 @@ static int occupancy_bs() {
   n = min(n, occupancy_one<BS, true, true, true, kBoundaryMix, true>());
   n = min(n, occupancy_one<BS, false, true, true, kBoundaryFirst>());
   n = min(n, occupancy_one<BS, false, true, true, kBoundaryHead>());
+  if constexpr (BS >= 256) {
+    n = min(n, occupancy_one<BS, false, true, false, kBoundaryMix, false, 4>());
+    n = min(n, occupancy_one<BS, false, true, true, kBoundaryMix, false, 4>());
+    n = min(n, occupancy_one<BS, true, true, false, kBoundaryMix, false, 4>());
+    n = min(n, occupancy_one<BS, true, true, true, kBoundaryMix, false, 4>());
+    n = min(n, occupancy_one<BS, false, true, false, kBoundaryMix, true, 4>());
+    n = min(n, occupancy_one<BS, false, true, true, kBoundaryMix, true, 4>());
+    n = min(n, occupancy_one<BS, true, true, false, kBoundaryMix, true, 4>());
+    n = min(n, occupancy_one<BS, true, true, true, kBoundaryMix, true, 4>());
+  }
   return n;
 }
 
@@ -688,8 +728,30 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   p.hidden = L.hidden;
   p.hv = L.hidden / 8;
   const bool pre = L.pre != nullptr || L.mode == kBoundaryFirst;  // a layer input is written
-  const int block = pre ? L.block : kResidualOnlyBlock;
-  p.chunks = boundary_chunks(L.hidden, block, pre);
+  const int row_blocks = (L.rows + kXcds - 1) / kXcds;  // rows per XCD in total
+  // rows per XCD per round: a round may use at most half of the XCD's resident workgroups
+  // (at least one row: a row's chunks fit half an XCD, checked at handle creation)
+  auto rows_per_round = [&](int max_wgs, int chunks) {
+    int rpr = (max_wgs / 2) / chunks;
+    if (rpr < 1) rpr = 1;
+    return rpr > row_blocks ? row_blocks : rpr;
+  };
+  // four elements per lane where asked for and instantiated (the mix kernels with a layer
+  // input, deferred or not, at 256 or 512 threads: the same chunks as `block` at eight),
+  // unless the larger workgroups would take more rounds (measured: a second round costs
+  // more than the shorter per-lane work saves). Deferred and undeferred calls choose alike,
+  // so their results stay bit-identical.
+  const int chunks8 = boundary_chunks(L.hidden, pre ? L.block : kResidualOnlyBlock, pre);
+  bool use4 = L.lane_elems == 4 && L.pre != nullptr && L.mode == kBoundaryMix && L.block4 >= 256;
+  if (use4) {
+    const int r8 = rows_per_round(L.max_wgs_per_xcd, chunks8);
+    const int r4 = rows_per_round(L.max_wgs_per_xcd4, chunks8);
+    use4 = (row_blocks + r4 - 1) / r4 <= (row_blocks + r8 - 1) / r8;
+  }
+  const int el = use4 ? 4 : 8;
+  const int block = !pre ? kResidualOnlyBlock : (use4 ? L.block4 : L.block);
+  const int max_wgs_per_xcd = use4 ? L.max_wgs_per_xcd4 : L.max_wgs_per_xcd;
+  p.chunks = chunks8;
   p.layer_out = reinterpret_cast<uint4*>(L.layer_input_out);
   p.mx_data = reinterpret_cast<uint2*>(L.mx_data_out);
   p.mx_scale = L.mx_scale_out;
@@ -706,14 +768,8 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   d.def_comb = L.defer ? const_cast<float*>(L.comb) : nullptr;
   const bool fin = L.gemm2_permuted != nullptr;
   const bool mx = L.mx_data_out != nullptr;
-  const int row_blocks = (L.rows + kXcds - 1) / kXcds;  // rows per XCD in total
   if (pre) {
-    // a round may use at most half of the XCD's resident workgroups
-    // (at least one row: a row's chunks fit half an XCD, checked at handle creation)
-    const int per_xcd = L.max_wgs_per_xcd / 2;
-    int rpr = per_xcd / p.chunks;
-    if (rpr < 1) rpr = 1;
-    if (rpr > row_blocks) rpr = row_blocks;
+    const int rpr = rows_per_round(max_wgs_per_xcd, p.chunks);
     p.rows_per_round = rpr;
     p.rounds = (row_blocks + rpr - 1) / rpr;
   } else {
@@ -722,9 +778,9 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   }
   const int grid = kXcds * p.rows_per_round * p.chunks;
   switch (block) {
-    case 128: return launch_bs<128>(p, d, fin, pre, mx, L.mode, L.defer, grid, stream);
-    case 256: return launch_bs<256>(p, d, fin, pre, mx, L.mode, L.defer, grid, stream);
-    case 512: return launch_bs<512>(p, d, fin, pre, mx, L.mode, L.defer, grid, stream);
+    case 128: return launch_bs<128>(p, d, fin, pre, mx, L.mode, L.defer, el, grid, stream);
+    case 256: return launch_bs<256>(p, d, fin, pre, mx, L.mode, L.defer, el, grid, stream);
+    case 512: return launch_bs<512>(p, d, fin, pre, mx, L.mode, L.defer, el, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -33,6 +33,16 @@ __device__ __forceinline__ void store_nt(uint2* p, const uint2& v) {
   __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
 }
 
+__device__ __forceinline__ void store_nt(uint32_t* p, uint32_t v) {
+  __builtin_nontemporal_store(v, p);
+}
+
+// 8-byte load with the non-temporal hint (four bf16 values).
+__device__ __forceinline__ uint2 load_nt(const uint2* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v[0], v[1]);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -54,6 +64,7 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+
 // Round eight floats to bf16 and pack them.
 __device__ __forceinline__ uint4 pack8_round(const float (&f)[8]) {
   uint4 v;
@@ -67,6 +78,21 @@ __device__ __forceinline__ uint4 pack8_round(const float (&f)[8]) {
 // Round eight floats to bf16 precision in place (they stay floats).
 __device__ __forceinline__ void round8_bf16(float (&f)[8]) {
   unpack8(pack8_round(f), f);
+}
+
+// The same for a lane's 16-byte (eight bf16) or 8-byte (four bf16) vector, by overload.
+__device__ __forceinline__ void unpack_bf16(const uint4& v, float (&f)[8]) { unpack8(v, f); }
+__device__ __forceinline__ void unpack_bf16(const uint2& v, float (&f)[4]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+}
+__device__ __forceinline__ uint4 pack_bf16(const float (&f)[8]) { return pack8_round(f); }
+__device__ __forceinline__ uint2 pack_bf16(const float (&f)[4]) {
+  return make_uint2(cvt_pk_bf16(f[0], f[1]), cvt_pk_bf16(f[2], f[3]));
+}
+template <int N>
+__device__ __forceinline__ void round_bf16(float (&f)[N]) {
+  unpack_bf16(pack_bf16(f), f);
 }
 
 // Four floats -> four OCP E4M3 (FN) codes (byte i = f[i]), round to nearest even,
@@ -121,6 +147,12 @@ __device__ __forceinline__ float dpp_f32(float x) {
 template <int CTRL>
 __device__ __forceinline__ uint4 dpp_u4(const uint4& v) {
   return make_uint4(dpp_u32<CTRL>(v.x), dpp_u32<CTRL>(v.y), dpp_u32<CTRL>(v.z), dpp_u32<CTRL>(v.w));
+}
+
+// x of lane i ^ 4 within each group of 32 lanes (ds_swizzle bit mode: and 0x1F, or 0,
+// xor 4; no LDS allocation).
+__device__ __forceinline__ float swizzle_xor4(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
 }
 
 // Sum over the 64 lanes on the DPP path: within each row of 16 (quad xors, then row
