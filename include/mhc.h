@@ -115,8 +115,8 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
  *         holds mhc_mxfp8_scale_bytes(R, H, MHC_SCALE_SWIZZLED_128X4) bytes; the
  *         padding bytes (rows >= R, blocks >= H/32) are not written.
  *     Other values: MHC_ERR_SHAPE.
- *   MHC_OPT_LANE_ELEMS: hidden elements per thread of the boundary and finalize kernels that
- *     write a layer input (deferred coefficients or not): 8 (16-byte vectors) or 4 (default; 8-byte vectors at
+ *   MHC_OPT_LANE_ELEMS: hidden elements per thread of the kernels that write a layer input
+ *     (mhc_boundary, mhc_finalize, mhc_collapse_norm and the fused calls' fallback): 8 (16-byte vectors) or 4 (default; 8-byte vectors at
  *     twice the threads per workgroup, so a row keeps the same number of workgroups). 4 is
  *     used only where the block size is chosen per call, the doubled workgroup fits the
  *     co-residency limit and the call needs no more rounds than at 8; otherwise 8. The new

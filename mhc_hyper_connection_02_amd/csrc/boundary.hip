@@ -646,6 +646,11 @@ static hipError_t launch_mix(const BoundaryParams& p, const DeferParams& d, bool
 template <int BS>
 static hipError_t launch_bs(const BoundaryParams& p, const DeferParams& d, bool fin, bool pre,
                             bool mx, int mode, bool defer, int el, int grid, hipStream_t st) {
+  if constexpr (BS >= 256) {
+    if (el == 4 && mode == kBoundaryHead)
+      return mx ? launch_one<BS, false, true, true, kBoundaryHead, false, 4>(p, d, grid, st)
+                : launch_one<BS, false, true, false, kBoundaryHead, false, 4>(p, d, grid, st);
+  }
   if (mode == kBoundaryFirst)
     return mx ? launch_one<BS, false, true, true, kBoundaryFirst>(p, d, grid, st)
               : launch_one<BS, false, true, false, kBoundaryFirst>(p, d, grid, st);
@@ -688,6 +693,7 @@ static int occupancy_bs() {
     n = min(n, occupancy_one<BS, false, true, true, kBoundaryMix, true, 4>());
     n = min(n, occupancy_one<BS, true, true, false, kBoundaryMix, true, 4>());
     n = min(n, occupancy_one<BS, true, true, true, kBoundaryMix, true, 4>());
+    n = min(n, occupancy_one<BS, false, true, true, kBoundaryHead, false, 4>());
   }
   return n;
 }
@@ -736,13 +742,14 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
     if (rpr < 1) rpr = 1;
     return rpr > row_blocks ? row_blocks : rpr;
   };
-  // four elements per lane where asked for and instantiated (the mix kernels with a layer
-  // input, deferred or not, at 256 or 512 threads: the same chunks as `block` at eight),
-  // unless the larger workgroups would take more rounds (measured: a second round costs
-  // more than the shorter per-lane work saves). Deferred and undeferred calls choose alike,
-  // so their results stay bit-identical.
+  // four elements per lane where asked for (the kernels that write a layer input, at 256 or
+  // 512 threads: the same chunks as `block` at eight), unless the larger workgroups would
+  // take more rounds (measured: a second round costs more than the shorter per-lane work
+  // saves). Deferred and undeferred calls choose alike, so their results stay bit-identical.
+  // Not the first layer's entry, which has almost no arithmetic to share (measured 4.19 at
+  // eight against 4.22 us at four per lane, 32 rows).
   const int chunks8 = boundary_chunks(L.hidden, pre ? L.block : kResidualOnlyBlock, pre);
-  bool use4 = L.lane_elems == 4 && L.pre != nullptr && L.mode == kBoundaryMix && L.block4 >= 256;
+  bool use4 = L.lane_elems == 4 && pre && L.mode != kBoundaryFirst && L.block4 >= 256;
   if (use4) {
     const int r8 = rows_per_round(L.max_wgs_per_xcd, chunks8);
     const int r4 = rows_per_round(L.max_wgs_per_xcd4, chunks8);

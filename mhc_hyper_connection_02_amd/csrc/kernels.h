@@ -40,8 +40,8 @@ struct BoundaryLaunch {
   int spin_limit;
   int max_wgs_per_xcd;          // resident workgroups of this block size on one XCD
   int block;                    // 128, 256 or 512 threads per workgroup (layer-input kernels)
-  int lane_elems;               // 4: the kernels that have the four-elements-per-lane form (the
-                                // mix kernels with a layer input) run it at block4
+  int lane_elems;               // 4: the kernels that write a layer input run four elements
+                                // per lane at block4
                                 // threads (twice block, the same chunks per row); else 8
   int block4;
   int max_wgs_per_xcd4;         // resident workgroups of block4 threads on one XCD

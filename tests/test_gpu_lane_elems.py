@@ -60,3 +60,36 @@ def test_lane_elems_option_values():
     h.set_option(binding.MHC_OPT_LANE_ELEMS, 4)
     h.set_option(binding.MHC_OPT_LANE_ELEMS, 8)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("rows,hidden", [(32, 7168), (5, 1056), (128, 7168), (3, 8)])
+def test_first_and_head_four_elements_per_lane(rows, hidden):
+    import oracle
+    from oracle import codecs
+    from gpu_helpers import N, T, assert_bf16_close
+    mx = hidden % 32 == 0
+    say(f"case: first/head lane_elems=4 rows={rows} hidden={hidden} mxfp8={mx}")
+    rng = np.random.default_rng(rows + hidden)
+    x = codecs.f64_to_bf16_bits(rng.normal(0, 1, (rows, hidden)))
+    w = codecs.f64_to_bf16_bits(rng.normal(1, 0.1, hidden))
+    d = synth.boundary_inputs(rows + 7, rows=rows, hidden=hidden, tp=1, mxfp8=mx)
+    for elems in (4, 8):
+        h = handle_for(hidden, rows)
+        h.set_option(binding.MHC_OPT_LANE_ELEMS, elems)
+        f = {k: N(v) for k, v in binding.first(h, T(x), T(w), 1e-6, mxfp8=mx).items()}
+        hd = {k: N(v) for k, v in binding.collapse_norm(h, T(d["residual"]), T(d["pre"]),
+                                                       T(d["norm_weight"]), d["eps"],
+                                                       mxfp8=mx).items()}
+        torch.cuda.synchronize()
+        wf = oracle.first(x, w, 1e-6, mxfp8=mx)
+        wh = oracle.collapse_norm(d["residual"], d["pre"], d["norm_weight"], d["eps"], mxfp8=mx)
+        assert np.array_equal(f["residual"], wf["residual"]), "first: streams are x, bit for bit"
+        assert_bf16_close(f["layer_input"], wf["layer_input"], f"first {elems}/lane")
+        assert_bf16_close(hd["layer_input"], wh["layer_input"], f"head {elems}/lane")
+        for got in (f, hd):
+            if mx:
+                codes, scales = codecs.mxfp8_quantize(got["layer_input"])
+                assert np.array_equal(got["mx_scale"], scales)
+                assert np.array_equal(got["mx_data"], codes)
+        assert h.errors() == 0
+        h.close()
