@@ -390,10 +390,10 @@ def main():
     h = binding.Handle(H, 4, max_rows=128, max_tp=8, top_k=8)
     if args.block:
         h.set_option(binding.MHC_OPT_BOUNDARY_BLOCK, args.block)
-    # the handle's choice for 32 rows: 256 threads at four elements per lane (the same seven
+    # the handle's choice for 32 rows: 512 threads at two elements per lane (the same seven
     # workgroups per row as 128 threads at eight); a fixed block size runs eight per lane
-    block = args.block or 256
-    lane_elems = 8 if args.block else 4
+    block = args.block or 512
+    lane_elems = 8 if args.block else 2
     nb = bytes_boundary(R, H, TP, pre=True, mxfp8=True)
     sets = n_sets(nb)
     base = {k: T(d1[k]) for k in ("x_partials", "residual", "post", "comb", "pre", "norm_weight")}

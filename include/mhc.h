@@ -115,14 +115,17 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
  *         holds mhc_mxfp8_scale_bytes(R, H, MHC_SCALE_SWIZZLED_128X4) bytes; the
  *         padding bytes (rows >= R, blocks >= H/32) are not written.
  *     Other values: MHC_ERR_SHAPE.
- *   MHC_OPT_LANE_ELEMS: hidden elements per thread of the kernels that write a layer input
- *     (mhc_boundary, mhc_finalize, mhc_collapse_norm and the fused calls' fallback): 8 (16-byte vectors) or 4 (default; 8-byte vectors at
- *     twice the threads per workgroup, so a row keeps the same number of workgroups). 4 is
- *     used only where the block size is chosen per call, the doubled workgroup fits the
- *     co-residency limit and the call needs no more rounds than at 8; otherwise 8. The new
- *     streams are identical either way (every element's arithmetic is the same); the row's
- *     sum of squares is added in another order, so the layer input may differ in the last
- *     bit of rare elements. Other values: MHC_ERR_SHAPE.
+ *   MHC_OPT_LANE_ELEMS: the fewest hidden elements per thread that the kernels writing a
+ *     layer input (mhc_boundary, mhc_finalize, mhc_collapse_norm and the fused calls'
+ *     fallback) may use: 2 (default), 4 or 8. With e elements per thread (8: 16-byte
+ *     vectors, 4: 8-byte, 2: 4-byte) a workgroup has 8 / e times the threads of the
+ *     eight-per-thread size, so a row keeps the same number of workgroups. A call takes the
+ *     fewest e >= the option whose workgroup exists (at most 512 threads) and fits the
+ *     co-residency limit, if the block size is chosen per call and the call then needs no
+ *     more rounds than at 8; otherwise 8. The new streams are identical for every e (every
+ *     element's arithmetic is the same); the row's sum of squares is added in another
+ *     order, so the layer input may differ in the last bit of rare elements. Other values:
+ *     MHC_ERR_SHAPE.
  * Unknown options: MHC_ERR_INVALID_ARG.
  */
 enum mhc_option {

@@ -34,8 +34,8 @@ struct mhc_ctx {
   int block_set;           // the size MHC_OPT_BOUNDARY_BLOCK set, 0: automatic
   int spin_limit;          // polls before a handoff wait gives up
   int scale_layout;        // MHC_SCALE_ROW_MAJOR or MHC_SCALE_SWIZZLED_128X4
-  int lane_elems;          // elements per lane of the layer-input kernels (8, or 4 at twice
-                           // the threads: the same chunks per row)
+  int lane_elems;          // the fewest elements per lane the layer-input kernels may use
+                           // (2, 4 or 8; fewer run at more threads: the same chunks per row)
   int wgs_per_xcd[3];      // resident layer-input workgroups per XCD at block 128 / 256 / 512
   int tile_wgs_per_xcd;    // resident workgroups of the fused boundary + coefficient kernel
   int tile_rows;           // rows the fused kernel's scratch covers (0: not available)
@@ -129,19 +129,21 @@ void fill_mix(const mhc_ctx* h, mhc::BoundaryLaunch& L, const uint16_t* residual
   const int block = h->block_set ? h->block_set : (rows > kSmallRows ? h->block_many : h->block);
   L.max_wgs_per_xcd = h->wgs_per_xcd[block_index(block)];
   L.block = block;
-  // the four-elements-per-lane form: twice the threads, the same chunks per row (used by the
-  // kernels that have it, if a row still fits half an XCD at that size)
+  // the narrower forms (2 or 4 elements per lane): 8 / elements times the threads, the same
+  // chunks per row; the fewest elements allowed whose workgroup size exists and still fits
+  // a row in half an XCD (used by the kernels that have them)
   L.lane_elems = 8;
-  L.block4 = 0;
-  L.max_wgs_per_xcd4 = 0;
-  if (h->lane_elems == 4 && !h->block_set && block <= 256) {
-    const int b4 = 2 * block;
-    const int w4 = h->wgs_per_xcd[block_index(b4)];
-    if (w4 / 2 >= mhc::boundary_chunks(h->hidden, block, true)) {
-      L.lane_elems = 4;
-      L.block4 = b4;
-      L.max_wgs_per_xcd4 = w4;
-    }
+  L.block_n = 0;
+  L.max_wgs_per_xcd_n = 0;
+  for (int el = h->lane_elems; el < 8 && !h->block_set; el *= 2) {
+    const int bn = block * (8 / el);
+    if (block_index(bn) < 0) continue;
+    const int wn = h->wgs_per_xcd[block_index(bn)];
+    if (wn / 2 < mhc::boundary_chunks(h->hidden, block, true)) continue;
+    L.lane_elems = el;
+    L.block_n = bn;
+    L.max_wgs_per_xcd_n = wn;
+    break;
   }
 }
 
@@ -231,7 +233,7 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   h->block = kDefaultBlock;
   h->spin_limit = kDefaultSpinLimit;
   h->scale_layout = MHC_SCALE_ROW_MAJOR;
-  h->lane_elems = 4;
+  h->lane_elems = 2;
   h->pending = false;
   h->slot_stride = mhc::boundary_chunks(hidden, kMinBlock, true);  // the most chunks per row
   int cus = 0;
@@ -326,7 +328,7 @@ int mhc_set_option(mhc_handle h, int option, int value) {
       h->spin_limit = value;
       return MHC_OK;
     case MHC_OPT_LANE_ELEMS:
-      if (value != 8 && value != 4) return MHC_ERR_SHAPE;
+      if (value != 8 && value != 4 && value != 2) return MHC_ERR_SHAPE;
       h->lane_elems = value;
       return MHC_OK;
     case MHC_OPT_SCALE_LAYOUT:

@@ -275,7 +275,7 @@ __device__ __forceinline__ void boundary_item_quad(const BoundaryParams& p,
   if constexpr (DEFER) __syncthreads();  // s_coef is rewritten for the next row
 }
 
-// One lane per vector of EL consecutive elements (EL = 8: 16-byte vectors, EL = 4: 8-byte
+// One lane per vector of EL consecutive elements (EL = 8, 4 or 2: 16-, 8- or 4-byte
 // vectors): the lane owns those elements of the row and all four streams of them (BS
 // vectors per workgroup). Same dataflow and handoff as the quad layout above.
 template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8, int MODE, bool DEFER, int EL>
@@ -291,8 +291,9 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  static_assert(EL == 8 || EL == 4, "a lane holds 8 or 4 elements");
-  using Vec = typename std::conditional<EL == 8, uint4, uint2>::type;
+  static_assert(EL == 8 || EL == 4 || EL == 2, "a lane holds 8, 4 or 2 elements");
+  using Vec = typename std::conditional<
+      EL == 8, uint4, typename std::conditional<EL == 4, uint2, uint32_t>::type>::type;
   const int nv = p.hv * (8 / EL);  // vectors per row
   const Vec* xp = reinterpret_cast<const Vec*>(p.xp);
   const Vec* gp = reinterpret_cast<const Vec*>(p.g);
@@ -522,7 +523,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   store_nt(layer_out + (size_t)r * nv + v, ob);
   if constexpr (MXFP8) {
     // 32-element block = the 32 / EL consecutive lanes holding vectors v & ~(32/EL - 1) ..
-    // (a quad at EL = 8, two quads at EL = 4)
+    // (a quad at EL = 8, two quads at EL = 4, a 16-lane DPP row at EL = 2)
     constexpr int kPerBlock = 32 / EL;
     float q[EL];
     unpack_bf16(ob, q);
@@ -531,16 +532,21 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     for (int e = 0; e < EL; ++e) amax = fmaxf(amax, fabsf(q[e]));
     amax = fmaxf(amax, dpp_f32<kDppQuadXor1>(amax));
     amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
-    if constexpr (EL == 4) amax = fmaxf(amax, swizzle_xor4(amax));
+    if constexpr (EL <= 4) amax = fmaxf(amax, swizzle_xor4(amax));
+    if constexpr (EL == 2) amax = fmaxf(amax, dpp_f32<kDppRowRor8>(amax));  // xor 8 in a row
     const int ex = e8m0_exponent(__float_as_uint(amax));
     const float sc = __uint_as_float((uint32_t)(127 - ex) << 23);
     // |q| * 2^-e <= 448 by the choice of e: in range, exact scaling
-    const uint32_t lo = cvt_pk4_e4m3(q[0] * sc, q[1] * sc, q[2] * sc, q[3] * sc);
     if constexpr (EL == 8) {
+      const uint32_t lo = cvt_pk4_e4m3(q[0] * sc, q[1] * sc, q[2] * sc, q[3] * sc);
       const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
       store_nt(p.mx_data + (size_t)r * p.hv + v, make_uint2(lo, hi));
-    } else {
+    } else if constexpr (EL == 4) {
+      const uint32_t lo = cvt_pk4_e4m3(q[0] * sc, q[1] * sc, q[2] * sc, q[3] * sc);
       store_nt(reinterpret_cast<uint32_t*>(p.mx_data) + (size_t)r * nv + v, lo);
+    } else {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0] * sc, q[1] * sc, 0, false);
+      store_nt(reinterpret_cast<uint16_t*>(p.mx_data) + (size_t)r * nv + v, (uint16_t)lo);
     }
     if ((v & (kPerBlock - 1)) == 0)
       p.mx_scale[mx_scale_offset(r, v / kPerBlock, p.hidden / 32, p.scale_kt)] =
@@ -624,6 +630,15 @@ static hipError_t launch_one(const BoundaryParams& p, const DeferParams& d, int 
 template <int BS, bool DEFER>
 static hipError_t launch_mix(const BoundaryParams& p, const DeferParams& d, bool fin, bool pre,
                              bool mx, int el, int grid, hipStream_t st) {
+  if constexpr (BS == 512) {
+    if (el == 2 && pre) {  // two elements per lane (the layer-input kernels)
+      if (!fin)
+        return mx ? launch_one<BS, false, true, true, kBoundaryMix, DEFER, 2>(p, d, grid, st)
+                  : launch_one<BS, false, true, false, kBoundaryMix, DEFER, 2>(p, d, grid, st);
+      return mx ? launch_one<BS, true, true, true, kBoundaryMix, DEFER, 2>(p, d, grid, st)
+                : launch_one<BS, true, true, false, kBoundaryMix, DEFER, 2>(p, d, grid, st);
+    }
+  }
   if constexpr (BS >= 256) {
     if (el == 4 && pre) {  // four elements per lane (the layer-input kernels)
       if (!fin)
@@ -646,6 +661,11 @@ static hipError_t launch_mix(const BoundaryParams& p, const DeferParams& d, bool
 template <int BS>
 static hipError_t launch_bs(const BoundaryParams& p, const DeferParams& d, bool fin, bool pre,
                             bool mx, int mode, bool defer, int el, int grid, hipStream_t st) {
+  if constexpr (BS == 512) {
+    if (el == 2 && mode == kBoundaryHead)
+      return mx ? launch_one<BS, false, true, true, kBoundaryHead, false, 2>(p, d, grid, st)
+                : launch_one<BS, false, true, false, kBoundaryHead, false, 2>(p, d, grid, st);
+  }
   if constexpr (BS >= 256) {
     if (el == 4 && mode == kBoundaryHead)
       return mx ? launch_one<BS, false, true, true, kBoundaryHead, false, 4>(p, d, grid, st)
@@ -695,6 +715,17 @@ static int occupancy_bs() {
     n = min(n, occupancy_one<BS, true, true, true, kBoundaryMix, true, 4>());
     n = min(n, occupancy_one<BS, false, true, true, kBoundaryHead, false, 4>());
   }
+  if constexpr (BS == 512) {
+    n = min(n, occupancy_one<BS, false, true, false, kBoundaryMix, false, 2>());
+    n = min(n, occupancy_one<BS, false, true, true, kBoundaryMix, false, 2>());
+    n = min(n, occupancy_one<BS, true, true, false, kBoundaryMix, false, 2>());
+    n = min(n, occupancy_one<BS, true, true, true, kBoundaryMix, false, 2>());
+    n = min(n, occupancy_one<BS, false, true, false, kBoundaryMix, true, 2>());
+    n = min(n, occupancy_one<BS, false, true, true, kBoundaryMix, true, 2>());
+    n = min(n, occupancy_one<BS, true, true, false, kBoundaryMix, true, 2>());
+    n = min(n, occupancy_one<BS, true, true, true, kBoundaryMix, true, 2>());
+    n = min(n, occupancy_one<BS, false, true, true, kBoundaryHead, false, 2>());
+  }
   return n;
 }
 
@@ -742,22 +773,22 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
     if (rpr < 1) rpr = 1;
     return rpr > row_blocks ? row_blocks : rpr;
   };
-  // four elements per lane where asked for (the kernels that write a layer input, at 256 or
-  // 512 threads: the same chunks as `block` at eight), unless the larger workgroups would
-  // take more rounds (measured: a second round costs more than the shorter per-lane work
-  // saves). Deferred and undeferred calls choose alike, so their results stay bit-identical.
-  // Not the first layer's entry, which has almost no arithmetic to share (measured 4.19 at
-  // eight against 4.22 us at four per lane, 32 rows).
+  // fewer elements per lane where asked for (the kernels that write a layer input, at
+  // block_n = block * 8 / lane_elems threads: the same chunks as `block` at eight), unless
+  // the larger workgroups would take more rounds (measured: a second round costs more than
+  // the shorter per-lane work saves). Deferred and undeferred calls choose alike, so their
+  // results stay bit-identical. Not the first layer's entry, which has almost no arithmetic
+  // to share (measured 4.19 at eight against 4.22 us at four per lane, 32 rows).
   const int chunks8 = boundary_chunks(L.hidden, pre ? L.block : kResidualOnlyBlock, pre);
-  bool use4 = L.lane_elems == 4 && pre && L.mode != kBoundaryFirst && L.block4 >= 256;
-  if (use4) {
+  bool narrow = L.lane_elems < 8 && pre && L.mode != kBoundaryFirst && L.block_n >= 256;
+  if (narrow) {
     const int r8 = rows_per_round(L.max_wgs_per_xcd, chunks8);
-    const int r4 = rows_per_round(L.max_wgs_per_xcd4, chunks8);
-    use4 = (row_blocks + r4 - 1) / r4 <= (row_blocks + r8 - 1) / r8;
+    const int rn = rows_per_round(L.max_wgs_per_xcd_n, chunks8);
+    narrow = (row_blocks + rn - 1) / rn <= (row_blocks + r8 - 1) / r8;
   }
-  const int el = use4 ? 4 : 8;
-  const int block = !pre ? kResidualOnlyBlock : (use4 ? L.block4 : L.block);
-  const int max_wgs_per_xcd = use4 ? L.max_wgs_per_xcd4 : L.max_wgs_per_xcd;
+  const int el = narrow ? L.lane_elems : 8;
+  const int block = !pre ? kResidualOnlyBlock : (narrow ? L.block_n : L.block);
+  const int max_wgs_per_xcd = narrow ? L.max_wgs_per_xcd_n : L.max_wgs_per_xcd;
   p.chunks = chunks8;
   p.layer_out = reinterpret_cast<uint4*>(L.layer_input_out);
   p.mx_data = reinterpret_cast<uint2*>(L.mx_data_out);

@@ -37,6 +37,14 @@ __device__ __forceinline__ void store_nt(uint32_t* p, uint32_t v) {
   __builtin_nontemporal_store(v, p);
 }
 
+// 4-byte load with the non-temporal hint (two bf16 values).
+__device__ __forceinline__ uint32_t load_nt(const uint32_t* p) {
+  return __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ void store_nt(uint16_t* p, uint16_t v) {
+  __builtin_nontemporal_store(v, p);
+}
+
 // 8-byte load with the non-temporal hint (four bf16 values).
 __device__ __forceinline__ uint2 load_nt(const uint2* p) {
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
@@ -86,7 +94,13 @@ __device__ __forceinline__ void unpack_bf16(const uint2& v, float (&f)[4]) {
   f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
   f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
 }
+__device__ __forceinline__ void unpack_bf16(const uint32_t& v, float (&f)[2]) {
+  f[0] = bf16_lo(v); f[1] = bf16_hi(v);
+}
 __device__ __forceinline__ uint4 pack_bf16(const float (&f)[8]) { return pack8_round(f); }
+__device__ __forceinline__ uint32_t pack_bf16(const float (&f)[2]) {
+  return cvt_pk_bf16(f[0], f[1]);
+}
 __device__ __forceinline__ uint2 pack_bf16(const float (&f)[4]) {
   return make_uint2(cvt_pk_bf16(f[0], f[1]), cvt_pk_bf16(f[2], f[3]));
 }

@@ -40,11 +40,11 @@ struct BoundaryLaunch {
   int spin_limit;
   int max_wgs_per_xcd;          // resident workgroups of this block size on one XCD
   int block;                    // 128, 256 or 512 threads per workgroup (layer-input kernels)
-  int lane_elems;               // 4: the kernels that write a layer input run four elements
-                                // per lane at block4
-                                // threads (twice block, the same chunks per row); else 8
-  int block4;
-  int max_wgs_per_xcd4;         // resident workgroups of block4 threads on one XCD
+  int lane_elems;               // 4 or 2: the kernels that write a layer input run that many
+                                // elements per lane at block_n = block * 8 / lane_elems threads
+                                // (the same chunks per row); 8: block, eight per lane
+  int block_n;
+  int max_wgs_per_xcd_n;        // resident workgroups of block_n threads on one XCD
   int mode;                     // kBoundaryMix, kBoundaryFirst or kBoundaryHead
   // deferred coefficients (mix mode): post, comb and pre are computed in the kernel from a
   // pending coefficient call's split-K partials, and written to post/comb/pre by the
