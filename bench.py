@@ -182,7 +182,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path has no "
-              "collectives; see DESIGN.md for how it would shard.", file=sys.stderr)
+              "collectives: each GPU would run this kernel on its own tensor-parallel share after "
+              "an exchange of the partial slices.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
