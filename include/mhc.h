@@ -121,8 +121,8 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
  *     vectors, 4: 8-byte, 2: 4-byte) a workgroup has 8 / e times the threads of the
  *     eight-per-thread size, so a row keeps the same number of workgroups. A call takes the
  *     fewest e >= the option whose workgroup exists (at most 512 threads) and fits the
- *     co-residency limit, if the block size is chosen per call and the call then needs no
- *     more rounds than at 8; otherwise 8. The new streams are identical for every e (every
+ *     co-residency limit, if the block size is chosen per call, the call has at most 128
+ *     rows and it then needs no more rounds than at 8; otherwise 8. The new streams are identical for every e (every
  *     element's arithmetic is the same); the row's sum of squares is added in another
  *     order, so the layer input may differ in the last bit of rare elements. Other values:
  *     MHC_ERR_SHAPE.

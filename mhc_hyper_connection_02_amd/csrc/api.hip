@@ -19,6 +19,11 @@ constexpr int kMinBlock = 128;      // smallest boundary workgroup: the most chu
 constexpr int kDefaultBlock = 128;   // up to kSmallRows rows
 constexpr int kManyRowsBlock = 256;
 constexpr int kSmallRows = 32;
+// Fewer elements per lane pay while the call has few waves per SIMD (measured at hidden
+// 7168, boundary + MXFP8: 8 rows 4.90 against 5.29 us, 128 rows 8.72 against 8.83); above
+// this many rows the arithmetic is hidden by other waves and the extra waves cost (256
+// rows 16.74 against 16.41, 512 rows 29.30 against 28.93)
+constexpr int kNarrowMaxRows = 128;
 constexpr int kMaxChunks = 64;      // one polling lane per chunk
 constexpr int kMaxHidden = 65536;   // chunks per row at the largest block stay <= one wave
 constexpr int kDefaultSpinLimit = 1 << 20;
@@ -135,7 +140,7 @@ void fill_mix(const mhc_ctx* h, mhc::BoundaryLaunch& L, const uint16_t* residual
   L.lane_elems = 8;
   L.block_n = 0;
   L.max_wgs_per_xcd_n = 0;
-  for (int el = h->lane_elems; el < 8 && !h->block_set; el *= 2) {
+  for (int el = h->lane_elems; el < 8 && !h->block_set && rows <= kNarrowMaxRows; el *= 2) {
     const int bn = block * (8 / el);
     if (block_index(bn) < 0) continue;
     const int wn = h->wgs_per_xcd[block_index(bn)];
