@@ -87,10 +87,11 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
                mhc_handle* out);
 
 /*
- * mhc_set_option -- knobs of a handle. Results do not depend on the first two
- * (except that a spin limit too small to cover the row handoff makes it give up,
- * see above); the third chooses where the MXFP8 scale bytes go. Takes effect for
- * calls issued afterwards.
+ * mhc_set_option -- knobs of a handle; none changes what is computed. The block size
+ * and the elements per lane change the order in which a row's sum of squares is added
+ * (the layer input may differ in the last bit of rare elements); a spin limit too small
+ * to cover the row handoff makes it give up (see above); the scale layout chooses where
+ * the MXFP8 scale bytes go. Takes effect for calls issued afterwards.
  *   MHC_OPT_BOUNDARY_BLOCK: threads per workgroup of the boundary kernels that write a
  *     layer input, 128, 256 or 512, for every call and row count (default: chosen
  *     per call from the row count, see mhc_create). Each thread owns 8 hidden
@@ -122,9 +123,8 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
  *     eight-per-thread size, so a row keeps the same number of workgroups. A call takes the
  *     fewest e >= the option whose workgroup exists (at most 512 threads) and fits the
  *     co-residency limit, if the block size is chosen per call, the call has at most 128
- *     rows and it then needs no more rounds than at 8; otherwise 8. The new streams are identical for every e (every
- *     element's arithmetic is the same); the row's sum of squares is added in another
- *     order, so the layer input may differ in the last bit of rare elements. Other values:
+ *     rows and it then needs no more rounds than at 8; otherwise 8. The new streams are
+ *     identical for every e (every element's arithmetic is the same). Other values:
  *     MHC_ERR_SHAPE.
  * Unknown options: MHC_ERR_INVALID_ARG.
  */
