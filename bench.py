@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 COPY_CALIBRATION_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "boundary_decode_r32_h7168_traffic.json")
-KERNEL_SOURCES = ["boundary.hip", "device_common.h"]
+KERNEL_SOURCES = ["boundary.hip", "device_common.h", "kernels.h"]
 
 
 def parse():

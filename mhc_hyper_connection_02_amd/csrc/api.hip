@@ -33,7 +33,7 @@ constexpr int kTileMaxRows = 1024;  // rows of the fused boundary + coefficient 
 
 struct mhc_ctx {
   int hidden, hc_mult, max_rows, max_tp, top_k, device;
-  int slot_stride;         // handoff words per row (chunks at the smallest block)
+  int slot_stride;         // handoff words per row (chunks at the smallest block, padded)
   int block;               // layer-input workgroup size for up to kSmallRows rows (auto)
   int block_many;          // ... for more rows (auto)
   int block_set;           // the size MHC_OPT_BOUNDARY_BLOCK set, 0: automatic
@@ -240,7 +240,10 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   h->scale_layout = MHC_SCALE_ROW_MAJOR;
   h->lane_elems = 2;
   h->pending = false;
-  h->slot_stride = mhc::boundary_chunks(hidden, kMinBlock, true);  // the most chunks per row
+  // the most chunks per row, rounded up to 16 words: each row's handoff words on a
+  // 128-byte line of their own (rows sharing a line, from different XCDs, measured
+  // 0.25 us slower per call: 5.35 against 5.08 us for 32 rows at hidden 7168)
+  h->slot_stride = (mhc::boundary_chunks(hidden, kMinBlock, true) + 15) / 16 * 16;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
       cus < 8) {
@@ -279,7 +282,7 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
                      : 0;
 
   const size_t slot_bytes = round_up((size_t)max_rows * h->slot_stride * 8, 256);
-  const size_t epoch_bytes = round_up((size_t)max_rows * 4, 256);
+  const size_t epoch_bytes = round_up((size_t)max_rows * mhc::kEpochStride * 4, 256);
   const size_t err_bytes = 256;
   const size_t tile_bytes = round_up(mhc::boundary_tile_words(h->tile_rows, hidden) * 8, 256);
   const size_t pre_bytes = round_up(pre_floats * sizeof(float), 256);

@@ -82,7 +82,7 @@ struct BoundaryParams {
   uint8_t* mx_scale;        // [rows][hidden / 32] or swizzled (scale_kt)
   // row-RMS handoff
   unsigned long long* slots;  // [max_rows][slot_stride]
-  unsigned* epoch;            // [max_rows]
+  unsigned* epoch;            // [max_rows][kEpochStride]
   unsigned* errors;           // [1]
   int slot_stride;
   int rows_per_round;         // rows per XCD per round
@@ -310,7 +310,8 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   // so that its latency hides under the data loads
   unsigned epoch_now = 0;
   if constexpr (HAS_PRE)
-    epoch_now = __hip_atomic_load(p.epoch + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    epoch_now = __hip_atomic_load(p.epoch + (size_t)r * kEpochStride, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
 
   float x[EL];
 #pragma unroll
@@ -509,7 +510,9 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
       tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), k));
     if (lane == 0) {
       *s_inv = 1.0f / sqrtf(tot / (float)p.hidden + p.eps);
-      if (c == 0) __hip_atomic_store(p.epoch + r, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (c == 0)
+        __hip_atomic_store(p.epoch + (size_t)r * kEpochStride, want, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   __syncthreads();

@@ -107,7 +107,7 @@ struct TileParams {
   // handoff
   unsigned long long* words;  // y^2 words [tiles][chunks][16], then coefficient words
                               // [tiles][chunks][16][25]
-  unsigned* epoch;            // [max_rows]
+  unsigned* epoch;            // [max_rows][kEpochStride]
   unsigned* errors;
   int tile_cap, tiles_per_round, rounds, spin_limit;  // tile_cap: tiles of the scratch
 };
@@ -228,7 +228,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   // out-of-range lanes are dropped later): a load behind a lane-dependent branch makes the
   // compiler wait for it before going on, which serializes the loads.
   // the rows' epochs (the call tag), kept in a register until the loads are issued
-  const unsigned epoch_now = __hip_atomic_load(p.epoch + min(row0 + (tid & 15), p.rows - 1),
+  const unsigned epoch_now = __hip_atomic_load(p.epoch + (size_t)min(row0 + (tid & 15), p.rows - 1) * kEpochStride,
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // --- DEFER_IN: the pending call's partial sums of this lane's row (the half wave's), value
@@ -535,7 +535,8 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
     const float tot = half_wave_sum(part);
     inv = 1.0f / sqrtf(tot / (float)(p.hv * 8) + p.eps);
     if (c == 0 && row_ok && vl == 0)
-      __hip_atomic_store(p.epoch + r, S.want[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.epoch + (size_t)r * kEpochStride, S.want[m], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // --- the next coefficients of rows c, c + chunks, ... (row j on wave j % 8), before that
