@@ -157,7 +157,13 @@ struct PreEpilogueParams {
 };
 
 __global__ __launch_bounds__(kWave) void pre_epilogue_kernel(const PreEpilogueParams p) {
-  const int r = blockIdx.x;
+  // rows dealt to the 8 XCDs in contiguous ranges (when the row count allows): XCD x then
+  // finishes the rows whose partials the split-K kernel wrote from XCD x at 128 rows (read
+  // from its own L2), and its outputs do not share lines with other XCDs' (measured 0.4 us
+  // less per 128-row call; the same at 64 rows)
+  const int nb = (int)gridDim.x;
+  const int r = (nb % 8 == 0) ? ((int)blockIdx.x % 8) * (nb / 8) + (int)blockIdx.x / 8
+                              : (int)blockIdx.x;
   const int L = threadIdx.x;
   float sc_l, base_l;
   coeff_lane_scale_base(p.e, L, &sc_l, &base_l);  // early: they arrive with the partials
