@@ -162,3 +162,52 @@ def test_mxfp8_codes_and_scales_at_format_edges_are_bit_exact():
     bad = np.argwhere(g != o)
     assert bad.size == 0, (f"{len(bad)} E4M3 codes differ; first at {tuple(bad[0])}: gpu "
                            f"{g[tuple(bad[0])]:#04x} oracle {o[tuple(bad[0])]:#04x}")
+
+
+def test_hand_derived_sum_and_rounding_of_x_bit_exact(golden_dir):
+    """The hand-derived cases of tests/golden/post_rounding_points.json: the slices are
+    summed (not averaged) and the sum is rounded to bf16 before post * x, so the new streams
+    equal the fixture's bits exactly, through the boundary, residual-only and finalize."""
+    import json
+    import os
+    with open(os.path.join(golden_dir, "post_rounding_points.json")) as f:
+        g = json.load(f)
+    n, H = 4, 1024
+    rng = np.random.default_rng(17)
+    for case in g["cases"]:
+        parts = [eval(e, {}) for e in case["partials_expr"]]  # noqa: S307 (fixture literals)
+        tp = len(parts)
+        say(f"case: hand-derived post rounding '{case['name']}' tp={tp} hidden={H}")
+        xp = np.stack([np.full((1, H), int(codecs.f64_to_bf16_bits(np.array(v))), np.uint16)
+                       for v in parts])
+        res = codecs.f64_to_bf16_bits(rng.normal(0, 1, (1, n, H)))
+        post = np.array([case["post"]], np.float32)
+        comb = np.zeros((1, n, n), np.float32)
+        pre = np.full((1, n), 0.25, np.float32)
+        w = codecs.f64_to_bf16_bits(np.ones(H))
+        want = np.repeat(np.array([int(b, 16) for b in case["stream_bits"]], np.uint16)[:, None],
+                         H, axis=1)
+        h = handle_for(H, 1, tp=tp)
+        full = binding.boundary(h, T(xp), T(res), T(post), T(comb), T(pre), T(w), 1e-6)
+        ro = binding.residual_only(h, T(xp), T(res), T(post), T(comb))
+        assert np.array_equal(N(full["residual"])[0], want), "boundary streams"
+        assert np.array_equal(N(ro)[0], want), "residual-only streams"
+    for case in g["finalize_cases"]:
+        say(f"case: hand-derived finalize rounding '{case['name']}' hidden={H}")
+        val = lambda e: int(codecs.f64_to_bf16_bits(np.array(eval(e, {}))))  # noqa: E731,S307
+        sh = np.full((1, H), val(case["shared_expr"]), np.uint16)
+        gg = np.full((1, H), val(case["g_expr"]), np.uint16)
+        wt = np.array([[case["w"]]], np.float32)
+        idx = np.array([0], np.int32)
+        res = codecs.f64_to_bf16_bits(rng.normal(0, 1, (1, n, H)))
+        post = np.array([case["post"]], np.float32)
+        comb = np.zeros((1, n, n), np.float32)
+        want = np.repeat(np.array([int(b, 16) for b in case["stream_bits"]], np.uint16)[:, None],
+                         H, axis=1)
+        h = handle_for(H, 1, tp=1, top_k=1)
+        for pre in (None, np.full((1, n), 0.25, np.float32)):
+            out = binding.finalize(h, T(gg), T(wt), T(idx), T(sh), T(res), T(post), T(comb),
+                                   None if pre is None else T(pre),
+                                   None if pre is None else T(codecs.f64_to_bf16_bits(np.ones(H))),
+                                   1e-6)
+            assert np.array_equal(N(out["residual"])[0], want), f"finalize streams pre={pre is not None}"

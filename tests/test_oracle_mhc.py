@@ -37,6 +37,68 @@ def test_tp_reduce_order_invariant_and_single_slice_copy():
     assert np.array_equal(oracle.tp_reduce(xp[:1]), dec(xp[0]))
 
 
+def _golden_post_rounding(golden_dir):
+    with open(os.path.join(golden_dir, "post_rounding_points.json")) as f:
+        return json.load(f)
+
+
+def _bits(hexes):
+    return np.array([int(h, 16) for h in hexes], np.uint16)
+
+
+def _flat_row(values, H=64):
+    """bf16 bits of one row per value, every hidden element equal: [len(values), 1, H]."""
+    return np.stack([np.full((1, H), int(bf(np.array(float(v)))), np.uint16) for v in values])
+
+
+def test_tp_reduce_hand_derived_sums(golden_dir):
+    """The slices are summed, not averaged (boundary page, module docstring): exact dyadic
+    sums of two and three slices, hand-derived in the fixture."""
+    g = _golden_post_rounding(golden_dir)
+    for case in g["cases"]:
+        parts = [eval(e, {}) for e in case["partials_expr"]]  # noqa: S307 (fixture literals)
+        xp = _flat_row(parts)
+        got = oracle.tp_reduce(xp)
+        assert got.shape == (1, 64)
+        assert np.all(got == eval(case["x_expr"], {})), case["name"]  # noqa: S307
+
+
+def test_post_reads_the_bf16_rounded_sum_hand_derived(golden_dir):
+    """D3: the new streams are bf16(post * bf16(x)) with x the exact sum of the slices, on
+    inputs where skipping the rounding of x, or a mean instead of the sum, changes output
+    bits (boundary page, Boundaries.post_only: the post kernel reads the reduced bf16
+    tensor). Expected streams are the fixture's hand-derived bits."""
+    g = _golden_post_rounding(golden_dir)
+    n, H = 4, 64
+    rng = np.random.default_rng(5)
+    for case in g["cases"]:
+        parts = [eval(e, {}) for e in case["partials_expr"]]  # noqa: S307
+        xp = _flat_row(parts, H)
+        res = bf(rng.normal(0, 1, (1, n, H)))
+        post = np.array([case["post"]], np.float32)
+        comb = np.zeros((1, n, n), np.float32)
+        want = _bits(case["stream_bits"])
+        for out in (oracle.residual_only(xp, res, post, comb),
+                    oracle.boundary(xp, res, post, comb, np.full((1, n), 0.25, np.float32),
+                                    bf(np.ones(H)), 1e-6)["residual"]):
+            assert np.array_equal(out[0], np.repeat(want[:, None], H, axis=1)), case["name"]
+        # the fixture's alternatives are real alternatives: each slip changes some stream
+        assert not np.array_equal(_bits(case["if_mean_bits"]), want)
+        if case["partials_expr"] != ["1.5", "2.25", "-0.75"]:
+            assert not np.array_equal(_bits(case["if_unrounded_bits"]), want)
+    for case in g["finalize_cases"]:
+        sh = np.full((1, H), int(bf(np.array(eval(case["shared_expr"], {})))), np.uint16)  # noqa: S307
+        gg = np.full((1, H), int(bf(np.array(eval(case["g_expr"], {})))), np.uint16)  # noqa: S307
+        w = np.array([[case["w"]]], np.float32)
+        idx = np.array([0], np.int32)
+        res = bf(rng.normal(0, 1, (1, n, H)))
+        post = np.array([case["post"]], np.float32)
+        out = oracle.finalize(gg, w, idx, sh, res, post, np.zeros((1, n, n), np.float32), None,
+                              None, 0.0)["residual"]
+        want = _bits(case["stream_bits"])
+        assert np.array_equal(out[0], np.repeat(want[:, None], H, axis=1)), case["name"]
+
+
 def test_finalize_sum_brute_force():
     d = synth.finalize_inputs(1, rows=3, hidden=64, top_k=2)
     g, w, idx, sh = (d["gemm2_permuted"], d["expert_weights"],
