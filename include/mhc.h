@@ -31,9 +31,16 @@
  *     wait between the workgroups of that row, which the library keeps
  *     co-resident (a launch uses at most half of the device's
  *     resident-workgroup capacity, in rounds if needed). A wait that
- *     exceeds the spin limit gives up, counts itself in the handle's error
- *     word (see mhc_get_errors) and the call's layer input is then wrong;
- *     nothing hangs.
+ *     exceeds the spin limit gives up and counts itself in the handle's error
+ *     word (see mhc_get_errors); nothing hangs. The failure shows in the data:
+ *     the part of the layer input whose wait gave up is NaN (bf16 NaN, E4M3
+ *     NaN codes, E8M0 scale byte 0xFF), and so are the next coefficients of a
+ *     fused call's row whose wait gave up. Such a row is marked in the handle
+ *     (a late workgroup of the call that gave up may have left a handoff word
+ *     that a later call would accept): every later call skips that row's
+ *     waits and writes its wait-dependent outputs as NaN, until mhc_reset (or
+ *     mhc_get_errors with clear) restores the handoff state. The new streams
+ *     never depend on a wait and stay exact.
  *   - The only aliasing allowed is residual_out == residual (in-place update
  *     of the streams); any other overlap of inputs and outputs is undefined.
  *   - Alignment: bf16 tensors 16 bytes; fp32 and int32 tensors 4 bytes;
@@ -153,8 +160,10 @@ int mhc_mxfp8_scale_bytes(int rows, int hidden, int layout, uint64_t* bytes);
  * mhc_get_errors -- the number of row-handoff waits that gave up since the
  * handle was created or last cleared. Enqueues a device-to-host copy of the
  * error word on `stream` and waits for that stream (so it follows every call
- * issued before it on `stream`); with clear != 0, then zeroes the word on
- * `stream`. count must be a host pointer.
+ * issued before it on `stream`); with clear != 0, then re-zeroes the whole
+ * handoff state on `stream` as mhc_reset does (the error word alone is not
+ * enough: a count above zero means stale handoff words may be left behind).
+ * count must be a host pointer.
  */
 int mhc_get_errors(mhc_handle h, unsigned* count, int clear, mhc_stream_t stream);
 
@@ -168,7 +177,8 @@ int mhc_destroy(mhc_handle h);
  * all_reduce page, BoundaryAllReduce.reset: drop what an aborted step left
  * behind. Completed calls leave the handoff state consistent by themselves;
  * this is only needed after a call whose kernels did not complete or whose
- * waits gave up.
+ * waits gave up, and then it is required: until it runs, every call writes
+ * its wait-dependent outputs as NaN (see the conventions above).
  */
 int mhc_reset(mhc_handle h, mhc_stream_t stream);
 
@@ -391,7 +401,7 @@ typedef struct mhc_coeff_args {
  * workgroups, which wait on one another. Kernels of other streams only delay it, but two
  * of these calls running at the same time on different streams can each hold part of an
  * XCD and wait for the rest: their waits then end at the spin limit (counted by
- * mhc_get_errors) with wrong results. Issue fused calls of one device on one stream.
+ * mhc_get_errors) with NaN outputs. Issue fused calls of one device on one stream.
  */
 int mhc_boundary_coeffs(mhc_handle h, const uint16_t* x_partials, int tp,
                         const uint16_t* residual, const float* post, const float* comb,

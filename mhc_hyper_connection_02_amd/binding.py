@@ -17,7 +17,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmhc_amd.so")
-HEADER = os.path.join(os.path.dirname(_PKG), "include", "mhc.h")
+INCLUDE = os.path.join(os.path.dirname(_PKG), "include")
+HEADER = os.path.join(INCLUDE, "mhc.h")
 
 MHC_OK = 0
 MHC_OPT_BOUNDARY_BLOCK = 1
@@ -64,14 +65,22 @@ _SIGS = {
                              ctypes.POINTER(CoeffArgs), _vp], _i),
     "mhc_finalize_coeffs": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _i, _vp,
                              _vp, _vp, _vp, ctypes.POINTER(CoeffArgs), _vp], _i),
+    # include/mhc_floor.h: measurement floors of the boundary's launch geometry
+    "mhc_floor_boundary_traffic": ([_vp, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp], _i),
+    "mhc_floor_empty": ([_i, _i, _vp], _i),
 }
 
 
-def header_functions(path=HEADER):
-    """Names of the functions include/mhc.h declares."""
-    with open(path) as f:
-        text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mhc_\w+)\s*\(", text, re.M)))
+def header_functions(paths=None):
+    """Names of the functions the headers under include/ declare."""
+    if paths is None:
+        paths = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
+    names = set()
+    for path in paths:
+        with open(path) as f:
+            text = f.read()
+        names.update(re.findall(r"^\s*(?:int|const char\*)\s+(mhc_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def load_library(path=LIB_PATH):
@@ -498,3 +507,31 @@ def finalize_coeffs(h, gemm2_permuted, expert_weights, expanded_idx_to_permuted_
     res = _result(ro, li, md, ms)
     res["next"] = nout
     return res
+
+
+# ---------------------------------------------------------------------------
+# include/mhc_floor.h: what a kernel of the boundary's shape costs without its arithmetic
+# ---------------------------------------------------------------------------
+
+def floor_boundary_traffic(x_partials, residual, residual_out, layer_input_out, mx_data_out,
+                           mx_scale_out, stream=None):
+    """``mhc_floor_boundary_traffic``: the boundary's bytes moved with its geometry, no
+    arithmetic (the outputs' values mean nothing)."""
+    tp, rows, hidden = x_partials.shape
+    dev = x_partials.device
+    _need(x_partials, "x_partials", torch.bfloat16, (tp, rows, hidden), dev)
+    _need(residual, "residual", torch.bfloat16, (rows, 4, hidden), dev)
+    _need(residual_out, "residual_out", torch.bfloat16, (rows, 4, hidden), dev)
+    _need(layer_input_out, "layer_input_out", torch.bfloat16, (rows, hidden), dev)
+    _need(mx_data_out, "mx_data_out", torch.uint8, (rows, hidden), dev)
+    _need(mx_scale_out, "mx_scale_out", torch.uint8, (rows, hidden // 32), dev)
+    _check(load_library().mhc_floor_boundary_traffic(
+        _ptr(x_partials), tp, _ptr(residual), rows, hidden, _ptr(residual_out),
+        _ptr(layer_input_out), _ptr(mx_data_out), _ptr(mx_scale_out), _stream(stream)),
+        "mhc_floor_boundary_traffic")
+
+
+def floor_empty(rows, hidden, stream=None):
+    """``mhc_floor_empty``: an empty kernel of the same grid."""
+    _check(load_library().mhc_floor_empty(int(rows), int(hidden), _stream(stream)),
+           "mhc_floor_empty")

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmhc_amd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["api.hip", "boundary.hip", "boundary_tile.hip", "pre_coeffs.hip"]
+SOURCES = ["api.hip", "boundary.hip", "boundary_tile.hip", "pre_coeffs.hip", "floor.hip"]
 ARCH = "gfx950"
 
 

@@ -372,7 +372,11 @@ int mhc_get_errors(mhc_handle h, unsigned* count, int clear, mhc_stream_t stream
   if (hipMemcpyAsync(count, h->errors, sizeof(unsigned), hipMemcpyDeviceToHost, s) != hipSuccess)
     return MHC_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return MHC_ERR_HIP;
-  if (clear) return launch_status(mhc::launch_fill_u32(h->errors, 1, 0u, s));
+  // a count above zero may leave stale handoff words behind: clearing it re-zeroes the
+  // whole handoff state, as mhc_reset does
+  if (clear)
+    return launch_status(mhc::launch_fill_u32(reinterpret_cast<unsigned*>(h->scratch),
+                                              h->zero_words, 0u, s));
   return MHC_OK;
 }
 

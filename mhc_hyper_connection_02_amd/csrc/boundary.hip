@@ -306,12 +306,16 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   const bool active = v < nv;
   const int va = active ? v : 0;
 
-  // the row's epoch (wave 0 runs the handoff), read by every wave without a branch, first,
-  // so that its latency hides under the data loads
-  unsigned epoch_now = 0;
-  if constexpr (HAS_PRE)
-    epoch_now = __hip_atomic_load(p.epoch + (size_t)r * kEpochStride, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
+  // the row's epoch and poison flag (wave 0 runs the handoff), read by every wave without a
+  // branch, first, so that their latency hides under the data loads
+  unsigned epoch_now = 0, poisoned = 0;
+  if constexpr (HAS_PRE) {
+    const unsigned long long ew = __hip_atomic_load(
+        reinterpret_cast<const unsigned long long*>(p.epoch + (size_t)r * kEpochStride),
+        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    epoch_now = (unsigned)ew;
+    poisoned = (unsigned)(ew >> 32);
+  }
 
   float x[EL];
 #pragma unroll
@@ -490,8 +494,12 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
       const unsigned long long word = ((unsigned long long)want << 32) | __float_as_uint(part);
       __hip_atomic_store(row_slots + c, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // a row whose wait gave up once (a late workgroup of that call may have left a word with
+    // a tag a later call wants) trusts no word until mhc_reset: the wait is skipped and the
+    // layer input poisoned
+    bool failed = poisoned != 0;
     float val = 0.f;
-    if (lane < p.chunks) {
+    if (lane < p.chunks && !failed) {
       unsigned long long wd;
       int spins = 0;
       for (;;) {
@@ -499,6 +507,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
         if ((unsigned)(wd >> 32) == want) break;
         if (++spins > p.spin_limit) {
           __hip_atomic_fetch_add(p.errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          failed = true;
           break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -508,6 +517,15 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     float tot = 0.f;
     for (int k = 0; k < p.chunks; ++k)  // chunk order
       tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), k));
+    // a wait that gave up makes this workgroup's share of the layer input NaN (and its
+    // MXFP8 scales the E8M0 NaN byte), so that the failure shows in the data, and marks the
+    // row (word 1 of its epoch line) for the calls after it
+    if (__ballot(failed) != 0) {
+      tot = __builtin_nanf("");
+      if (lane == 0 && !poisoned)
+        __hip_atomic_store(p.epoch + (size_t)r * kEpochStride + 1, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (lane == 0) {
       *s_inv = 1.0f / sqrtf(tot / (float)p.hidden + p.eps);
       if (c == 0)
@@ -553,7 +571,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     }
     if ((v & (kPerBlock - 1)) == 0)
       p.mx_scale[mx_scale_offset(r, v / kPerBlock, p.hidden / 32, p.scale_kt)] =
-          (uint8_t)(ex + 127);
+          inv == inv ? (uint8_t)(ex + 127) : (uint8_t)0xFF;  // NaN: a wait gave up
   }
 }
 

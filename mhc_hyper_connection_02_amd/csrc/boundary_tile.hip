@@ -197,6 +197,7 @@ struct TileShared {
   float red[kTileWaves][kTileRows][kCoefNC];    // per-wave partial logits
   float rowsum[kTileRows][2];                   // per-row sum of y^2, of v^2
   unsigned want[kTileRows];
+  unsigned poisoned[kTileRows];  // the rows' poison flags (a wait of the row gave up)
   float4 cf[kTileRows][kCoefNC / 4];            // a pending call's coefficients (pre|post|comb)
 };
 
@@ -228,8 +229,14 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   // out-of-range lanes are dropped later): a load behind a lane-dependent branch makes the
   // compiler wait for it before going on, which serializes the loads.
   // the rows' epochs (the call tag), kept in a register until the loads are issued
-  const unsigned epoch_now = __hip_atomic_load(p.epoch + (size_t)min(row0 + (tid & 15), p.rows - 1) * kEpochStride,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // with the row's poison flag (word 1 of its epoch line): set once a wait of the row gave
+  // up, after which no handoff word of the row is trusted until mhc_reset (a late workgroup
+  // of that call may have left a word with a tag a later call wants)
+  const unsigned long long ew = __hip_atomic_load(
+      reinterpret_cast<const unsigned long long*>(
+          p.epoch + (size_t)min(row0 + (tid & 15), p.rows - 1) * kEpochStride),
+      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned epoch_now = (unsigned)ew;
 
   // --- DEFER_IN: the pending call's partial sums of this lane's row (the half wave's), value
   // vl (lanes past 24 repeat value 24), first: their wait then leaves the loads below in flight
@@ -427,7 +434,10 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   }
 
   // --- fn slice -> LDS, transposed to [logit][k] (k = stream * 256 + element of the chunk)
-  if (tid < kTileRows) S.want[tid] = epoch_now + 1u;
+  if (tid < kTileRows) {
+    S.want[tid] = epoch_now + 1u;
+    S.poisoned[tid] = (unsigned)(ew >> 32);
+  }
 #pragma unroll
   for (int j = 0; j < kFnVecs; ++j) {
     const int q = tid + j * kTileThreads;
@@ -517,7 +527,8 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   {
     const int cl = vl < p.chunks ? vl : p.chunks - 1;  // lanes past the chunks repeat the last
     float part = 0.f;
-    if (row_ok) {
+    bool failed = S.poisoned[m] != 0;
+    if (row_ok && !failed) {
       const unsigned want = S.want[m];
       unsigned long long w = 0;
       for (int spins = 0;; ++spins) {
@@ -526,13 +537,23 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
         if ((unsigned)(w >> 32) == want) break;
         if (spins >= p.spin_limit) {
           __hip_atomic_fetch_add(p.errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          failed = true;
           break;
         }
         __builtin_amdgcn_s_sleep(1);
       }
       part = vl < p.chunks ? __uint_as_float((unsigned)w) : 0.f;
     }
-    const float tot = half_wave_sum(part);
+    float tot = half_wave_sum(part);
+    // a wait of this row (half wave) that gave up makes its share of the layer input NaN
+    // (and its MXFP8 scales the E8M0 NaN byte)
+    const unsigned long long gave_up = __ballot(failed);
+    if (((lane < 32) ? (gave_up & 0xFFFFFFFFull) : (gave_up >> 32)) != 0) {
+      tot = __builtin_nanf("");
+      if (vl == 0 && row_ok && S.poisoned[m] == 0)
+        __hip_atomic_store(p.epoch + (size_t)r * kEpochStride + 1, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
     inv = 1.0f / sqrtf(tot / (float)(p.hv * 8) + p.eps);
     if (c == 0 && row_ok && vl == 0)
       __hip_atomic_store(p.epoch + (size_t)r * kEpochStride, S.want[m], __ATOMIC_RELAXED,
@@ -549,7 +570,8 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
     if (rc >= p.rows) continue;
     const unsigned want = S.want[rt];
     float acc = 0.f;
-    if (lane < kCoefPartW) {
+    bool failed = S.poisoned[rt] != 0;
+    if (lane < kCoefPartW && !failed) {
       for (int spins = 0;; ++spins) {
         bool ok = true;
         acc = 0.f;
@@ -572,10 +594,18 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
         if (ok) break;
         if (spins >= p.spin_limit) {
           __hip_atomic_fetch_add(p.errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          failed = true;
           break;
         }
         __builtin_amdgcn_s_sleep(1);
       }
+    }
+    // a wait that gave up makes the row's next coefficients NaN and marks the row
+    if (__ballot(failed) != 0) {
+      acc = __builtin_nanf("");
+      if (lane == 0 && S.poisoned[rt] == 0)
+        __hip_atomic_store(p.epoch + (size_t)rc * kEpochStride + 1, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     int slot;
     const float val = coeff_from_sums(coef, lane, acc, sc_l, base_l, &slot);
@@ -608,7 +638,8 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
       if (active) {
         store_nt(p.mx_data + (size_t)r * p.hv + v, make_uint2(lo, hi));
         if ((v & 3) == 0)
-          p.mx_scale[mx_scale_offset(r, v >> 2, p.hv / 4, p.scale_kt)] = (uint8_t)(ex + 127);
+          p.mx_scale[mx_scale_offset(r, v >> 2, p.hv / 4, p.scale_kt)] =
+              inv == inv ? (uint8_t)(ex + 127) : (uint8_t)0xFF;  // NaN: a wait gave up
       }
     }
   }

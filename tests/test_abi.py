@@ -20,7 +20,8 @@ def test_header_declares_the_entry_points():
                  "mhc_residual_only", "mhc_finalize", "mhc_collapse_mean", "mhc_pre_coeffs",
                  "mhc_status_string", "mhc_get_errors", "mhc_first", "mhc_collapse_norm",
                  "mhc_pre_coeffs_deferred", "mhc_pre_coeffs_flush", "mhc_boundary_coeffs",
-                 "mhc_finalize_coeffs", "mhc_mxfp8_scale_bytes"):
+                 "mhc_finalize_coeffs", "mhc_mxfp8_scale_bytes", "mhc_floor_boundary_traffic",
+                 "mhc_floor_empty"):
         assert want in names
 
 
@@ -155,3 +156,22 @@ def test_fused_binding_rejects_bad_arguments(case):
     with pytest.raises(ValueError):
         binding.boundary_coeffs(h, d["x"], d["s"], d["post"], d["comb"], pre, d["w"], 1e-6, nxt,
                                 next_out=next_out)
+
+
+def test_floor_calls_reject_bad_sizes_before_any_device_call():
+    lib = binding.load_library()
+    z = None
+    p = ctypes.c_void_p(256)
+    # shape first (rows, tp, hidden), then null pointers, then alignment; rows == 0 is a no-op
+    assert lib.mhc_floor_boundary_traffic(p, 0, p, 4, 1024, p, p, p, p, z) == 2
+    assert lib.mhc_floor_boundary_traffic(p, 65, p, 4, 1024, p, p, p, p, z) == 2
+    assert lib.mhc_floor_boundary_traffic(p, 8, p, -1, 1024, p, p, p, p, z) == 2
+    assert lib.mhc_floor_boundary_traffic(p, 8, p, 4, 1000, p, p, p, p, z) == 2
+    assert lib.mhc_floor_boundary_traffic(p, 8, p, 4, 16, p, p, p, p, z) == 2
+    assert lib.mhc_floor_boundary_traffic(p, 8, p, 0, 1024, z, z, z, z, z) == 0
+    assert lib.mhc_floor_boundary_traffic(z, 8, p, 4, 1024, p, p, p, p, z) == 1
+    assert lib.mhc_floor_boundary_traffic(p, 8, p, 4, 1024, p, p, p, z, z) == 1
+    assert lib.mhc_floor_boundary_traffic(ctypes.c_void_p(258), 8, p, 4, 1024, p, p, p, p, z) == 3
+    assert lib.mhc_floor_empty(-1, 1024, z) == 2
+    assert lib.mhc_floor_empty(4, 1000, z) == 2
+    assert lib.mhc_floor_empty(0, 1024, z) == 0
