@@ -1,9 +1,10 @@
 """One decode step's boundaries over all layers, on the library's entry points.
 
 decode page, ``SpecializedDecode.run``: the first layer enters through
-``Boundaries.first`` (``mhc_first``: the embedding broadcast to the hc streams, whose
-identity pre-mix selects stream zero, and the first sublayer's normalized input, then
-the coefficient call on the broadcast streams); then each sublayer's output is reduced at the
+``Boundaries.first`` (``mhc_first``: every one of the hc streams starts as a copy of the
+embedding, and since the first pre-mix is the identity on stream 0 the first sublayer's
+input is the embedding normalized; then the coefficient call runs on those copies); then
+each sublayer's output is reduced at the
 next boundary (``Boundaries.sublayer``: the fused kernel, then the coefficient
 call on the new streams), and after the last sublayer ``Boundaries.post_only``
 reduces it residual-only, followed by the streams' mean (the final collapse).
@@ -94,25 +95,34 @@ class DecodeChain:
                    hidden=synth.CHAIN_HIDDEN, tp=synth.CHAIN_TP, top_k=synth.CHAIN_TOP_K,
                    handle=None, standin=False, side_stream=False, deferred=False, fused=False):
         """The chained step on the seeded synthetic inputs (see ``synth.chain_sublayer``)."""
+        emb = synth.chain_embedding(rows, hidden)
+        subs = (synth.chain_sublayer(layer, ffn, rows=rows, hidden=hidden, tp=tp, top_k=top_k)
+                for layer in range(layers) for ffn in (False, True))
+        return cls.from_arrays(device, emb, subs, tp=tp, top_k=top_k, handle=handle,
+                               standin=standin, side_stream=side_stream, deferred=deferred,
+                               fused=fused)
+
+    @classmethod
+    def from_arrays(cls, device, embedding, sublayers, tp=synth.CHAIN_TP, top_k=synth.CHAIN_TOP_K,
+                    handle=None, **kw):
+        """The chained step on host arrays: ``embedding`` [R,H] bf16 bits and ``sublayers``
+        as ``synth.chain_sublayer`` returns them (uploaded here, one sublayer at a time)."""
         T = lambda a: synth.to_torch(a, device)  # noqa: E731
+        rows, hidden = embedding.shape
         if handle is None:
             handle = binding.Handle(hidden, 4, max_rows=rows, max_tp=tp, top_k=top_k,
                                     device=device.index)
-        emb = T(synth.chain_embedding(rows, hidden))
         subs = []
-        for layer in range(layers):
-            for ffn in (False, True):
-                d = synth.chain_sublayer(layer, ffn, rows=rows, hidden=hidden, tp=tp, top_k=top_k)
-                t = {k: T(d[k]) for k in ("fn", "scale", "base", "norm_w")}
-                t["mxfp8"] = d["mxfp8"]
-                if "partials" in d["output"]:
-                    t["partials"] = T(d["output"]["partials"])
-                else:
-                    g, w, idx, sh = d["output"]["finalize"]
-                    t["finalize"] = (T(g), T(w), T(idx), T(sh))
-                subs.append(t)
-        return cls(handle, emb, subs, synth.chain_params(), device, standin=standin,
-                   side_stream=side_stream, deferred=deferred, fused=fused)
+        for d in sublayers:
+            t = {k: T(d[k]) for k in ("fn", "scale", "base", "norm_w")}
+            t["mxfp8"] = d["mxfp8"]
+            if "partials" in d["output"]:
+                t["partials"] = T(d["output"]["partials"])
+            else:
+                g, w, idx, sh = d["output"]["finalize"]
+                t["finalize"] = (T(g), T(w), T(idx), T(sh))
+            subs.append(t)
+        return cls(handle, T(embedding), subs, synth.chain_params(), device, **kw)
 
     def input_bytes(self):
         tot = self.emb.numel() * 2

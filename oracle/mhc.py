@@ -178,11 +178,11 @@ def _with_mxfp8(out, mxfp8):
 
 
 def first(x_bits, norm_weight_bits, eps, hc_mult=4, mxfp8=False):
-    """The first layer's entry: the embedding broadcast to the hc streams, and the first
+    """The first layer's entry: hc copies of the embedding as the streams, and the first
     sublayer's input.
 
-    boundary page, ``Boundaries.first``: the residual is the embedding x repeated over the
-    hc streams, and the identity pre-mix selects stream zero, so the collapse is x itself
+    boundary page, ``Boundaries.first``: each of the hc streams starts as a copy of the
+    embedding x, and the first pre-mix is the identity on stream 0, so the collapse is x itself
     and the layer input is x RMS-normalized with the sublayer's norm (``Boundaries._pre``
     receives x and the attention norm). Returns {"residual": [R,n,H] bf16 bits,
     "layer_input": [R,H] bf16 bits} (and "mx_data", "mx_scale" with ``mxfp8``).
@@ -274,7 +274,7 @@ def pre_coeffs(residual_bits, fn_bits, scale, base, rms_eps, pre_eps, sinkhorn_e
 # ----------------------------------------------------------------------------
 
 def decode_chain(embedding_bits, sublayers, rms_eps, hc_eps, post_alpha, sinkhorn_iters,
-                 norm_eps, hc_mult=4, record=None):
+                 norm_eps, hc_mult=4, record=None, progress=None, coeff_perturb=None):
     """One decode step's boundaries over all sublayers, fp64 per step.
 
     decode page, ``SpecializedDecode.run``: the first layer enters through
@@ -297,7 +297,10 @@ def decode_chain(embedding_bits, sublayers, rms_eps, hc_eps, post_alpha, sinkhor
     normalized embedding. Coefficients pass between steps as fp32, as they do
     between the library's calls. Returns the final streams and their mean; with
     ``record`` (a list), appends the first entry's outputs with the first
-    coefficients, and then each boundary's outputs.
+    coefficients, and then each boundary's outputs. ``progress``, if given, is called
+    with each sublayer's index after its boundary (reporting only). ``coeff_perturb``, if
+    given, maps every (pre, post, comb) the coefficient calls return to the values passed
+    on (for measuring how the chain responds to coefficient errors; None: unchanged).
     """
     emb = np.asarray(embedding_bits, dtype=np.uint16)
     head = sublayers[0]
@@ -305,6 +308,8 @@ def decode_chain(embedding_bits, sublayers, rms_eps, hc_eps, post_alpha, sinkhor
     streams = entry["residual"]
     pre, post, comb = pre_coeffs(streams, head["fn"], head["scale"], head["base"],
                                  rms_eps, hc_eps, hc_eps, post_alpha, sinkhorn_iters)
+    if coeff_perturb is not None:
+        pre, post, comb = coeff_perturb(pre, post, comb)
     if record is not None:
         entry.update({"pre": pre, "post": post, "comb": comb})
         record.append(entry)
@@ -328,7 +333,11 @@ def decode_chain(embedding_bits, sublayers, rms_eps, hc_eps, post_alpha, sinkhor
         if not last:
             pre, post, comb = pre_coeffs(streams, nxt["fn"], nxt["scale"], nxt["base"],
                                          rms_eps, hc_eps, hc_eps, post_alpha, sinkhorn_iters)
+            if coeff_perturb is not None:
+                pre, post, comb = coeff_perturb(pre, post, comb)
             res.update({"pre": pre, "post": post, "comb": comb})
         if record is not None:
             record.append(res)
+        if progress is not None:
+            progress(idx)
     return streams, collapse_mean(streams)
