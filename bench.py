@@ -10,10 +10,17 @@ Cache left there by an earlier call. The other calls of the path are timed the
 same way and reported under "rows", as is the 61-layer chained decode step
 (config 4: 122 boundaries plus their coefficient calls at rows=128).
 
-Timing: W eager warm-up calls, then EXACTLY K calls captured in one HIP graph
-and replayed once between two events recorded on the launch stream (the
-caller's graph is how the path runs in a decode step); the eager per-call
-time of the same K calls is reported beside it.
+Timing: W eager warm-up calls; then one HIP graph of EXACTLY K calls and one
+of 2K calls (the caller's graph is how the path runs in a decode step), each
+replayed once between two events recorded on the launch stream. The per-call
+time is the slope, (t(2K) - t(K)) / K: the replay's fixed cost cancels, so
+it does not depend on K; t(K) / K, with that cost, and the eager per-call
+time of K calls launched one by one are reported beside it. Before each
+timed region a read of 1 GiB (four times the 256 MB Infinity Cache) evicts
+whatever the untimed work left in the cache, without leaving dirty lines,
+and keeps the GPU busy while the host enqueues the timed work. Call i uses
+buffer set i mod B, B sets covering >= 512 MB, so no call finds its data in
+the cache.
 """
 
 import argparse
@@ -29,8 +36,10 @@ sys.path.insert(0, ROOT)
 METRIC = "fused mHC boundary µs/call + achieved HBM GB/s (rows=32, hidden=7168, hc=4)"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
+FLUSH_BYTES = 1 << 30  # read before each timed region
 COPY_CALIBRATION_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "boundary_decode_r32_h7168_traffic.json")
+KSTATS_FILE = os.path.join(ROOT, "profiles", "boundary_decode_mxfp8_r32_h7168_kernel_stats.json")
 KERNEL_SOURCES = ["boundary.hip", "device_common.h", "kernels.h"]
 
 
@@ -78,6 +87,12 @@ def bytes_finalize(rows, hidden, top_k, n=4, pre=True, mxfp8=False):
     return rows * per_row + (hidden * 2 if pre else 0)
 
 
+def bytes_floor(rows, hidden, tp, n=4):
+    """What mhc_floor_boundary_traffic moves: the partials and streams read; the streams,
+    a layer input, its E4M3 bytes and scale bytes written."""
+    return rows * (tp * hidden * 2 + 2 * n * hidden * 2 + hidden * 2 + hidden + hidden // 32)
+
+
 def bytes_pre(rows, hidden, n=4):
     nc = 2 * n + n * n
     return rows * n * hidden * 2 + n * hidden * nc * 2 + (3 + nc) * 4 + rows * nc * 4
@@ -103,54 +118,83 @@ def bytes_collapse_norm(rows, hidden, n=4):
 # ---------------------------------------------------------------------------
 
 GRAPH_ONLY = False
+_FLUSH = []
+
+
+def flush(torch):
+    """Enqueue a read of 1 GiB (a sum): it evicts the 256 MB Infinity Cache without leaving
+    dirty lines behind (a copy would leave its writes for the next kernels to write back)
+    and occupies the GPU for ~0.2 ms while the host enqueues what follows."""
+    if not _FLUSH:
+        _FLUSH.append(torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda"))
+    _FLUSH[0].sum()
+
+
+def _timed(torch, fn):
+    """Milliseconds between two events on the current stream around fn(), behind a flush."""
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush(torch)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
 
 
 def time_calls(torch, calls, steps, warmup):
-    """calls: list of zero-argument launchers, one per buffer set; call i uses set i % len.
-    Returns (eager, graph) microseconds per call; eager is None under --graph-only."""
+    """calls: zero-argument launchers, one per buffer set; call i uses set i % len(calls).
+
+    Returns (eager, graph, graph_single) microseconds per call. graph: the slope between one
+    HIP graph of exactly `steps` calls and one of 2 * `steps` (the second continuing over the
+    buffer sets), each replayed once behind a cache flush: the replay's fixed cost cancels,
+    so the figure does not depend on `steps`. graph_single: the `steps`-call graph's time per
+    call, that fixed cost included. eager: `steps` calls launched one by one (None under
+    --graph-only)."""
     nset = len(calls)
     for i in range(warmup):
         calls[i % nset]()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     eager_ms = None
     if not GRAPH_ONLY:
-        e0.record(stream)
-        for i in range(steps):
-            calls[i % nset]()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        eager_ms = e0.elapsed_time(e1)
+        eager_ms = _timed(torch, lambda: [calls[i % nset]() for i in range(steps)])
 
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(steps):
-            calls[i % nset]()
-    g.replay()  # untimed: first replay uploads the graph
+    graphs = []
+    for n in (steps, 2 * steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                calls[i % nset]()
+        g.replay()  # untimed: the first replay uploads the graph
+        graphs.append(g)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0.record(stream)
-    g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    graph_ms = e0.elapsed_time(e1)
-    del g
+    t1 = _timed(torch, graphs[0].replay)
+    t2 = _timed(torch, graphs[1].replay)
+    del graphs
     eager_us = None if eager_ms is None else eager_ms / steps * 1e3
-    return eager_us, graph_ms / steps * 1e3  # us per call
+    return eager_us, (t2 - t1) / steps * 1e3, t1 / steps * 1e3
 
 
 def n_sets(bytes_per_set):
     return max(2, int((2 * MALL_BYTES + bytes_per_set - 1) // bytes_per_set))
 
 
-def row_entry(name, nbytes, us_eager, us_graph, sets):
-    us = us_graph
+def row_entry(name, nbytes, t, sets):
+    """t: time_calls' (eager, graph slope, single graph) microseconds per call."""
+    us_eager, us, us_single = t
     gbs = nbytes / (us * 1e-6) / 1e9
-    return {"us_per_call": round(us, 3),
+    return {"us_per_call": round(us, 3), "us_per_call_single_graph": round(us_single, 3),
             "us_per_call_eager": None if us_eager is None else round(us_eager, 3),
             "algorithmic_bytes": int(nbytes), "gb_per_s": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "buffer_sets": sets}
+
+
+def time_entry(t, note):
+    """A row without bytes: time_calls' microseconds per call."""
+    us_eager, us, us_single = t
+    return {"us_per_call": round(us, 3), "us_per_call_single_graph": round(us_single, 3),
+            "us_per_call_eager": None if us_eager is None else round(us_eager, 3),
+            "note": note}
 
 
 def source_hash():
@@ -159,6 +203,19 @@ def source_hash():
         with open(os.path.join(ROOT, "mhc_hyper_connection_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def kernel_stats():
+    """The headline kernel's rocprofv3 per-dispatch durations from the committed summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(KSTATS_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    return t
 
 
 def measured_traffic(block):
@@ -222,7 +279,7 @@ def main():
         out = {}
         s5 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, fused=True,
                                    deferred=True)
-        e5, g5 = time_calls(torch, [s5.run], k, 2)
+        e5, g5, _ = time_calls(torch, [s5.run], k, 2)
         out["chain_decode_step"] = {
             "us_per_step": round(g5, 1), "us_per_step_eager": None if e5 is None else round(e5, 1),
             "algorithmic_bytes": int(s5.algorithmic_bytes()),
@@ -233,14 +290,14 @@ def main():
         log(f"  chain (fused, deferred) {out['chain_decode_step']}")
         del s5
         s4 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, fused=True)
-        e4, g4 = time_calls(torch, [s4.run], k, 2)
+        e4, g4, _ = time_calls(torch, [s4.run], k, 2)
         out["chain_decode_step_fused"] = {
             "us_per_step": round(g4, 1), "us_per_step_eager": None if e4 is None else round(e4, 1),
             "gb_per_s": round(s4.algorithmic_bytes() / g4 / 1e3, 1),
             "note": "fused calls that finish the next coefficients themselves"}
         log(f"  chain (fused) {out['chain_decode_step_fused']}")
         del s4
-        us_e, us_g = time_calls(torch, [step.run], k, 2)
+        us_e, us_g, _ = time_calls(torch, [step.run], k, 2)
         out["chain_decode_step_unfused"] = {
             "us_per_step": round(us_g, 1),
             "us_per_step_eager": None if us_e is None else round(us_e, 1),
@@ -249,7 +306,7 @@ def main():
             "note": "boundary calls, each followed by a separate mhc_pre_coeffs call"}
         log(f"  chain (unfused) {out['chain_decode_step_unfused']}")
         s3 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, deferred=True)
-        e3, g3 = time_calls(torch, [s3.run], k, 2)
+        e3, g3, _ = time_calls(torch, [s3.run], k, 2)
         out["chain_decode_step_deferred"] = {
             "us_per_step": round(g3, 1), "us_per_step_eager": None if e3 is None else round(e3, 1),
             "gb_per_s": round(step.algorithmic_bytes() / g3 / 1e3, 1),
@@ -261,7 +318,7 @@ def main():
         for side in (False, True):
             s2 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, standin=True,
                                        side_stream=side)
-            e2, g2 = time_calls(torch, [s2.run], k, 2)
+            e2, g2, _ = time_calls(torch, [s2.run], k, 2)
             name = "chain_standin_side_stream" if side else "chain_standin_inline"
             out[name] = {"us_per_step": round(g2, 1),
                          "us_per_step_eager": None if e2 is None else round(e2, 1),
@@ -336,17 +393,17 @@ def main():
                                    nxt["rms_eps"], nxt["pre_eps"], nxt["sinkhorn_eps"],
                                    nxt["post_alpha"], nxt["sinkhorn_iters"], out=b["nx"])
 
-            e, g = time_calls(torch, [(lambda b=b: fused(b)) for b in bufs], args.steps,
+            t = time_calls(torch, [(lambda b=b: fused(b)) for b in bufs], args.steps,
                               args.warmup)
             name = f"{kind}_coeffs_r128" + ("_mxfp8" if mx else "")
-            out[name] = row_entry(name, nb + extra, e, g, ns)
+            out[name] = row_entry(name, nb + extra, t, ns)
             out[name]["note"] = ("boundary + the next coefficient call in one kernel "
                                  "(no second read of the streams)")
             log(f"  {name} {out[name]}")
-            e, g = time_calls(torch, [(lambda b=b: two(b)) for b in bufs], args.steps,
+            t = time_calls(torch, [(lambda b=b: two(b)) for b in bufs], args.steps,
                               args.warmup)
             name2 = f"{kind}_then_coeffs_r128" + ("_mxfp8" if mx else "")
-            out[name2] = row_entry(name2, nb + extra + Rc * 4 * H * 2, e, g, ns)
+            out[name2] = row_entry(name2, nb + extra + Rc * 4 * H * 2, t, ns)
             out[name2]["note"] = "the same work as two calls (boundary, then mhc_pre_coeffs)"
             log(f"  {name2} {out[name2]}")
 
@@ -368,12 +425,12 @@ def main():
                                                b["shared_output"], b["s"], qq, cc, pp,
                                                co["norm_weight"], d["eps"], nxt, **kw)
 
-            e, g = time_calls(torch, [(lambda i=i: chained(i)) for i in range(ns)],
+            t = time_calls(torch, [(lambda i=i: chained(i)) for i in range(ns)],
                               args.steps, args.warmup)
             binding.pre_coeffs_flush(h)  # the last call's coefficients, before the buffers go
             torch.cuda.synchronize()
             name3 = f"{kind}_coeffs_deferred_r128" + ("_mxfp8" if mx else "")
-            out[name3] = row_entry(name3, nb + extra, e, g, ns)
+            out[name3] = row_entry(name3, nb + extra, t, ns)
             out[name3]["note"] = ("as " + name + ", chained: each call finishes the previous "
                                   "call's coefficients in its kernel and leaves its own as "
                                   "partial sums (mhc_coeff_args.deferred)")
@@ -415,15 +472,15 @@ def main():
                                         residual_out=b["so"], layer_input_out=b["li"],
                                         mx_out=(b["md"], b["ms"]))
 
-    us_e, us_g = time_calls(torch, [mk(b) for b in bufs], args.steps, args.warmup)
-    rows = {"boundary_decode_mxfp8": row_entry("boundary", nb, us_e, us_g, sets)}
+    t = time_calls(torch, [mk(b) for b in bufs], args.steps, args.warmup)
+    rows = {"boundary_decode_mxfp8": row_entry("boundary", nb, t, sets)}
     log(f"  {rows['boundary_decode_mxfp8']}")
     if not args.no_rows:
         # the same call on one buffer set: its 8 MB stay in the 256 MB Infinity Cache between
         # calls (the case of a producer that has just written the partials); context only,
         # the headline is the cold figure above
-        e, g = time_calls(torch, [mk(bufs[0])], args.steps, args.warmup)
-        rows["boundary_decode_mxfp8_warm"] = row_entry("boundary_warm", nb, e, g, 1)
+        t = time_calls(torch, [mk(bufs[0])], args.steps, args.warmup)
+        rows["boundary_decode_mxfp8_warm"] = row_entry("boundary_warm", nb, t, 1)
         rows["boundary_decode_mxfp8_warm"]["note"] = (
             "one buffer set reused every call (inputs resident in the Infinity Cache); "
             "context, not the headline")
@@ -436,18 +493,31 @@ def main():
         cbufs = [(torch.empty(half, dtype=torch.uint8, device=dev),
                   torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(cs)]
         calls = [(lambda a=a, b=b: b.copy_(a)) for a, b in cbufs]
-        e, g = time_calls(torch, calls, args.steps, args.warmup)
-        rows["copy_floor_8mb"] = row_entry("copy", 2 * half, e, g, cs)
+        t = time_calls(torch, calls, args.steps, args.warmup)
+        rows["copy_floor_8mb"] = row_entry("copy", 2 * half, t, cs)
         rows["copy_floor_8mb"]["note"] = ("device copy of the headline's bytes (read + written), "
                                           "cold buffers: the floor of an 8 MB pass")
         log(f"  copy floor {rows['copy_floor_8mb']}")
         del cbufs, calls
         one = torch.empty(1, dtype=torch.float32, device=dev)
-        e, g = time_calls(torch, [one.zero_], args.steps, args.warmup)
-        rows["launch_floor"] = {"us_per_call": round(g, 3),
-                                "us_per_call_eager": None if e is None else round(e, 3),
-                                "note": "a one-element fill kernel: the cost of one launch"}
+        t = time_calls(torch, [one.zero_], args.steps, args.warmup)
+        rows["launch_floor"] = time_entry(t, "a one-element fill kernel: the cost of one launch")
         log(f"  launch floor {rows['launch_floor']}")
+    # the in-house floors of the headline's launch geometry (include/mhc_floor.h), on the
+    # headline's own buffer sets: its bytes moved with its grid and access kind but without
+    # its arithmetic or row handoff, and the same grid doing nothing
+    nfl = bytes_floor(R, H, TP)
+    t = time_calls(torch, [(lambda b=b: binding.floor_boundary_traffic(
+        b["x"], b["s"], b["so"], b["li"], b["md"], b["ms"])) for b in bufs], args.steps,
+        args.warmup)
+    rows["floor_boundary_traffic"] = row_entry("floor_traffic", nfl, t, sets)
+    rows["floor_boundary_traffic"]["note"] = (
+        "mhc_floor_boundary_traffic: the headline's bytes with its grid (224 x 512 threads), "
+        "non-temporal 4-byte loads and stores, no arithmetic, no row handoff")
+    log(f"  floor (traffic) {rows['floor_boundary_traffic']}")
+    t = time_calls(torch, [lambda: binding.floor_empty(R, H)], args.steps, args.warmup)
+    rows["floor_empty_grid"] = time_entry(t, "mhc_floor_empty: the headline's grid, doing nothing")
+    log(f"  floor (empty grid) {rows['floor_empty_grid']}")
     del bufs
 
     if not args.no_rows:
@@ -461,8 +531,8 @@ def main():
                                                base["pre"], base["norm_weight"], d1["eps"],
                                                residual_out=b["so"], layer_input_out=b["li"]))
                  for b in bufs]
-        e, g = time_calls(torch, calls, args.steps, args.warmup)
-        rows["boundary_decode_bf16"] = row_entry("boundary_bf16", nb16, e, g, s1)
+        t = time_calls(torch, calls, args.steps, args.warmup)
+        rows["boundary_decode_bf16"] = row_entry("boundary_bf16", nb16, t, s1)
         log(f"  bf16-only {rows['boundary_decode_bf16']}")
         del bufs, calls
 
@@ -473,8 +543,8 @@ def main():
                  "so": torch.empty_like(base["residual"])} for _ in range(s2)]
         calls = [(lambda b=b: binding.residual_only(h, b["x"], b["s"], base["post"], base["comb"],
                                                     residual_out=b["so"])) for b in bufs]
-        e, g = time_calls(torch, calls, args.steps, args.warmup)
-        rows["residual_only_decode"] = row_entry("residual_only", nro, e, g, s2)
+        t = time_calls(torch, calls, args.steps, args.warmup)
+        rows["residual_only_decode"] = row_entry("residual_only", nro, t, s2)
         log(f"  residual-only {rows['residual_only_decode']}")
         del bufs, calls
 
@@ -496,8 +566,8 @@ def main():
             c2["post"], c2["comb"], c2["pre"], c2["norm_weight"], d2["eps"], mxfp8=True,
             residual_out=b["so"], layer_input_out=b["li"], mx_out=(b["md"], b["ms"])))
             for b in bufs]
-        e, g = time_calls(torch, calls, args.steps, args.warmup)
-        rows["finalize_moe_mxfp8"] = row_entry("finalize", nf, e, g, s3)
+        t = time_calls(torch, calls, args.steps, args.warmup)
+        rows["finalize_moe_mxfp8"] = row_entry("finalize", nf, t, s3)
         log(f"  finalize {rows['finalize_moe_mxfp8']}")
         del bufs, calls
 
@@ -514,8 +584,8 @@ def main():
                                                  d3["pre_eps"], d3["sinkhorn_eps"],
                                                  d3["post_alpha"], d3["sinkhorn_iters"],
                                                  out=b["o"])) for b in bufs]
-        e, g = time_calls(torch, calls, args.steps, args.warmup)
-        rows["pre_coeffs"] = row_entry("pre_coeffs", npb, e, g, s4)
+        t = time_calls(torch, calls, args.steps, args.warmup)
+        rows["pre_coeffs"] = row_entry("pre_coeffs", npb, t, s4)
         log(f"  pre_coeffs {rows['pre_coeffs']}")
         del bufs, calls
 
@@ -531,8 +601,8 @@ def main():
         calls = [(lambda b=b: binding.first(h, b["x"], base["norm_weight"], d1["eps"], mxfp8=True,
                                             residual_out=b["so"], layer_input_out=b["li"],
                                             mx_out=(b["md"], b["ms"]))) for b in bufs]
-        e, g = time_calls(torch, calls, args.steps, args.warmup)
-        rows["first_decode_mxfp8"] = row_entry("first", nfi, e, g, s6)
+        t = time_calls(torch, calls, args.steps, args.warmup)
+        rows["first_decode_mxfp8"] = row_entry("first", nfi, t, s6)
         log(f"  first {rows['first_decode_mxfp8']}")
         del bufs, calls
 
@@ -545,8 +615,8 @@ def main():
                 for _ in range(s7)]
         calls = [(lambda b=b: binding.collapse_norm(h, b["s"], ph, wh, dh["eps"], out=b["o"]))
                  for b in bufs]
-        e, g = time_calls(torch, calls, args.steps, args.warmup)
-        rows["collapse_norm_r128"] = row_entry("collapse_norm", nhd, e, g, s7)
+        t = time_calls(torch, calls, args.steps, args.warmup)
+        rows["collapse_norm_r128"] = row_entry("collapse_norm", nhd, t, s7)
         log(f"  collapse_norm {rows['collapse_norm_r128']}")
         del bufs, calls
 
@@ -557,8 +627,8 @@ def main():
         bufs = [{"s": sm.clone(), "o": torch.empty((128, H), dtype=torch.bfloat16, device=dev)}
                 for _ in range(s5)]
         calls = [(lambda b=b: binding.collapse_mean(h, b["s"], out=b["o"])) for b in bufs]
-        e, g = time_calls(torch, calls, args.steps, args.warmup)
-        rows["collapse_mean_r128"] = row_entry("collapse_mean", nm, e, g, s5)
+        t = time_calls(torch, calls, args.steps, args.warmup)
+        rows["collapse_mean_r128"] = row_entry("collapse_mean", nm, t, s5)
         log(f"  collapse_mean {rows['collapse_mean_r128']}")
         del bufs, calls
 
@@ -574,6 +644,14 @@ def main():
     us = head["us_per_call"]
     achieved = head["gb_per_s"]
     traffic = measured_traffic(block)
+    ks = kernel_stats()
+    rocprof = None
+    if ks is not None:
+        rocprof = {"kernel": ks["kernel"], "dispatches": ks["dispatches"],
+                   "avg_us": ks["avg_us"], "median_us": ks["median_us"],
+                   "frac_avg": round(nb / (ks["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "frac_median": round(nb / (ks["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "source": os.path.relpath(KSTATS_FILE, ROOT)}
     out = {
         "metric": METRIC,
         "value": achieved,
@@ -592,10 +670,14 @@ def main():
                                "hc_mult=4 tp=8 (bf16 in/out, fp32 arithmetic)",
                    "rows": R, "hidden": H, "hc_mult": 4, "tp": TP, "mxfp8": True,
                    "block": block, "lane_elems": lane_elems, "buffer_sets": head["buffer_sets"],
-                   "timing": "one HIP graph of the K calls, events on the launch stream"},
+                   "timing": "slope between one HIP graph of exactly K calls and one of 2K, "
+                             "each replayed between two events on the launch stream behind a "
+                             "1 GiB cache-evicting read; call i on buffer set i mod "
+                             "buffer_sets (>= 512 MB)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": nb},
+                     "algorithmic_bytes_per_launch": nb,
+                     "kernel_time_rocprof": rocprof},
         "rows": rows,
     }
     if not args.no_cpu:
@@ -606,8 +688,16 @@ def main():
 
 def cpu_baseline(d, nbytes, seconds, log):
     """The oracle as it stands (numpy fp64) on the same config-1 inputs, repeated for about
-    `seconds` of host time."""
+    `seconds` of host time. Its boundary is numpy element-wise and einsum loops, which run on
+    one thread whatever cores and BLAS threads the host offers (both reported)."""
     import oracle
+    host_cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = sum(i.get("num_threads", 0) for i in threadpool_info()
+                   if i.get("user_api") == "blas")
+    except Exception:  # noqa: BLE001 (threadpoolctl missing or failing: report unknown)
+        blas = None
     log(f"cpu baseline: oracle boundary on config 1, ~{seconds:.0f} s")
     n = 0
     t0 = time.perf_counter()
@@ -620,9 +710,11 @@ def cpu_baseline(d, nbytes, seconds, log):
             break
     per = el / n
     return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "ms_per_call": round(per * 1e3, 2),
+            "ms_per_call": round(per * 1e3, 2), "host_cores_available": host_cores,
+            "blas_threads": blas,
             "sample": f"{n} full calls of the config-1 boundary (32 rows, MXFP8) in {el:.1f} s; "
-                      "numpy fp64 loops, one thread"}
+                      "numpy fp64 element-wise and einsum loops, which use one thread "
+                      f"({host_cores} host cores available, BLAS threads {blas}, unused here)"}
 
 
 if __name__ == "__main__":

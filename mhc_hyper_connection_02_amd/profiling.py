@@ -1,7 +1,9 @@
 """Summaries of rocprofv3 output (CSV format) for the kernels of this library.
 
   python -m mhc_hyper_connection_02_amd.profiling stats <trace_dir> --cmd "<command>"
-      per-kernel dispatch count and duration from a ``--kernel-trace --stats`` run
+      [--json-kernel <substr> --json-out <json> --source-hash H]
+      per-kernel dispatch count and duration from a ``--kernel-trace --stats`` run (and
+      one kernel's figures as JSON, which bench.py reports beside its own timing)
   python -m mhc_hyper_connection_02_amd.profiling mfma <dir> [<dir> ...] --match <substr>
       --cmd "<commands>"
       per (kernel, grid size): mean of every counter found in the ``--pmc`` runs' CSVs
@@ -78,6 +80,10 @@ def main(argv=None):
     s = sub.add_parser("stats")
     s.add_argument("trace_dir")
     s.add_argument("--cmd", required=True)
+    s.add_argument("--json-kernel", help="with --json-out: the kernel (name substring) whose "
+                   "durations go to the JSON summary")
+    s.add_argument("--json-out")
+    s.add_argument("--source-hash", help="hash of the kernel sources the trace was taken on")
     m = sub.add_parser("mfma")
     m.add_argument("dirs", nargs="+")
     m.add_argument("--match", action="append", required=True)
@@ -103,8 +109,20 @@ def main(argv=None):
     if a.what == "stats":
         print(f"# rocprofv3 kernel trace: per-dispatch duration\n# command: {a.cmd}\n")
         print(f"{'calls':>6} {'avg_us':>9} {'median_us':>9} {'min_us':>9} {'max_us':>9}  kernel")
-        for name, n, avg, med, mn, mx in kernel_stats(a.trace_dir):
+        stats = kernel_stats(a.trace_dir)
+        for name, n, avg, med, mn, mx in stats:
             print(f"{n:6d} {avg / 1e3:9.3f} {med / 1e3:9.3f} {mn / 1e3:9.3f} {mx / 1e3:9.3f}  {name}")
+        if a.json_out:
+            hit = [t for t in stats if a.json_kernel in t[0]]
+            if len(hit) != 1:
+                raise ValueError(f"{len(hit)} kernels match {a.json_kernel!r}")
+            name, n, avg, med, mn, mx = hit[0]
+            with open(a.json_out, "w") as f:
+                json.dump({"kernel": name, "dispatches": n, "avg_us": round(avg / 1e3, 3),
+                           "median_us": round(med / 1e3, 3), "min_us": round(mn / 1e3, 3),
+                           "max_us": round(mx / 1e3, 3), "source_hash": a.source_hash,
+                           "command": a.cmd}, f, indent=1)
+                f.write("\n")
         return 0
 
     fk, nf = counter_mean(a.fetch, "FETCH_SIZE", a.kernel)
