@@ -16,11 +16,11 @@ replayed once between two events recorded on the launch stream. The per-call
 time is the slope, (t(2K) - t(K)) / K: the replay's fixed cost cancels, so
 it does not depend on K; t(K) / K, with that cost, and the eager per-call
 time of K calls launched one by one are reported beside it. Before each
-timed region a read of 1 GiB (four times the 256 MB Infinity Cache) evicts
-whatever the untimed work left in the cache, without leaving dirty lines,
-and keeps the GPU busy while the host enqueues the timed work. Call i uses
-buffer set i mod B, B sets covering >= 512 MB, so no call finds its data in
-the cache.
+timed region a spacer (the headline call over its own >= 512 MB of buffer
+sets, twice the 256 MB Infinity Cache) evicts whatever the untimed work left
+in the cache and keeps the GPU busy while the host enqueues the timed work.
+Call i uses buffer set i mod B, B sets covering >= 512 MB, so no call finds
+its data in the cache.
 """
 
 import argparse
@@ -36,7 +36,6 @@ sys.path.insert(0, ROOT)
 METRIC = "fused mHC boundary µs/call + achieved HBM GB/s (rows=32, hidden=7168, hc=4)"
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
-FLUSH_BYTES = 1 << 30  # read before each timed region
 COPY_CALIBRATION_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "boundary_decode_r32_h7168_traffic.json")
 KSTATS_FILE = os.path.join(ROOT, "profiles", "boundary_decode_mxfp8_r32_h7168_kernel_stats.json")
@@ -49,6 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--block", type=int, default=None, help="boundary workgroup size (128/256/512)")
+    ap.add_argument("--tile-placement", choices=("default", "per-xcd", "spread"),
+                    default="default", help="MHC_OPT_TILE_PLACEMENT of the fused calls' kernel")
     ap.add_argument("--no-chain", action="store_true", help="skip the 61-layer chained step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--no-rows", action="store_true", help="time only the headline call")
@@ -118,16 +119,34 @@ def bytes_collapse_norm(rows, hidden, n=4):
 # ---------------------------------------------------------------------------
 
 GRAPH_ONLY = False
-_FLUSH = []
+_SPACER = []
+
+
+def set_spacer(torch, calls):
+    """The cache flush of every timed region: one graph of `calls`, headline boundary calls
+    on a pool of buffer sets (>= 512 MB) that no timed call uses."""
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    # the graph holds raw addresses: keep the launchers, and with them the buffers they
+    # hold, alive as long as the graph (freed buffers would be handed out again while the
+    # spacer still writes them)
+    _SPACER[:] = [g, list(calls)]
 
 
 def flush(torch):
-    """Enqueue a read of 1 GiB (a sum): it evicts the 256 MB Infinity Cache without leaving
-    dirty lines behind (a copy would leave its writes for the next kernels to write back)
-    and occupies the GPU for ~0.2 ms while the host enqueues what follows."""
-    if not _FLUSH:
-        _FLUSH.append(torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda"))
-    _FLUSH[0].sum()
+    """Enqueue the spacer: it evicts the timed buffers from the 256 MB Infinity Cache with
+    the same kind of work as the timed calls, and occupies the GPU while the host enqueues
+    what follows. (A foreign 1 GiB read or copy in its place was measured to slow the
+    boundary calls after it by ~0.45 us each, for milliseconds, even calls whose data sits
+    in the cache; a spin kernel that touches no memory left them unchanged.)"""
+    _SPACER[0].replay()
 
 
 def _timed(torch, fn):
@@ -274,6 +293,8 @@ def main():
         log("chain: generating 122 sublayers of synthetic inputs")
         t0 = time.time()
         step = chain_mod.DecodeChain.from_synth(dev)
+        if placement is not None:
+            step.h.set_option(binding.MHC_OPT_TILE_PLACEMENT, placement)
         log(f"  inputs ready in {time.time() - t0:.1f} s ({step.input_bytes() / 1e9:.2f} GB)")
         k = max(3, args.steps // 40)
         out = {}
@@ -438,16 +459,16 @@ def main():
             del bufs
         return out
 
-    if args.chain_only:
-        print(json.dumps({"rows": chain_rows()}), flush=True)
-        return
-
     # --- headline: config 1, decode boundary + MXFP8 --------------------------------
     R, H, TP = 32, 7168, 8
     d1 = synth.config(1)
     h = binding.Handle(H, 4, max_rows=128, max_tp=8, top_k=8)
     if args.block:
         h.set_option(binding.MHC_OPT_BOUNDARY_BLOCK, args.block)
+    placement = {"per-xcd": binding.MHC_TILE_PER_XCD, "spread": binding.MHC_TILE_SPREAD}.get(
+        args.tile_placement)
+    if placement is not None:
+        h.set_option(binding.MHC_OPT_TILE_PLACEMENT, placement)
     # the handle's choice for 32 rows: 512 threads at two elements per lane (the same seven
     # workgroups per row as 128 threads at eight); a fixed block size runs eight per lane
     block = args.block or 512
@@ -455,22 +476,28 @@ def main():
     nb = bytes_boundary(R, H, TP, pre=True, mxfp8=True)
     sets = n_sets(nb)
     base = {k: T(d1[k]) for k in ("x_partials", "residual", "post", "comb", "pre", "norm_weight")}
-    bufs = []
-    for _ in range(sets):
-        bufs.append({
-            "x": base["x_partials"].clone(), "s": base["residual"].clone(),
-            "so": torch.empty_like(base["residual"]),
-            "li": torch.empty((R, H), dtype=torch.bfloat16, device=dev),
-            "md": torch.empty((R, H), dtype=torch.uint8, device=dev),
-            "ms": torch.empty((R, H // 32), dtype=torch.uint8, device=dev),
-        })
-    log(f"headline: boundary rows={R} hidden={H} tp={TP} mxfp8, {sets} buffer sets, block {block}")
+
+    def buffer_sets(n):
+        return [{"x": base["x_partials"].clone(), "s": base["residual"].clone(),
+                 "so": torch.empty_like(base["residual"]),
+                 "li": torch.empty((R, H), dtype=torch.bfloat16, device=dev),
+                 "md": torch.empty((R, H), dtype=torch.uint8, device=dev),
+                 "ms": torch.empty((R, H // 32), dtype=torch.uint8, device=dev)}
+                for _ in range(n)]
 
     def mk(b):
         return lambda: binding.boundary(h, b["x"], b["s"], base["post"], base["comb"], base["pre"],
                                         base["norm_weight"], d1["eps"], mxfp8=True,
                                         residual_out=b["so"], layer_input_out=b["li"],
                                         mx_out=(b["md"], b["ms"]))
+
+    # the flush before every timed region: the headline call on its own pool of buffer sets
+    set_spacer(torch, [mk(b) for b in buffer_sets(sets)])
+    if args.chain_only:
+        print(json.dumps({"rows": chain_rows()}), flush=True)
+        return
+    bufs = buffer_sets(sets)
+    log(f"headline: boundary rows={R} hidden={H} tp={TP} mxfp8, {sets} buffer sets, block {block}")
 
     t = time_calls(torch, [mk(b) for b in bufs], args.steps, args.warmup)
     rows = {"boundary_decode_mxfp8": row_entry("boundary", nb, t, sets)}
@@ -672,8 +699,8 @@ def main():
                    "block": block, "lane_elems": lane_elems, "buffer_sets": head["buffer_sets"],
                    "timing": "slope between one HIP graph of exactly K calls and one of 2K, "
                              "each replayed between two events on the launch stream behind a "
-                             "1 GiB cache-evicting read; call i on buffer set i mod "
-                             "buffer_sets (>= 512 MB)"},
+                             "cache-evicting spacer (the same call on >= 512 MB of other "
+                             "buffers); call i on buffer set i mod buffer_sets (>= 512 MB)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": nb,

@@ -133,15 +133,24 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
  *     rows and it then needs no more rounds than at 8; otherwise 8. The new streams are
  *     identical for every e (every element's arithmetic is the same). Other values:
  *     MHC_ERR_SHAPE.
+ *   MHC_OPT_TILE_PLACEMENT: where the fused calls' single kernel (mhc_boundary_coeffs,
+ *     mhc_finalize_coeffs) runs the 256-element chunks of a 16-row tile:
+ *       MHC_TILE_PER_XCD (default): all chunks of a tile on one XCD (tiles dealt to XCDs);
+ *       MHC_TILE_SPREAD: chunk c of every tile on XCD c % 8, so each XCD reads only its
+ *         chunks' rows of fn, and a call of few rows still uses every XCD.
+ *     Results are identical either way (the same arithmetic per chunk and the same order
+ *     of every sum). Other values: MHC_ERR_SHAPE.
  * Unknown options: MHC_ERR_INVALID_ARG.
  */
 enum mhc_option {
   MHC_OPT_BOUNDARY_BLOCK = 1,
   MHC_OPT_SPIN_LIMIT = 2,
   MHC_OPT_SCALE_LAYOUT = 3,
-  MHC_OPT_LANE_ELEMS = 4
+  MHC_OPT_LANE_ELEMS = 4,
+  MHC_OPT_TILE_PLACEMENT = 5
 };
 enum mhc_scale_layout { MHC_SCALE_ROW_MAJOR = 0, MHC_SCALE_SWIZZLED_128X4 = 1 };
+enum mhc_tile_placement { MHC_TILE_PER_XCD = 0, MHC_TILE_SPREAD = 1 };
 int mhc_set_option(mhc_handle h, int option, int value);
 
 /*

@@ -25,6 +25,9 @@ MHC_OPT_BOUNDARY_BLOCK = 1
 MHC_OPT_SPIN_LIMIT = 2
 MHC_OPT_SCALE_LAYOUT = 3
 MHC_OPT_LANE_ELEMS = 4
+MHC_OPT_TILE_PLACEMENT = 5
+MHC_TILE_PER_XCD = 0
+MHC_TILE_SPREAD = 1
 MHC_SCALE_ROW_MAJOR = 0
 MHC_SCALE_SWIZZLED_128X4 = 1
 _VALUE_ERRORS = {1, 2, 3, 4, 5}

@@ -39,6 +39,7 @@ struct mhc_ctx {
   int block_set;           // the size MHC_OPT_BOUNDARY_BLOCK set, 0: automatic
   int spin_limit;          // polls before a handoff wait gives up
   int scale_layout;        // MHC_SCALE_ROW_MAJOR or MHC_SCALE_SWIZZLED_128X4
+  int tile_placement;      // MHC_TILE_PER_XCD or MHC_TILE_SPREAD (the fused kernel)
   int lane_elems;          // the fewest elements per lane the layer-input kernels may use
                            // (2, 4 or 8; fewer run at more threads: the same chunks per row)
   int wgs_per_xcd[3];      // resident layer-input workgroups per XCD at block 128 / 256 / 512
@@ -239,6 +240,7 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   h->spin_limit = kDefaultSpinLimit;
   h->scale_layout = MHC_SCALE_ROW_MAJOR;
   h->lane_elems = 2;
+  h->tile_placement = MHC_TILE_PER_XCD;
   h->pending = false;
   // the most chunks per row, rounded up to 16 words: each row's handoff words on a
   // 128-byte line of their own (rows sharing a line, from different XCDs, measured
@@ -342,6 +344,10 @@ int mhc_set_option(mhc_handle h, int option, int value) {
     case MHC_OPT_SCALE_LAYOUT:
       if (value != MHC_SCALE_ROW_MAJOR && value != MHC_SCALE_SWIZZLED_128X4) return MHC_ERR_SHAPE;
       h->scale_layout = value;
+      return MHC_OK;
+    case MHC_OPT_TILE_PLACEMENT:
+      if (value != MHC_TILE_PER_XCD && value != MHC_TILE_SPREAD) return MHC_ERR_SHAPE;
+      h->tile_placement = value;
       return MHC_OK;
     default:
       return MHC_ERR_INVALID_ARG;
@@ -598,6 +604,7 @@ int boundary_then_coeffs(mhc_ctx* h, mhc::BoundaryLaunch& L, const mhc_coeff_arg
   T.words = h->tile_words;
   T.tile_rows = h->tile_rows;
   T.wgs_per_xcd = h->tile_wgs_per_xcd;
+  T.spread = h->tile_placement == MHC_TILE_SPREAD;
   if (!a->deferred) return launch_status(mhc::launch_boundary_tile(T, s));
   // deferred: the kernel leaves the next coefficients as partials; the call is pending
   // until a consumer or a flush finishes them

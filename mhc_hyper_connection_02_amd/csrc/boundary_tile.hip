@@ -98,6 +98,8 @@ struct TileParams {
   const float* base;        // [24]
   float rms_eps, pre_eps, sk_eps, alpha;
   int iters;
+  int groups;               // 0: a tile's chunks on one XCD; else chunk c on XCD c % 8, with
+                            // `groups` = ceil(chunks / 8) chunks of each tile per XCD
   union {
     float* next_pre;        // [rows][4]
     float* part_out;        // DEFER_OUT: [rows][25][part_ks] partials of the next call
@@ -686,13 +688,29 @@ __global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_kernel(const Ti
   const int wg = blockIdx.x;
   const int xcd = wg % kXcd;
   const int local = wg / kXcd;
-  const int c = local % p.chunks;
-  const int jt = local / p.chunks;  // which tile of this XCD's block in a round
-  for (int round = 0; round < p.rounds; ++round) {
-    const int tile = (round * p.tiles_per_round + jt) * kXcd + xcd;
-    if (tile * kTileRows >= p.rows) break;  // uniform per workgroup; later rounds go higher
-    if (round > 0) __syncthreads();          // LDS reused
-    tile_item<FINALIZE, MXFP8, DEFER>(p, coef, din, tile, c, S, sc_l, base_l, dsc_l, dbase_l);
+  if (p.groups == 0) {
+    // a tile's chunks on one XCD: tiles dealt to the XCDs
+    const int c = local % p.chunks;
+    const int jt = local / p.chunks;  // which tile of this XCD's block in a round
+    for (int round = 0; round < p.rounds; ++round) {
+      const int tile = (round * p.tiles_per_round + jt) * kXcd + xcd;
+      if (tile * kTileRows >= p.rows) break;  // uniform per workgroup; later rounds go higher
+      if (round > 0) __syncthreads();          // LDS reused
+      tile_item<FINALIZE, MXFP8, DEFER>(p, coef, din, tile, c, S, sc_l, base_l, dsc_l,
+                                        dbase_l);
+    }
+  } else {
+    // chunk c of every tile on XCD c % 8: each XCD reads the fn rows of its own chunks only
+    const int c = xcd + kXcd * (local % p.groups);
+    const int jt = local / p.groups;  // which tile of the round
+    if (c >= p.chunks) return;        // past the last chunk: no work, in no handoff
+    for (int round = 0; round < p.rounds; ++round) {
+      const int tile = round * p.tiles_per_round + jt;
+      if (tile * kTileRows >= p.rows) break;
+      if (round > 0) __syncthreads();
+      tile_item<FINALIZE, MXFP8, DEFER>(p, coef, din, tile, c, S, sc_l, base_l, dsc_l,
+                                        dbase_l);
+    }
   }
 }
 
@@ -799,16 +817,29 @@ hipError_t launch_boundary_tile(const TileLaunch& T, hipStream_t stream) {
   const int tiles = (L.rows + kTileRows - 1) / kTileRows;
   p.tile_cap = (T.tile_rows + kTileRows - 1) / kTileRows;
   if (tiles > p.tile_cap) return hipErrorInvalidConfiguration;
-  const int tile_blocks = (tiles + kXcd - 1) / kXcd;  // tiles per XCD in total
-  // a round may use half of the XCD's resident workgroups, or all of them where half
-  // does not hold one tile
-  int per_xcd = T.wgs_per_xcd / 2;
-  if (per_xcd < p.chunks) per_xcd = T.wgs_per_xcd;
-  int tpr = per_xcd / p.chunks;
-  if (tpr > tile_blocks) tpr = tile_blocks;
-  p.tiles_per_round = tpr;
-  p.rounds = (tile_blocks + tpr - 1) / tpr;
-  const int grid = kXcd * tpr * p.chunks;
+  int grid;
+  if (!T.spread) {
+    p.groups = 0;
+    const int tile_blocks = (tiles + kXcd - 1) / kXcd;  // tiles per XCD in total
+    // a round may use half of the XCD's resident workgroups, or all of them where half
+    // does not hold one tile
+    int per_xcd = T.wgs_per_xcd / 2;
+    if (per_xcd < p.chunks) per_xcd = T.wgs_per_xcd;
+    int tpr = per_xcd / p.chunks;
+    if (tpr > tile_blocks) tpr = tile_blocks;
+    p.tiles_per_round = tpr;
+    p.rounds = (tile_blocks + tpr - 1) / tpr;
+    grid = kXcd * tpr * p.chunks;
+  } else {
+    // every tile of a round on every XCD, `groups` chunks of it per XCD; a round takes as
+    // many tiles as the XCD's resident workgroups hold
+    p.groups = (p.chunks + kXcd - 1) / kXcd;
+    int tpr = T.wgs_per_xcd / p.groups;
+    if (tpr > tiles) tpr = tiles;
+    p.tiles_per_round = tpr;
+    p.rounds = (tiles + tpr - 1) / tpr;
+    grid = kXcd * tpr * p.groups;
+  }
   const bool fin = L.gemm2_permuted != nullptr;
   const bool mx = L.mx_data_out != nullptr;
   TileDeferIn din;

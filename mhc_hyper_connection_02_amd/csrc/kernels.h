@@ -103,6 +103,7 @@ struct TileLaunch {
   unsigned long long* words;    // boundary_tile_words(tile_rows, hidden) tagged partials
   int tile_rows;                // rows the words cover (the handle's), >= the call's rows
   int wgs_per_xcd;              // resident workgroups of the tile kernel on one XCD
+  bool spread;                  // chunk c of every tile on XCD c % 8 (else a tile per XCD)
 };
 int boundary_tile_resident_wgs_per_cu();
 int boundary_tile_chunks(int hidden);

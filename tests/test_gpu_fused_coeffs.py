@@ -313,3 +313,33 @@ def test_fused_calls_beside_a_gemm_on_another_stream():
         for x, y in zip(o["next"], alone_next):
             assert np.array_equal(N(x), y)
     assert h.errors() == 0
+
+
+@pytest.mark.parametrize("kind,rows,hidden", [("boundary", 128, 7168), ("finalize", 32, 7168),
+                                              ("boundary", 5, 2080), ("finalize", 200, 7168),
+                                              ("boundary", 17, 1024), ("boundary", 48, 8192)])
+def test_tile_placements_give_identical_results(kind, rows, hidden):
+    """MHC_OPT_TILE_PLACEMENT only moves where a tile's chunks run: every output of the fused
+    call (undeferred and deferred) is bit-identical under both placements, and matches the
+    oracle."""
+    say(f"case: fused {kind} rows={rows} hidden={hidden}: tile per XCD vs chunks spread")
+    mx = hidden % 32 == 0
+    d = _inputs(kind, 900 + rows, rows, hidden, mx)
+    nxt, c = _next_args(901 + rows, hidden)
+    out = {}
+    for placement in (binding.MHC_TILE_PER_XCD, binding.MHC_TILE_SPREAD):
+        h = handle_for(hidden, rows)
+        h.set_option(binding.MHC_OPT_TILE_PLACEMENT, placement)
+        out[placement] = _run_fused(h, kind, d, nxt, mx)
+        assert h.errors() == 0
+    (a, na), (b, nb) = out[binding.MHC_TILE_PER_XCD], out[binding.MHC_TILE_SPREAD]
+    for k in a:
+        assert np.array_equal(a[k], b[k]), f"{k} differs between placements"
+    for x, y in zip(na, nb):
+        assert np.array_equal(x, y), "next coefficients differ between placements"
+    want = oracle_boundary(d) if kind == "boundary" else oracle_finalize(d)
+    compare_boundary_outputs(b, want, f"spread {kind} {rows}x{hidden}")
+    for name, x, y in zip(("pre", "post", "comb"), nb, _oracle_next(b["residual"], c)):
+        assert_f32_close(x, y, f"spread {kind} {rows}x{hidden} next {name}")
+    with pytest.raises(binding.MhcValueError):
+        h.set_option(binding.MHC_OPT_TILE_PLACEMENT, 2)

@@ -205,3 +205,20 @@ def test_graph_replays_of_a_deferred_fused_chain():
         _chain(h, 2, False, inputs)
         torch.cuda.synchronize()
     assert h.errors() == 0
+
+
+def test_deferred_fused_chain_with_spread_tiles_equals_tile_per_xcd():
+    """A chain of deferred fused calls gives the same bits with a tile's chunks spread over the
+    XCDs as with each tile on one XCD (MHC_OPT_TILE_PLACEMENT)."""
+    rows, hidden = 128, 7168
+    say(f"case: chain of 6 deferred fused calls, spread vs per-XCD tiles rows={rows}")
+    inputs = _chain_inputs(rows, hidden)
+    out = []
+    for placement in (binding.MHC_TILE_PER_XCD, binding.MHC_TILE_SPREAD):
+        h = handle_for(hidden, rows)
+        h.set_option(binding.MHC_OPT_TILE_PLACEMENT, placement)
+        out.append([N(t) for t in _chain(h, 6, True, inputs)])
+        torch.cuda.synchronize()
+        assert h.errors() == 0
+    for i, (x, y) in enumerate(zip(*out)):
+        assert np.array_equal(x, y), f"chain output {i} differs between placements"
