@@ -224,6 +224,35 @@ int mhc_boundary(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_
                  mhc_stream_t stream);
 
 /*
+ * mhc_boundary_noalloc -- mhc_boundary for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, hosts that forbid hipMalloc): no
+ * handle, and no allocation by the library at any call.
+ *
+ * Computes exactly what mhc_boundary computes on a handle with default options (same
+ * kernels, launch shape and order of sums, so the outputs are bit-identical), with the
+ * same arguments, layouts, aliasing and validation, hc_mult = 4, on the current HIP device.
+ * The row handoff's words, epochs and marks live in a fixed array of 256.25 KiB in device
+ * memory (one copy per GPU, held until the process ends) instead of a handle's scratch:
+ *   rows   in [0, 1024]   (0: no-op)          else MHC_ERR_LIMIT (beyond the array)
+ *   hidden a multiple of 8, at most 16384     else MHC_ERR_SHAPE / MHC_ERR_LIMIT
+ *   tp     in [1, 64]                         else MHC_ERR_SHAPE / MHC_ERR_LIMIT
+ * The first call on each device sets it up: it looks up the array's address on that device
+ * and the kernels' occupancy there, and zeroes the array on `stream` (a fill kernel, ahead
+ * of the call's own). Make one call outside any graph capture first. reset != 0 zeroes the
+ * array again on `stream` before the call: needed only after a call whose handoff wait
+ * gave up (its NaN outputs show it; the conventions above apply, with this array for the
+ * handle's scratch, and no count is kept).
+ * Every call on a device shares that device's array, which keeps the last call's state:
+ * calls that overlap on one device (different streams, or different host threads without
+ * ordering) race on it and give wrong layer inputs. Issue them in one stream order.
+ */
+int mhc_boundary_noalloc(int hidden, const uint16_t* x_partials, int tp,
+                         const uint16_t* residual, const float* post, const float* comb,
+                         const float* pre, const uint16_t* norm_weight, float norm_eps, int rows,
+                         uint16_t* residual_out, uint16_t* layer_input_out, uint8_t* mx_data_out,
+                         uint8_t* mx_scale_out, int reset, mhc_stream_t stream);
+
+/*
  * mhc_residual_only -- reduce and mix only: writes residual_out and nothing else.
  *
  * boundary page, Boundaries.post_only and Boundaries._reduce (without a pre

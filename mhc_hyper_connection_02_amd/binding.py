@@ -68,6 +68,8 @@ _SIGS = {
                              ctypes.POINTER(CoeffArgs), _vp], _i),
     "mhc_finalize_coeffs": ([_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _i, _vp,
                              _vp, _vp, _vp, ctypes.POINTER(CoeffArgs), _vp], _i),
+    "mhc_boundary_noalloc": ([_i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _f, _i, _vp, _vp, _vp, _vp,
+                              _i, _vp], _i),
     # include/mhc_floor.h: measurement floors of the boundary's launch geometry
     "mhc_floor_boundary_traffic": ([_vp, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp], _i),
     "mhc_floor_empty": ([_i, _i, _vp], _i),
@@ -279,6 +281,43 @@ def boundary(h, x_partials, residual, post, comb, pre=None, norm_weight=None, ep
                                      _ptr(ro), _ptr(li), _ptr(md), _ptr(ms), _stream(stream))
     _check(st, "mhc_boundary")
     return _result(ro, li, md, ms)
+
+
+def boundary_noalloc(x_partials, residual, post, comb, pre=None, norm_weight=None, eps=0.0,
+                     mxfp8=False, residual_out=None, layer_input_out=None, mx_out=None,
+                     reset=False, stream=None):
+    """``mhc_boundary_noalloc``: ``boundary`` without a handle (the library allocates nothing;
+    outputs not passed in are allocated here by torch)."""
+    if x_partials.dim() != 3 or residual.dim() != 3:
+        raise ValueError("x_partials must be [tp, rows, hidden], residual [rows, 4, hidden]")
+    tp, rows, hidden = x_partials.shape
+    dev = residual.device
+    _need(x_partials, "x_partials", torch.bfloat16, (tp, rows, hidden), dev)
+    _need(residual, "residual", torch.bfloat16, (rows, 4, hidden), dev)
+    _need(post, "post", torch.float32, (rows, 4), dev)
+    _need(comb, "comb", torch.float32, (rows, 4, 4), dev)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    _need(residual_out, "residual_out", torch.bfloat16, (rows, 4, hidden), dev)
+    li = md = ms = None
+    if pre is not None:
+        _need(pre, "pre", torch.float32, (rows, 4), dev)
+        _need(norm_weight, "norm_weight", torch.bfloat16, (hidden,), dev)
+        li = layer_input_out if layer_input_out is not None else torch.empty(
+            (rows, hidden), dtype=torch.bfloat16, device=dev)
+        _need(li, "layer_input_out", torch.bfloat16, (rows, hidden), dev)
+        if mxfp8:
+            md, ms = mx_out if mx_out is not None else (
+                torch.empty((rows, hidden), dtype=torch.uint8, device=dev),
+                torch.empty((rows, hidden // 32), dtype=torch.uint8, device=dev))
+            _need(md, "mx_data_out", torch.uint8, (rows, hidden), dev)
+            _need(ms, "mx_scale_out", torch.uint8, (rows, hidden // 32), dev)
+    st = load_library().mhc_boundary_noalloc(
+        hidden, _ptr(x_partials), tp, _ptr(residual), _ptr(post), _ptr(comb), _ptr(pre),
+        _ptr(norm_weight), float(eps), rows, _ptr(residual_out), _ptr(li), _ptr(md), _ptr(ms),
+        int(bool(reset)), _stream(stream))
+    _check(st, "mhc_boundary_noalloc")
+    return _result(residual_out, li, md, ms)
 
 
 def residual_only(h, x_partials, residual, post, comb, residual_out=None, stream=None):

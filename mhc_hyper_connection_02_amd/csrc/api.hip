@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "kernels.h"
@@ -193,6 +195,70 @@ hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned value, hipStream_t st
 
 }  // namespace mhc
 
+// ---------------------------------------------------------------------------
+// The allocation-free boundary (mhc_boundary_noalloc): the row handoff's words, epochs and
+// error word live in a fixed array in device memory, one copy per GPU, instead of a
+// handle's hipMalloc. Its size bounds the rows (one 128-byte line of words and one of
+// epochs per row) and the chunks per row (16, i.e. hidden <= 16384).
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kNoAllocRows = 1024;
+constexpr int kNoAllocSlotStride = 16;
+constexpr int kNoAllocMaxHidden = 16384;
+constexpr size_t kNoAllocSlotBytes = (size_t)kNoAllocRows * kNoAllocSlotStride * 8;
+constexpr size_t kNoAllocEpochBytes = (size_t)kNoAllocRows * mhc::kEpochStride * 4;
+constexpr size_t kNoAllocBytes = kNoAllocSlotBytes + kNoAllocEpochBytes + 256;
+constexpr int kNoAllocMaxDevices = 64;
+
+struct NoAllocDevice {
+  std::atomic<int> ready;  // set-up done on this device
+  char* scratch;           // this device's copy of `scratch` (from hipGetSymbolAddress)
+  int wgs_per_xcd[3];      // resident layer-input workgroups per XCD at 128 / 256 / 512
+};
+NoAllocDevice g_noalloc[kNoAllocMaxDevices];
+std::mutex g_noalloc_mu;
+
+}  // namespace
+
+// In host code this name stands for the array but is not its device address: kernels and
+// fills get the address each device reports at set-up.
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+namespace {
+
+// Once per device, with that device current: the array's address on it, the kernels'
+// occupancy there, and the array zeroed on `stream` before the first call's kernels.
+int noalloc_setup(int dev, hipStream_t stream, NoAllocDevice** out) {
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return MHC_ERR_UNSUPPORTED;
+  NoAllocDevice& d = g_noalloc[dev];
+  if (d.ready.load(std::memory_order_acquire) == 0) {
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    if (d.ready.load(std::memory_order_relaxed) == 0) {
+      void* ptr = nullptr;
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+        return MHC_ERR_HIP;
+      int cus = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+              hipSuccess ||
+          cus < 8)
+        return MHC_ERR_HIP;
+      const int blocks[3] = {128, 256, 512};
+      for (int i = 0; i < 3; ++i)
+        d.wgs_per_xcd[i] = mhc::boundary_resident_wgs_per_cu(blocks[i]) * (cus / 8);
+      if (mhc::launch_fill_u32(static_cast<unsigned*>(ptr), kNoAllocBytes / 4, 0u, stream) !=
+          hipSuccess)
+        return MHC_ERR_HIP;
+      d.scratch = static_cast<char*>(ptr);
+      d.ready.store(1, std::memory_order_release);
+    }
+  }
+  *out = &d;
+  return MHC_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* mhc_status_string(int status) {
@@ -201,7 +267,9 @@ const char* mhc_status_string(int status) {
     case MHC_ERR_INVALID_ARG: return "MHC_ERR_INVALID_ARG: null or inconsistent argument";
     case MHC_ERR_SHAPE: return "MHC_ERR_SHAPE: invalid size";
     case MHC_ERR_ALIGN: return "MHC_ERR_ALIGN: misaligned pointer";
-    case MHC_ERR_LIMIT: return "MHC_ERR_LIMIT: rows or tp above the handle's limit";
+    case MHC_ERR_LIMIT:
+      return "MHC_ERR_LIMIT: rows, tp or hidden above the limit (the handle's, or the "
+             "allocation-free call's fixed scratch)";
     case MHC_ERR_UNSUPPORTED: return "MHC_ERR_UNSUPPORTED: unsupported configuration";
     case MHC_ERR_HIP: return "MHC_ERR_HIP: HIP runtime call failed";
     case MHC_ERR_DEVICE: return "MHC_ERR_DEVICE: current device is not the handle's device";
@@ -431,6 +499,62 @@ int mhc_boundary(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_
   st = take_pending(h, L, post, comb, pre, rows, static_cast<hipStream_t>(stream));
   if (st != MHC_OK) return st;
   return launch_status(mhc::launch_boundary(L, static_cast<hipStream_t>(stream)));
+}
+
+int mhc_boundary_noalloc(int hidden, const uint16_t* x_partials, int tp,
+                         const uint16_t* residual, const float* post, const float* comb,
+                         const float* pre, const uint16_t* norm_weight, float norm_eps, int rows,
+                         uint16_t* residual_out, uint16_t* layer_input_out, uint8_t* mx_data_out,
+                         uint8_t* mx_scale_out, int reset, mhc_stream_t stream) {
+  if (hidden <= 0 || hidden % 8 != 0 || rows < 0 || tp < 1) return MHC_ERR_SHAPE;
+  if (hidden > kNoAllocMaxHidden || rows > kNoAllocRows || tp > kMaxTp) return MHC_ERR_LIMIT;
+  if (rows == 0) return MHC_OK;
+  if (!x_partials) return MHC_ERR_INVALID_ARG;
+  // a context on the stack: the device's set-up and this call's hidden size, with the
+  // handle's defaults (automatic block size, two elements per lane, row-major scales)
+  mhc_ctx h{};
+  h.hidden = hidden;
+  h.hc_mult = kHcMult;
+  h.max_rows = kNoAllocRows;
+  h.max_tp = kMaxTp;
+  h.top_k = 1;
+  h.slot_stride = kNoAllocSlotStride;
+  h.spin_limit = kDefaultSpinLimit;
+  h.scale_layout = MHC_SCALE_ROW_MAJOR;
+  h.lane_elems = 2;
+  int st = check_mix(&h, residual, post, comb, pre, norm_weight, norm_eps, residual_out,
+                     layer_input_out, mx_data_out, mx_scale_out);
+  if (st != MHC_OK) return st;
+  if (!aligned(x_partials, 16)) return MHC_ERR_ALIGN;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MHC_ERR_HIP;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  NoAllocDevice* d = nullptr;
+  st = noalloc_setup(dev, s, &d);
+  if (st != MHC_OK) return st;
+  h.device = dev;
+  for (int i = 0; i < 3; ++i) h.wgs_per_xcd[i] = d->wgs_per_xcd[i];
+  h.block = 0;
+  for (int b : {kDefaultBlock, 256, 512}) {
+    if (block_usable(&h, b)) {
+      h.block = b;
+      break;
+    }
+  }
+  if (h.block == 0) return MHC_ERR_UNSUPPORTED;
+  h.block_many = block_usable(&h, kManyRowsBlock) ? kManyRowsBlock : h.block;
+  h.slots = reinterpret_cast<unsigned long long*>(d->scratch);
+  h.epoch = reinterpret_cast<unsigned*>(d->scratch + kNoAllocSlotBytes);
+  h.errors = reinterpret_cast<unsigned*>(d->scratch + kNoAllocSlotBytes + kNoAllocEpochBytes);
+  if (reset && mhc::launch_fill_u32(reinterpret_cast<unsigned*>(d->scratch), kNoAllocBytes / 4,
+                                    0u, s) != hipSuccess)
+    return MHC_ERR_HIP;
+  mhc::BoundaryLaunch L = {};
+  L.x_partials = x_partials;
+  L.tp = tp;
+  fill_mix(&h, L, residual, post, comb, pre, norm_weight, norm_eps, rows, residual_out,
+           layer_input_out, mx_data_out, mx_scale_out);
+  return launch_status(mhc::launch_boundary(L, s));
 }
 
 int mhc_residual_only(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_t* residual,
