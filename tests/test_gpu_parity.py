@@ -13,8 +13,8 @@ from oracle import codecs
 from mhc_hyper_connection_02_amd import binding, synth
 
 from gpu_helpers import (T, N, say, assert_bf16_close, assert_f32_close, handle_for,
-                         gpu_boundary, oracle_boundary, gpu_finalize, oracle_finalize,
-                         compare_boundary_outputs)
+                         with_stated_comb, gpu_boundary, oracle_boundary, gpu_finalize,
+                         oracle_finalize, compare_boundary_outputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,8 +24,8 @@ pytestmark = pytest.mark.gpu
 # ---------------------------------------------------------------------------
 
 def test_config0_tiny_boundary():
-    say("case: config 0 boundary rows=4 hidden=1024 tp=2")
-    d = synth.config(0)
+    say("case: config 0 boundary rows=4 hidden=1024 tp=2, comb = Sinkhorn(exp N(0,1))")
+    d = with_stated_comb(synth.config(0), 1000)
     h = handle_for(1024, 4, tp=2)
     g = gpu_boundary(h, d)
     o = oracle_boundary(d)
@@ -35,8 +35,8 @@ def test_config0_tiny_boundary():
 
 
 def test_config1_decode_boundary_mxfp8_and_determinism():
-    say("case: config 1 boundary rows=32 hidden=7168 tp=8 mxfp8")
-    d = synth.config(1)
+    say("case: config 1 boundary rows=32 hidden=7168 tp=8 mxfp8, comb = Sinkhorn(exp N(0,1))")
+    d = with_stated_comb(synth.config(1), 1001)
     h = handle_for(7168, 32, tp=8)
     g = gpu_boundary(h, d)
     o = oracle_boundary(d)
@@ -48,8 +48,8 @@ def test_config1_decode_boundary_mxfp8_and_determinism():
 
 
 def test_config1_residual_only_equals_full_streams():
-    say("case: config 1 residual-only rows=32 hidden=7168 tp=8")
-    d = synth.config(1)
+    say("case: config 1 residual-only rows=32 hidden=7168 tp=8, comb = Sinkhorn(exp N(0,1))")
+    d = with_stated_comb(synth.config(1), 1001)
     h = handle_for(7168, 32, tp=8)
     ro = gpu_boundary(h, d, residual_only=True)
     full = gpu_boundary(h, d)
@@ -62,8 +62,8 @@ def test_config1_residual_only_equals_full_streams():
 
 
 def test_config2_moe_finalize_mxfp8():
-    say("case: config 2 finalize rows=64 top_k=8 hidden=7168 mxfp8")
-    d = synth.config(2)
+    say("case: config 2 finalize rows=64 top_k=8 hidden=7168 mxfp8, comb = Sinkhorn(exp N(0,1))")
+    d = with_stated_comb(synth.config(2), 1002)
     h = handle_for(7168, 64, tp=1, top_k=8)
     g = gpu_finalize(h, d)
     o = oracle_finalize(d)
