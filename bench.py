@@ -12,10 +12,11 @@ same way and reported under "rows", as is the 61-layer chained decode step
 
 Timing: W eager warm-up calls; then one HIP graph of EXACTLY K calls and one
 of 2K calls (the caller's graph is how the path runs in a decode step), each
-replayed once between two events recorded on the launch stream. The per-call
-time is the slope, (t(2K) - t(K)) / K: the replay's fixed cost cancels, so
-it does not depend on K; t(K) / K, with that cost, and the eager per-call
-time of K calls launched one by one are reported beside it. Before each
+replayed five times, interleaved, between two events recorded on the launch
+stream. The per-call time is the slope between the medians, (t(2K) - t(K)) / K:
+the replay's fixed cost cancels, so it does not depend on K; t(K) / K, with
+that cost, and the eager per-call time of K calls launched one by one are
+reported beside it. Before each
 timed region a spacer (the headline call over its own >= 512 MB of buffer
 sets, twice the 256 MB Infinity Cache) evicts whatever the untimed work left
 in the cache and keeps the GPU busy while the host enqueues the timed work.
@@ -120,6 +121,7 @@ def bytes_collapse_norm(rows, hidden, n=4):
 
 GRAPH_ONLY = False
 _SPACER = []
+REPEATS = 5  # replays of each graph; the medians give the slope
 
 
 def set_spacer(torch, calls):
@@ -166,10 +168,10 @@ def time_calls(torch, calls, steps, warmup):
 
     Returns (eager, graph, graph_single) microseconds per call. graph: the slope between one
     HIP graph of exactly `steps` calls and one of 2 * `steps` (the second continuing over the
-    buffer sets), each replayed once behind a cache flush: the replay's fixed cost cancels,
-    so the figure does not depend on `steps`. graph_single: the `steps`-call graph's time per
-    call, that fixed cost included. eager: `steps` calls launched one by one (None under
-    --graph-only)."""
+    buffer sets), each replayed REPEATS times, interleaved, each replay behind a cache flush,
+    from the median times: the replay's fixed cost cancels, so the figure does not depend on
+    `steps`. graph_single: the `steps`-call graph's median time per call, that fixed cost
+    included. eager: `steps` calls launched one by one (None under --graph-only)."""
     nset = len(calls)
     for i in range(warmup):
         calls[i % nset]()
@@ -187,11 +189,14 @@ def time_calls(torch, calls, steps, warmup):
         g.replay()  # untimed: the first replay uploads the graph
         graphs.append(g)
     torch.cuda.synchronize()
-    t1 = _timed(torch, graphs[0].replay)
-    t2 = _timed(torch, graphs[1].replay)
+    t1, t2 = [], []
+    for _ in range(REPEATS):  # interleaved, each behind its own spacer
+        t1.append(_timed(torch, graphs[0].replay))
+        t2.append(_timed(torch, graphs[1].replay))
     del graphs
+    m1, m2 = sorted(t1)[REPEATS // 2], sorted(t2)[REPEATS // 2]
     eager_us = None if eager_ms is None else eager_ms / steps * 1e3
-    return eager_us, (t2 - t1) / steps * 1e3, t1 / steps * 1e3
+    return eager_us, (m2 - m1) / steps * 1e3, m1 / steps * 1e3
 
 
 def n_sets(bytes_per_set):
@@ -697,10 +702,11 @@ def main():
                                "hc_mult=4 tp=8 (bf16 in/out, fp32 arithmetic)",
                    "rows": R, "hidden": H, "hc_mult": 4, "tp": TP, "mxfp8": True,
                    "block": block, "lane_elems": lane_elems, "buffer_sets": head["buffer_sets"],
-                   "timing": "slope between one HIP graph of exactly K calls and one of 2K, "
-                             "each replayed between two events on the launch stream behind a "
-                             "cache-evicting spacer (the same call on >= 512 MB of other "
-                             "buffers); call i on buffer set i mod buffer_sets (>= 512 MB)"},
+                   "timing": "slope between the median times of one HIP graph of exactly K "
+                             "calls and one of 2K, each replayed 5 times between two events "
+                             "on the launch stream behind a cache-evicting spacer (the same "
+                             "call on >= 512 MB of other buffers); call i on buffer set i mod "
+                             "buffer_sets (>= 512 MB)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": nb,
