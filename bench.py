@@ -341,18 +341,21 @@ def main():
         log(f"  chain deferred {out['chain_decode_step_deferred']}")
         del s3
 
-        for side in (False, True):
-            s2 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, standin=True,
-                                       side_stream=side)
-            e2, g2, _ = time_calls(torch, [s2.run], k, 2)
-            name = "chain_standin_side_stream" if side else "chain_standin_inline"
-            out[name] = {"us_per_step": round(g2, 1),
-                         "us_per_step_eager": None if e2 is None else round(e2, 1),
-                         "note": "boundaries + one [R,H]x[H,H] bf16 GEMM per sublayer as a "
-                                 "stand-in; coefficient calls " + ("on a side stream, joined "
-                                 "before the next boundary" if side else "inline")}
-            log(f"  {name} {out[name]}")
-            del s2
+        for cols, tag in ((None, ""), (1024, "_narrow")):
+            for side in (False, True):
+                s2 = chain_mod.DecodeChain(step.h, step.emb, step.subs, step.p, dev, standin=True,
+                                           side_stream=side, standin_cols=cols)
+                e2, g2, _ = time_calls(torch, [s2.run], k, 2)
+                name = f"chain_standin{tag}_" + ("side_stream" if side else "inline")
+                shape = "[R,H]x[H,H]" if cols is None else f"[R,H]x[H,{cols}]"
+                out[name] = {"us_per_step": round(g2, 1),
+                             "us_per_step_eager": None if e2 is None else round(e2, 1),
+                             "note": f"boundaries + one {shape} bf16 GEMM per sublayer as a "
+                                     "stand-in; coefficient calls " + (
+                                         "on a side stream, joined before the next boundary"
+                                         if side else "inline")}
+                log(f"  {name} {out[name]}")
+                del s2
         del step
         return out
 

@@ -26,7 +26,9 @@ coefficient call after a boundary may run on a second stream while the sublayer
 computes on the layer input, joined before the next boundary. With
 ``standin=True`` each sublayer is stood in for by one bf16 GEMM of the layer input
 ([R, H] x [H, H], a projection's worth of work, outside the hot path and its
-result unused), so that the overlap has something to hide under.
+result unused), so that the overlap has something to hide under; ``standin_cols``
+narrows it to [R, H] x [H, cols], a GEMM with few output tiles that leaves most CUs idle
+(as a decode sublayer of few rows can).
 
 Fused (``fused=True``): each boundary that is followed by a coefficient call runs as one
 call with it (``mhc_boundary_coeffs`` / ``mhc_finalize_coeffs``), which reads the current
@@ -43,7 +45,7 @@ from . import binding, synth
 
 class DecodeChain:
     def __init__(self, handle, embedding, sublayers, params, device, standin=False,
-                 side_stream=False, deferred=False, fused=False):
+                 side_stream=False, deferred=False, fused=False, standin_cols=None):
         """embedding: [R,H] bf16 tensor; sublayers: list of dicts of device tensors as built by
         :meth:`from_synth`; params: rms_eps, hc_eps, post_alpha, sinkhorn_iters, norm_eps."""
         self.h = handle
@@ -80,11 +82,12 @@ class DecodeChain:
         self.side = torch.cuda.Stream(device=device) if side_stream else None
         self.standin_w = self.standin_out = None
         if standin:
+            cols = H if standin_cols is None else standin_cols
             g = torch.Generator(device=device)
             g.manual_seed(1234)
-            self.standin_w = (torch.randn((H, H), generator=g, device=device) * H ** -0.5
+            self.standin_w = (torch.randn((H, cols), generator=g, device=device) * H ** -0.5
                               ).to(torch.bfloat16)
-            self.standin_out = torch.empty((R, H), dtype=torch.bfloat16, device=device)
+            self.standin_out = torch.empty((R, cols), dtype=torch.bfloat16, device=device)
         # optional callback(index, stage, chain) around every boundary: stage "before", "after"
         # (the boundary's outputs), "coeffs" (the coefficient call that follows it); and once
         # with index -1, stage "first", after the first layer's entry
