@@ -297,12 +297,12 @@ int mhc_collapse_mean(mhc_handle h, const uint16_t* streams, int rows, uint16_t*
                       mhc_stream_t stream);
 
 /*
- * mhc_first -- the first layer's entry: the embedding broadcast to the hc
- * streams and the first sublayer's input.
+ * mhc_first -- the first layer's entry: hc copies of the embedding as the
+ * streams, and the first sublayer's input.
  *
- * boundary page, Boundaries.first: the residual streams are the embedding x
- * repeated over the hc streams, and the identity pre-mix selects stream zero,
- * so the layer input is x normalized with the sublayer's norm:
+ * boundary page, Boundaries.first: every residual stream starts as a copy of
+ * the embedding x, and the first pre-mix is the identity on stream 0, so the
+ * layer input is x normalized with the sublayer's norm:
  *   residual_out[r, i, :] = x[r, :]                     (bit for bit, every i)
  *   layer[r, h] = bf16( x[r,h] * (mean_h x[r]^2 + eps)^(-1/2) * w[h] )
  * and the optional MXFP8 form as for mhc_boundary. The coefficients of the

@@ -32,9 +32,9 @@ def _f64(a):
 def tp_reduce(x_partials_bits):
     """Sum of the tensor-parallel partial slices of a sublayer output, [T,R,H] -> [R,H] fp64.
 
-    boundary page, module docstring: every sublayer ends in a TP-partial output
-    that the next boundary reduces across the TP group. On one GPU the T slices
-    are resident and the reduction is their plain sum.
+    boundary page, module docstring: each sublayer leaves its output as partial slices
+    over the tensor-parallel ranks, and the boundary after it adds them up. On one GPU
+    the T slices are resident and the reduction is their plain sum.
     """
     xp = bf16_bits_to_f64(x_partials_bits)
     return xp.sum(axis=0)
@@ -72,8 +72,8 @@ def moe_finalize_sum(gemm2_permuted_bits, expert_weights, expanded_idx_to_permut
 def mhc_post(x_f64, residual_bits, post, comb):
     """New residual streams: s'[r,i] = bf16( sum_j comb[r,i,j] * s[r,j] + post[r,i] * x[r] ).
 
-    boundary page, module docstring (the boundary mixes the reduced output into
-    the hc residual streams) and ``BoundaryState`` (post and comb belong to the
+    boundary page, module docstring (the reduced output is mixed into the streams
+    at the boundary) and ``BoundaryState`` (post and comb belong to the
     sublayer that produced the pending output). Reading: in comb[r,i,j], i is
     the output stream and j the input stream.
     x must already be bf16-valued (it is rounded after the reduction).
@@ -88,9 +88,9 @@ def mhc_post(x_f64, residual_bits, post, comb):
 def collapse(streams_bits, pre):
     """Pre-mix collapse of the streams, y[r] = sum_j pre[r,j] * s[r,j], fp64 [R,H].
 
-    boundary page, module docstring (the boundary collapses the streams into the
-    next sublayer's input) and ``BoundaryState`` (pre is the pre-mix the next
-    collapse uses).
+    boundary page, module docstring (the streams are collapsed to one hidden state,
+    which becomes the following sublayer's input) and ``BoundaryState`` (pre is kept
+    for the collapse at the following boundary).
     """
     s = bf16_bits_to_f64(streams_bits)
     return np.einsum("rj,rjh->rh", _f64(pre), s)
@@ -278,7 +278,7 @@ def decode_chain(embedding_bits, sublayers, rms_eps, hc_eps, post_alpha, sinkhor
     """One decode step's boundaries over all sublayers, fp64 per step.
 
     decode page, ``SpecializedDecode.run``: the first layer enters through
-    ``Boundaries.first`` (the embedding broadcast to the streams); then every
+    ``Boundaries.first`` (every stream starts as a copy of the embedding); then every
     sublayer's output is reduced at the next boundary (``Boundaries.sublayer``),
     and after the last sublayer ``Boundaries.post_only`` reduces it
     residual-only, followed by the streams' mean.
