@@ -175,3 +175,26 @@ def test_floor_calls_reject_bad_sizes_before_any_device_call():
     assert lib.mhc_floor_empty(-1, 1024, z) == 2
     assert lib.mhc_floor_empty(4, 1000, z) == 2
     assert lib.mhc_floor_empty(0, 1024, z) == 0
+
+
+def test_noalloc_boundary_rejects_bad_sizes_before_any_device_call():
+    """mhc_boundary_noalloc validates shapes, limits and pointers before touching the device
+    (these cases never reach a HIP call)."""
+    lib = binding.load_library()
+    z = None
+    q = ctypes.c_void_p(256)
+    assert lib.mhc_boundary_noalloc(7168, q, 8, q, q, q, q, q, 1e-6, 1025, q, q, q, q, 0, z) == 4
+    assert lib.mhc_boundary_noalloc(16392, q, 8, q, q, q, q, q, 1e-6, 4, q, q, q, q, 0, z) == 4
+    assert lib.mhc_boundary_noalloc(7168, q, 65, q, q, q, q, q, 1e-6, 4, q, q, q, q, 0, z) == 4
+    assert lib.mhc_boundary_noalloc(7164, q, 8, q, q, q, q, q, 1e-6, 4, q, q, q, q, 0, z) == 2
+    assert lib.mhc_boundary_noalloc(0, q, 8, q, q, q, q, q, 1e-6, 4, q, q, q, q, 0, z) == 2
+    assert lib.mhc_boundary_noalloc(7168, q, 0, q, q, q, q, q, 1e-6, 4, q, q, q, q, 0, z) == 2
+    assert lib.mhc_boundary_noalloc(7168, q, 8, q, q, q, q, q, 1e-6, -1, q, q, q, q, 0, z) == 2
+    assert lib.mhc_boundary_noalloc(7168, z, 8, q, q, q, q, q, 1e-6, 4, q, q, q, q, 0, z) == 1
+    assert lib.mhc_boundary_noalloc(7168, q, 8, z, q, q, q, q, 1e-6, 4, q, q, q, q, 0, z) == 1
+    # pre without a norm weight; MXFP8 data without scales; misaligned partials
+    assert lib.mhc_boundary_noalloc(7168, q, 8, q, q, q, q, z, 1e-6, 4, q, q, q, q, 0, z) == 1
+    assert lib.mhc_boundary_noalloc(7168, q, 8, q, q, q, q, q, 1e-6, 4, q, q, q, z, 0, z) == 1
+    assert lib.mhc_boundary_noalloc(7168, ctypes.c_void_p(258), 8, q, q, q, q, q, 1e-6, 4, q, q,
+                                    q, q, 0, z) == 3
+    assert lib.mhc_boundary_noalloc(7168, q, 8, q, q, q, q, q, 1e-6, 0, z, z, z, z, 0, z) == 0
