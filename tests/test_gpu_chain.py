@@ -152,10 +152,13 @@ def _compare_end_to_end(step, chains, what, boundaries):
     coefficient 1e-7 off there) move the next coefficients of the whole row, and the
     trajectories drift apart. The bound asserted is the chain's own response to errors the
     per-call tolerance admits, measured on the oracle: chain B, whose every coefficient set
-    is perturbed by up to 1e-5 relative. The GPU's RMS difference from A must not exceed
-    B's, nor its largest difference B's largest plus the bf16 tolerance; and no element may
-    exceed the worst case of one bf16 ulp of the row's largest stream per boundary on top of
-    the bf16 tolerance. Prints the statistics."""
+    is perturbed by up to 1e-5 relative. Once the drift saturates (tens of layers), the GPU
+    chain and chain B are two draws of the same decorrelated drift, whose RMS over millions
+    of elements varies by well under a percent; so the GPU's RMS difference from A may be at
+    most 1.25 times B's, and its largest difference at most twice B's largest plus the bf16
+    tolerance (a transposed comb or a dropped term moves the RMS by orders of magnitude);
+    and no element may exceed the worst case of one bf16 ulp of the row's largest stream per
+    boundary on top of the bf16 tolerance. Prints the statistics."""
     (sa, ma), (sb, mb) = chains["A"], chains["B"]
     for name, got, want, ref in (("streams", N(step.streams), sa, sb),
                                  ("mean", N(step.mean), ma, mb)):
@@ -176,8 +179,8 @@ def _compare_end_to_end(step, chains, what, boundaries):
             f"coefficients perturbed within tolerance: bit-identical {np.mean(ref == want):.4%}, "
             f"max {err_b.max():.4g}, RMS {rms(err_b):.2e}")
         assert np.all(err <= tol + boundaries * ulp_row), f"{what}: {name} beyond the worst case"
-        assert rms(err) <= rms(err_b), f"{what}: {name}: RMS drift above the oracle's own"
-        assert err.max() <= err_b.max() + 2e-2 + 1e-2 * np.abs(o).max(), (
+        assert rms(err) <= 1.25 * rms(err_b), f"{what}: {name}: RMS drift above the oracle's own"
+        assert err.max() <= 2 * err_b.max() + 2e-2 + 1e-2 * np.abs(o).max(), (
             f"{what}: {name}: largest drift above the oracle's own")
 
 
