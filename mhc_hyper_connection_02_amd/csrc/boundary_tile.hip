@@ -467,13 +467,21 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
     const int mm = lane & 15, kg = lane >> 4;
     const int hg = wave * 4 + kg;  // vector of the chunk
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    // logits 16..31, of which 24..31 are zero: the load reads a row that exists and the
+    // value is masked, so it stays an LDS read (a select between the LDS row and a zero in
+    // a local variable compiled to a generic load from either place, whose wait then also
+    // waited for every store the wave had in flight)
+    const bool hi_ok = 16 + mm < kCoefNC;
+    const uint32_t keep = hi_ok ? ~0u : 0u;
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       const int kl = i * kTileH + hg * 8;
       const uint4 a0 = *reinterpret_cast<const uint4*>(&S.fnT[mm][kl]);
-      const uint4 a1 =
-          (16 + mm < kCoefNC) ? *reinterpret_cast<const uint4*>(&S.fnT[16 + mm][kl]) : zero;
+      uint4 a1 = *reinterpret_cast<const uint4*>(&S.fnT[hi_ok ? 16 + mm : mm][kl]);
+      a1.x &= keep;
+      a1.y &= keep;
+      a1.z &= keep;
+      a1.w &= keep;
       const bf16x8_t b = __builtin_bit_cast(bf16x8_t, S.sT[i][mm][hg]);
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), b, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), b, acc1, 0, 0, 0);

@@ -112,13 +112,23 @@ __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const Pr
 
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float sq = 0.f;
+  // logits 16..31, of which 24..31 are zero: the load reads a row that exists and the value
+  // is masked, so it stays an LDS read (a select between the LDS row and a zero in a local
+  // variable compiled to a generic load from either place, with a wait for every
+  // outstanding memory access)
+  const bool hi_ok = 16 + m < kNC;
+  const uint32_t keep = hi_ok ? ~0u : 0u;
 #pragma unroll
   for (int i = 0; i < kMaxWaveSteps; ++i) {
     const int sl = wave + kPreWaves * i;
     if (s0 + sl < s1) {
       const int kl = sl * kStepK + kg * 8;  // k offset inside the slice
       const uint4 a0 = *reinterpret_cast<const uint4*>(&fnT[m][kl]);
-      const uint4 a1 = (16 + m < kNC) ? *reinterpret_cast<const uint4*>(&fnT[16 + m][kl]) : zero;
+      uint4 a1 = *reinterpret_cast<const uint4*>(&fnT[hi_ok ? 16 + m : m][kl]);
+      a1.x &= keep;
+      a1.y &= keep;
+      a1.z &= keep;
+      a1.w &= keep;
       const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv[i]);
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), b, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), b, acc1, 0, 0, 0);
