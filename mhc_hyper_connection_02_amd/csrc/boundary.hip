@@ -585,6 +585,7 @@ __global__ __launch_bounds__(BS, DEFER ? 4 : 1) void boundary_kernel(const Bound
                                                       const int* __restrict__ idx,
                                                       const float* __restrict__ ew,
                                                       const DeferArg<DEFER> dp) {
+  prefetch_kernargs<sizeof(BoundaryParams) + 5 * sizeof(void*) + sizeof(DeferArg<DEFER>)>();
   // the layer-input kernels (with the row handoff) run one lane per vector; the
   // residual-only kernels run four lanes per vector
   __shared__ float s_red[BS / kWave];

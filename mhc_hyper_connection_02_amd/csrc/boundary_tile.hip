@@ -102,7 +102,7 @@ struct TileParams {
                             // `groups` = ceil(chunks / 8) chunks of each tile per XCD
   union {
     float* next_pre;        // [rows][4]
-    float* part_out;        // DEFER_OUT: [rows][25][part_ks] partials of the next call
+    float* part_out;        // DEFER_OUT: partials of the next call (coeff_part_index, part_ks)
   };
   float* next_post;         // [rows][4]
   float* next_comb;         // [rows][16]
@@ -145,7 +145,7 @@ __device__ __forceinline__ float half_wave_sum(float v) {
 }
 
 // A pending coefficient call finished in this kernel: its epilogue arguments, with `part`
-// its per-chunk partial sums ([rows][25][ks_count], ks_count <= 32) written by the previous
+// its per-chunk partial sums (coeff_part_index, ks_count <= 32) written by the previous
 // fused kernel. A kernel argument of those variants only.
 struct TileDeferIn {
   CoeffEpilogue coef;
@@ -245,11 +245,10 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   float4 dpart[kFinishBatch / 4];
   if constexpr (DEFER_IN) {
     const CoeffEpilogue& e = din->coef;
-    const float4* src = reinterpret_cast<const float4*>(
-        e.part + ((size_t)rl * kCoefPartW + min(vl, kCoefPartW - 1)) * e.ks_count);
+    const int Lc = min(vl, kCoefPartW - 1);
     const int last = e.ks_count / 4 - 1;  // past it: in-bounds repeats, never added
 #pragma unroll
-    for (int u = 0; u < kFinishBatch / 4; ++u) dpart[u] = src[u < last ? u : last];
+    for (int u = 0; u < kFinishBatch / 4; ++u) dpart[u] = coeff_quad(e, rl, Lc, u < last ? u : last);
   }
 
   // --- loads: fn slice (mostly L2 hits), the row's mixes, norm weight, streams, sublayer
@@ -497,7 +496,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   __syncthreads();  // red complete
   // --- the coefficient partials of this chunk (waves added in order), out before the
   // handoff wait so that they travel while it runs; deferred: as plain floats, in the split
-  // layout of the coefficient epilogue ([row][25][split], split = chunk, splits padded to a
+  // layout of the coefficient epilogue (coeff_part_index, split = chunk, splits padded to a
   // multiple of 4 with zeros that chunk 0 writes), read after this kernel has completed
   if (DEFER_OUT && tid < kTileRows * kCoefPartW) {
     const int rr = tid / kCoefPartW, vv = tid % kCoefPartW;
@@ -510,10 +509,10 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
         t = S.rowsum[rr][1];
       }
       const int ks = (p.chunks + 3) & ~3;
-      float* dst = p.part_out + ((size_t)(row0 + rr) * kCoefPartW + vv) * ks;
-      dst[c] = t;
+      const int row = row0 + rr;
+      p.part_out[coeff_part_index(row, vv, c, ks)] = t;
       if (c == 0)
-        for (int z = p.chunks; z < ks; ++z) dst[z] = 0.f;
+        for (int z = p.chunks; z < ks; ++z) p.part_out[coeff_part_index(row, vv, z, ks)] = 0.f;
     }
   }
   if (!DEFER_OUT && tid < kTileRows * kCoefPartW) {
@@ -672,6 +671,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
 template <bool FINALIZE, bool MXFP8, int DEFER, typename... Extra>
 __global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_kernel(const TileParams p,
                                                                         const Extra... d) {
+  prefetch_kernargs<sizeof(TileParams) + (0 + ... + sizeof(Extra))>();
   const TileDeferIn* din = nullptr;
   if constexpr (sizeof...(Extra) > 0) ((din = &d), ...);
 

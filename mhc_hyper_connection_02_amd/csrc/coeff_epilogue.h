@@ -18,7 +18,7 @@ constexpr int kCoefNC = 2 * kCoefN + kCoefN * kCoefN;  // 24 logits
 constexpr int kCoefPartW = kCoefNC + 1;              // + sum of squares
 
 struct CoeffEpilogue {
-  const float* part;     // [rows_pad][25][ks_count] split-K partials
+  const float* part;     // [rows_pad][ks_count / 4][25][4] split-K partials (coeff_part_index)
   const float* scale;    // [3]
   const float* base;     // [24]
   int ks_count;          // a multiple of 4
@@ -42,8 +42,17 @@ struct CoeffPrefetch {
   float4 v[NP];
 };
 
-__device__ __forceinline__ const float4* coeff_src(const CoeffEpilogue& e, int r, int L) {
-  return reinterpret_cast<const float4*>(e.part + ((size_t)r * kCoefPartW + L) * e.ks_count);
+// The split-K partials of a row: value L (logit L < 24, the sum of squares at 24) of split s
+// sits at coeff_part_index(r, L, s, ks): per row, one float4 of four consecutive splits per
+// value, the 25 values of a split quad contiguous. A reader lane of value L then loads its
+// splits four at a time, and the lanes of a row read one contiguous 400-byte block per quad.
+__host__ __device__ __forceinline__ size_t coeff_part_index(int r, int L, int s, int ks) {
+  return (((size_t)r * (ks / 4) + s / 4) * kCoefPartW + L) * 4 + (s & 3);
+}
+
+// Value L's splits 4u .. 4u + 3 of row r.
+__device__ __forceinline__ float4 coeff_quad(const CoeffEpilogue& e, int r, int L, int u) {
+  return *reinterpret_cast<const float4*>(e.part + coeff_part_index(r, L, 4 * u, e.ks_count));
 }
 
 // Lanes 0..24 (logits 0..23 and the sum of squares) load their first splits of row r.
@@ -54,10 +63,10 @@ template <bool ALL_LANES, int NP>
 __device__ __forceinline__ void coeff_row_prefetch(const CoeffEpilogue& e, int r, int L,
                                                    CoeffPrefetch<NP>& f) {
   if (!ALL_LANES && L >= kCoefPartW) return;
-  const float4* src = coeff_src(e, r, L < kCoefPartW ? L : kCoefPartW - 1);
+  const int Lc = L < kCoefPartW ? L : kCoefPartW - 1;
   const int last = e.ks_count / 4 - 1;  // past it: in-bounds repeats, never added
 #pragma unroll
-  for (int u = 0; u < NP; ++u) f.v[u] = src[u < last ? u : last];
+  for (int u = 0; u < NP; ++u) f.v[u] = coeff_quad(e, r, Lc, u < last ? u : last);
 }
 
 __device__ __forceinline__ float coeff_from_sums(const CoeffEpilogue& e, int L, float acc,
@@ -78,14 +87,14 @@ __device__ __forceinline__ float coeff_row_finish(const CoeffEpilogue& e, int r,
 #pragma unroll
     for (int u = 0; u < NP; ++u)
       if (u < n4) acc = (((acc + f.v[u].x) + f.v[u].y) + f.v[u].z) + f.v[u].w;
-    const float4* src = coeff_src(e, r, L < kCoefPartW ? L : kCoefPartW - 1);
+    const int Lc = L < kCoefPartW ? L : kCoefPartW - 1;
     constexpr int kBatch = 16;
     for (int b0 = NP; b0 < n4; b0 += kBatch) {  // splits beyond the prefetched ones
       float4 v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int i = b0 + u;
-        v[u] = src[i < n4 ? i : n4 - 1];  // in-bounds repeats past the end, never added
+        v[u] = coeff_quad(e, r, Lc, i < n4 ? i : n4 - 1);  // in-bounds repeats, never added
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)

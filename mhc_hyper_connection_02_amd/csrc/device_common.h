@@ -183,4 +183,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Touches every 64-byte line of the kernel's argument block in one round of scalar loads.
+// The compiler reads a large argument block in several rounds, each waiting for its loads
+// (it parks the values in VGPR lanes between them); with the lines already in the scalar
+// cache those rounds no longer wait for memory. BYTES: the summed sizes of the explicit
+// arguments, at most the argument segment's size; the first word of each line is read, and
+// only where it lies inside those bytes.
+template <int BYTES>
+__device__ __forceinline__ void prefetch_kernargs() {
+  static_assert(BYTES >= 4, "an argument block of at least one word");
+  const uint32_t* ka = (const uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < (BYTES - 4) / 64 + 1; ++i) t ^= ka[i * 16];
+  asm volatile("" ::"s"(t));
+}
+
 }  // namespace mhc

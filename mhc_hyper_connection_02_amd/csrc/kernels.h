@@ -95,7 +95,7 @@ struct TileLaunch {
   float* next_post;
   float* next_comb;
   float* part_out;              // non-NULL: write the next coefficients' partials here
-                                // ([rows][25][boundary_tile_part_ks(hidden)]) and finish none
+                                // (coeff_part_index, ks = boundary_tile_part_ks(hidden)) and finish none
   bool defer_in;                // b.post, b.comb and b.pre are a pending call's outputs: finish
                                 // them from in_coef.part (another fused kernel's part_out;
                                 // requires part_out) and write them, instead of reading them

@@ -15,8 +15,9 @@
 // afterwards, so no normalized copy is rounded). The MFMA's M side is fn^T
 // (logit columns 0..15 and 16..31, the last 8 zero), its N side the 16 rows.
 // The same pass accumulates the rows' sums of squares. Each workgroup writes
-// its 16 x 25 partials to scratch laid out [row][25][k-split], so that the
-// epilogue reads each (row, logit) range contiguously.
+// its 16 x 25 partials to scratch laid out per row by quads of k-splits
+// (coeff_part_index), so that the epilogue's lanes, one per logit, read
+// contiguous blocks four splits at a time.
 //
 // Kernel 2: one wave per row runs the row's epilogue (coeff_epilogue.h): the
 // k-split partials added in split order, 1/RMS, scale and base, the sigmoids
@@ -45,7 +46,7 @@ constexpr int kLdsPad = 8;
 struct PrePartialParams {
   const uint16_t* res;   // [rows][K] bf16 (the streams, flattened)
   const uint16_t* fn;    // [K][24] bf16
-  float* part;           // [rows_pad][25][ks]
+  float* part;           // [rows_pad][ks / 4][25][4] (coeff_part_index)
   int rows, K, ks_count, steps_per_wg, nsteps;
 };
 
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const Pr
     float t = 0.f;
 #pragma unroll
     for (int w = 0; w < kPreWaves; ++w) t += red[w][rr][cc];
-    p.part[((size_t)(rb * kRB + rr) * kPartW + cc) * p.ks_count + ks] = t;
+    p.part[coeff_part_index(rb * kRB + rr, cc, ks, p.ks_count)] = t;
   }
 }
 
