@@ -429,9 +429,10 @@ typedef struct mhc_coeff_args {
  * layer_input_out non-NULL). Arguments, layouts, aliasing and errors as the two calls,
  * plus MHC_ERR_INVALID_ARG for a NULL `next`; next's outputs must not overlap any other
  * argument. The single kernel runs when rows <= min(max_rows, 1024), post, comb and pre
- * are 16-byte aligned and a row's 256-element pieces fit the workgroups one XCD holds at
- * once (H <= 8192 on MI355X); otherwise the call runs the two calls (same results as
- * above). A pending deferred coefficient call whose outputs are this call's post, comb and
+ * are 16-byte aligned, a row's 256-element pieces fit the workgroups one XCD holds at
+ * once (H <= 8192 on MI355X) and, for mhc_finalize_coeffs, the permuted expert rows span
+ * less than 4 GiB (num_permuted * hidden * 2 bytes); otherwise the call runs the two calls
+ * (same results as above). A pending deferred coefficient call whose outputs are this call's post, comb and
  * pre (same rows) is finished inside the kernel when this call is deferred too and the
  * pending call was a fused one (its partial sums are the fused kernel's); in the two-call
  * form the boundary kernel finishes it; otherwise its epilogue is enqueued first.

@@ -685,8 +685,12 @@ int check_coeff_args(const mhc_coeff_args* a) {
 // the fused form applies, else the two calls. L is the boundary's launch, already filled.
 int boundary_then_coeffs(mhc_ctx* h, mhc::BoundaryLaunch& L, const mhc_coeff_args* a,
                          hipStream_t s) {
+  // (the fused kernel addresses its tensors with 32-bit byte offsets: the gathered MoE rows
+  // must stay below 4 GiB; the others do within its row and hidden limits)
   const bool fused = h->tile_rows >= L.rows && aligned(L.post, 16) && aligned(L.comb, 16) &&
-                     aligned(L.pre, 16);
+                     aligned(L.pre, 16) &&
+                     (L.gemm2_permuted == nullptr ||
+                      (unsigned long long)L.num_permuted * L.hidden * 2 < (1ull << 32));
   // a pending call whose outputs are this call's post, comb and pre is finished inside the
   // kernel: the fused kernel takes it when this call is deferred too and the pending
   // partial sums are a fused kernel's; the boundary kernel of the two-call form takes any

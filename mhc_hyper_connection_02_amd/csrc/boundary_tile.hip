@@ -120,15 +120,19 @@ static_assert(sizeof(TileParams) == 256, "TileParams grew");
 // Handoff words, tile-major: per (tile, chunk) the 16 rows' sums of y^2, then per (tile,
 // chunk, row) the 25 coefficient partials (24 logits, the sum of v^2). One workgroup's
 // words are contiguous.
-__device__ __forceinline__ size_t ysq_index(const TileParams& p, int tile, int c, int rr) {
-  return ((size_t)tile * p.chunks + c) * kTileRows + rr;
+// (The words of a handle of at most 1024 rows and 32 chunks per row: a 32-bit index.)
+__device__ __forceinline__ uint32_t ysq_index(const TileParams& p, int tile, int c, int rr) {
+  return ((uint32_t)tile * p.chunks + c) * kTileRows + rr;
 }
-__device__ __forceinline__ size_t coef_index(const TileParams& p, int tile, int c, int rr,
-                                             int v) {
+__device__ __forceinline__ uint32_t coef_index(const TileParams& p, int tile, int c, int rr,
+                                               int v) {
   // after the y^2 words of every tile the handle holds: each word's place belongs to one
   // row whatever the call's row count, so a stale word carries an older tag of that row
-  const size_t base = (size_t)p.tile_cap * p.chunks * kTileRows;
-  return base + (((size_t)tile * p.chunks + c) * kTileRows + rr) * kCoefPartW + v;
+  const uint32_t base = (uint32_t)p.tile_cap * p.chunks * kTileRows;
+  return base + (((uint32_t)tile * p.chunks + c) * kTileRows + rr) * kCoefPartW + v;
+}
+__device__ __forceinline__ unsigned long long* word_at(const TileParams& p, uint32_t i) {
+  return byte_at(p.words, i * 8u);
 }
 
 __device__ __forceinline__ unsigned long long tagged(unsigned tag, float f) {
@@ -259,14 +263,14 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
     const int i = q / (kTileH * 3), rem = q % (kTileH * 3);
     const int kk = rem / 3, part = rem % 3;
     const int h = min(c * kTileH + kk, (p.hv * 8) - 1);  // past the end: zeroed below
-    fv[j] = p.fn[((size_t)i * (p.hv * 8) + h) * 3 + part];
+    fv[j] = *byte_at(p.fn, (((uint32_t)i * (p.hv * 8) + h) * 3 + part) * 16u);
   }
   float4 pst4, cmb4[kN], pr4;
   if constexpr (!DEFER_IN) {
-    pst4 = p.post[rl];
+    pst4 = *byte_at(p.post, (uint32_t)rl * 16u);
 #pragma unroll
-    for (int i = 0; i < kN; ++i) cmb4[i] = p.comb[rl * kN + i];
-    pr4 = p.pre[rl];
+    for (int i = 0; i < kN; ++i) cmb4[i] = *byte_at(p.comb, ((uint32_t)rl * kN + i) * 16u);
+    pr4 = *byte_at(p.pre, (uint32_t)rl * 16u);
   }
   // DEFER_IN: the pending call's coefficients of rows 2 wave and 2 wave + 1 (this wave's
   // halves), from their partial sums added in chunk order; into LDS, from which each half
@@ -298,24 +302,28 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int uu = u < p.top_k ? u : p.top_k - 1;
-      const int pi = p.idx[rl * p.top_k + uu];
-      const float w = p.ew[rl * p.top_k + uu];
+      const uint32_t o = ((uint32_t)rl * p.top_k + uu) * 4u;
+      const int pi = *byte_at(p.idx, o);
+      const float w = *byte_at(p.ew, o);
       pk[u] = u < p.top_k ? pi : -1;
       wk[u] = u < p.top_k ? w : 0.f;
     }
   }
-  const uint4 wv = p.norm_w[va];
+  // per-lane byte offsets in 32 bits (the tile kernel's tensors are below 4 GiB: rows <= 1024,
+  // hidden <= 8192, tp <= 64, num_permuted * hidden * 2 < 2^32, checked by the host)
+  const uint32_t row_off = ((uint32_t)rl * p.hv + va) * 16u;  // [rows][hv] tensors
+  const uint4 wv = *byte_at(p.norm_w, (uint32_t)va * 16u);
   uint4 sv[kN];
 #pragma unroll
-  for (int j = 0; j < kN; ++j) sv[j] = load_nt(p.res_in + ((size_t)rl * kN + j) * p.hv + va);
+  for (int j = 0; j < kN; ++j)
+    sv[j] = load_nt(byte_at(p.res_in, (((uint32_t)rl * kN + j) * p.hv + va) * 16u));
 
   float x[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] = 0.f;
   if constexpr (!FINALIZE) {
     // t ascending
-    const uint4* src = p.xp + (size_t)rl * p.hv + va;
-    const size_t slice = (size_t)p.rows * p.hv;
+    const uint32_t slice = (uint32_t)p.rows * p.hv * 16u;
     auto add_batch = [&](int t0, const uint4* xv) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -333,7 +341,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
       uint4 xv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (u < p.tp) xv[u] = load_nt(src + (size_t)u * slice);
+        if (u < p.tp) xv[u] = load_nt(byte_at(p.xp, row_off + (uint32_t)u * slice));
       finish_pending();
       add_batch(0, xv);
       t_first = 8;
@@ -342,18 +350,18 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
       uint4 xv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (t0 + u < p.tp) xv[u] = load_nt(src + (size_t)(t0 + u) * slice);
+        if (t0 + u < p.tp) xv[u] = load_nt(byte_at(p.xp, row_off + (uint32_t)(t0 + u) * slice));
       add_batch(t0, xv);
     }
   } else {
     // k ascending, then the shared row
-    const uint4 shv = load_nt(p.shared + (size_t)rl * p.hv + va);
+    const uint4 shv = load_nt(byte_at(p.shared, row_off));
     uint4 gv[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (u < p.top_k) {
         const bool ok = pk[u] >= 0 && pk[u] < p.num_permuted;
-        gv[u] = load_nt(p.g + (size_t)(ok ? pk[u] : 0) * p.hv + va);
+        gv[u] = load_nt(byte_at(p.g, ((uint32_t)(ok ? pk[u] : 0) * p.hv + va) * 16u));
         if (!ok) wk[u] = 0.f;
       }
     }
@@ -368,10 +376,10 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
       }
     }
     for (int k = 8; k < p.top_k; ++k) {  // slots beyond 8, in order
-      const int pi = p.idx[rl * p.top_k + k];
+      const int pi = *byte_at(p.idx, ((uint32_t)rl * p.top_k + k) * 4u);
       const bool ok = pi >= 0 && pi < p.num_permuted;
-      const float w = ok ? p.ew[rl * p.top_k + k] : 0.f;
-      const uint4 gk = load_nt(p.g + (size_t)(ok ? pi : 0) * p.hv + va);
+      const float w = ok ? *byte_at(p.ew, ((uint32_t)rl * p.top_k + k) * 4u) : 0.f;
+      const uint4 gk = load_nt(byte_at(p.g, ((uint32_t)(ok ? pi : 0) * p.hv + va) * 16u));
       float f[8];
       unpack8(gk, f);
 #pragma unroll
@@ -394,7 +402,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   float s[kN][8], sn[kN][8];
 #pragma unroll
   for (int j = 0; j < kN; ++j) unpack8(sv[j], s[j]);
-  uint4* out = p.res_out + (size_t)rl * kN * p.hv + va;
+  const uint32_t out_off = ((uint32_t)rl * kN * p.hv + va) * 16u;
   float vsq = 0.f;
 #pragma unroll
   for (int i = 0; i < kN; ++i) {
@@ -406,7 +414,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
       sn[i][e] = a;
     }
     const uint4 o = pack8_round(sn[i]);
-    if (active) store_nt(out + (size_t)i * p.hv, o);
+    if (active) store_nt(byte_at(p.res_out, out_off + (uint32_t)i * p.hv * 16u), o);
     S.sT[i][m][vl] = active ? o : make_uint4(0u, 0u, 0u, 0u);
     unpack8(o, sn[i]);
 #pragma unroll
@@ -457,7 +465,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
 
   // --- the rows' sums of y^2 go out first (the handoff waits for them)
   if (tid < kTileRows && row0 + tid < p.rows)
-    __hip_atomic_store(p.words + ysq_index(p, tile, c, tid), tagged(S.want[tid], S.rowsum[tid][0]),
+    __hip_atomic_store(word_at(p, ysq_index(p, tile, c, tid)), tagged(S.want[tid], S.rowsum[tid][0]),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // --- partial logits: wave w takes elements 32w .. 32w + 31 of the chunk for all 16 rows;
@@ -510,9 +518,10 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
       }
       const int ks = (p.chunks + 3) & ~3;
       const int row = row0 + rr;
-      p.part_out[coeff_part_index(row, vv, c, ks)] = t;
+      *byte_at(p.part_out, (uint32_t)coeff_part_index(row, vv, c, ks) * 4u) = t;
       if (c == 0)
-        for (int z = p.chunks; z < ks; ++z) p.part_out[coeff_part_index(row, vv, z, ks)] = 0.f;
+        for (int z = p.chunks; z < ks; ++z)
+          *byte_at(p.part_out, (uint32_t)coeff_part_index(row, vv, z, ks) * 4u) = 0.f;
     }
   }
   if (!DEFER_OUT && tid < kTileRows * kCoefPartW) {
@@ -525,7 +534,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
       } else {
         t = S.rowsum[rr][1];
       }
-      __hip_atomic_store(p.words + coef_index(p, tile, c, rr, vv), tagged(S.want[rr], t),
+      __hip_atomic_store(word_at(p, coef_index(p, tile, c, rr, vv)), tagged(S.want[rr], t),
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -541,7 +550,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
       const unsigned want = S.want[m];
       unsigned long long w = 0;
       for (int spins = 0;; ++spins) {
-        w = __hip_atomic_load(p.words + ysq_index(p, tile, cl, m), __ATOMIC_RELAXED,
+        w = __hip_atomic_load(word_at(p, ysq_index(p, tile, cl, m)), __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_AGENT);
         if ((unsigned)(w >> 32) == want) break;
         if (spins >= p.spin_limit) {
@@ -589,7 +598,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
 #pragma unroll
           for (int u = 0; u < kFinishBatch; ++u) {
             const int cc = b0 + u < p.chunks ? b0 + u : p.chunks - 1;
-            w[u] = __hip_atomic_load(p.words + coef_index(p, tile, cc, rt, lane),
+            w[u] = __hip_atomic_load(word_at(p, coef_index(p, tile, cc, rt, lane)),
                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
 #pragma unroll
@@ -630,7 +639,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (y[e] * inv) * w[e];
     const uint4 ob = pack8_round(o);
-    if (active) store_nt(p.layer_out + (size_t)r * p.hv + v, ob);
+    if (active) store_nt(byte_at(p.layer_out, ((uint32_t)r * p.hv + v) * 16u), ob);
     if constexpr (MXFP8) {
       // 32-element block = the quad of lanes holding vectors v & ~3 .. v | 3
       float q[8];
@@ -645,7 +654,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
       const uint32_t lo = cvt_pk4_e4m3(q[0] * sc, q[1] * sc, q[2] * sc, q[3] * sc);
       const uint32_t hi = cvt_pk4_e4m3(q[4] * sc, q[5] * sc, q[6] * sc, q[7] * sc);
       if (active) {
-        store_nt(p.mx_data + (size_t)r * p.hv + v, make_uint2(lo, hi));
+        store_nt(byte_at(p.mx_data, ((uint32_t)r * p.hv + v) * 8u), make_uint2(lo, hi));
         if ((v & 3) == 0)
           p.mx_scale[mx_scale_offset(r, v >> 2, p.hv / 4, p.scale_kt)] =
               inv == inv ? (uint8_t)(ex + 127) : (uint8_t)0xFF;  // NaN: a wait gave up
@@ -696,29 +705,23 @@ __global__ __launch_bounds__(kTileThreads, 2) void boundary_tile_kernel(const Ti
   const int wg = blockIdx.x;
   const int xcd = wg % kXcd;
   const int local = wg / kXcd;
-  if (p.groups == 0) {
-    // a tile's chunks on one XCD: tiles dealt to the XCDs
-    const int c = local % p.chunks;
-    const int jt = local / p.chunks;  // which tile of this XCD's block in a round
-    for (int round = 0; round < p.rounds; ++round) {
-      const int tile = (round * p.tiles_per_round + jt) * kXcd + xcd;
-      if (tile * kTileRows >= p.rows) break;  // uniform per workgroup; later rounds go higher
-      if (round > 0) __syncthreads();          // LDS reused
-      tile_item<FINALIZE, MXFP8, DEFER>(p, coef, din, tile, c, S, sc_l, base_l, dsc_l,
-                                        dbase_l);
-    }
-  } else {
-    // chunk c of every tile on XCD c % 8: each XCD reads the fn rows of its own chunks only
-    const int c = xcd + kXcd * (local % p.groups);
-    const int jt = local / p.groups;  // which tile of the round
-    if (c >= p.chunks) return;        // past the last chunk: no work, in no handoff
-    for (int round = 0; round < p.rounds; ++round) {
-      const int tile = round * p.tiles_per_round + jt;
-      if (tile * kTileRows >= p.rows) break;
-      if (round > 0) __syncthreads();
-      tile_item<FINALIZE, MXFP8, DEFER>(p, coef, din, tile, c, S, sc_l, base_l, dsc_l,
-                                        dbase_l);
-    }
+  // Placement, in one body for both layouts (uniform selects, not two inlined copies):
+  //  groups == 0: a tile's chunks on one XCD, tiles dealt to the XCDs: chunk local % chunks,
+  //    tile (round * tiles_per_round + local / chunks) * 8 + xcd;
+  //  groups > 0: chunk c of every tile on XCD c % 8 (each XCD reads the fn rows of its own
+  //    chunks only): chunk xcd + 8 * (local % groups), tile round * tiles_per_round +
+  //    local / groups.
+  const bool spread = p.groups != 0;
+  const int per = spread ? p.groups : p.chunks;
+  const int c = (spread ? xcd : 0) + (spread ? kXcd : 1) * (local % per);
+  const int jt = local / per;        // which tile of the round
+  if (c >= p.chunks) return;         // past the last chunk (spread only): in no handoff
+  const int tile_mul = spread ? 1 : kXcd, tile_add = spread ? 0 : xcd;
+  for (int round = 0; round < p.rounds; ++round) {
+    const int tile = (round * p.tiles_per_round + jt) * tile_mul + tile_add;
+    if (tile * kTileRows >= p.rows) break;  // uniform per workgroup; later rounds go higher
+    if (round > 0) __syncthreads();          // LDS reused
+    tile_item<FINALIZE, MXFP8, DEFER>(p, coef, din, tile, c, S, sc_l, base_l, dsc_l, dbase_l);
   }
 }
 

@@ -50,9 +50,12 @@ __host__ __device__ __forceinline__ size_t coeff_part_index(int r, int L, int s,
   return (((size_t)r * (ks / 4) + s / 4) * kCoefPartW + L) * 4 + (s & 3);
 }
 
-// Value L's splits 4u .. 4u + 3 of row r.
+// Value L's splits 4u .. 4u + 3 of row r (the partials are far below 4 GiB: a 32-bit
+// byte offset).
 __device__ __forceinline__ float4 coeff_quad(const CoeffEpilogue& e, int r, int L, int u) {
-  return *reinterpret_cast<const float4*>(e.part + coeff_part_index(r, L, 4 * u, e.ks_count));
+  const uint32_t off = ((((uint32_t)r * (uint32_t)(e.ks_count / 4) + (uint32_t)u) * kCoefPartW +
+                         (uint32_t)L) * 16u);
+  return *byte_at(reinterpret_cast<const float4*>(e.part), off);
 }
 
 // Lanes 0..24 (logits 0..23 and the sum of squares) load their first splits of row r.

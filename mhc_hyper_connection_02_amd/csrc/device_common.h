@@ -199,4 +199,16 @@ __device__ __forceinline__ void prefetch_kernargs() {
   asm volatile("" ::"s"(t));
 }
 
+// base plus a byte offset held in 32 bits: a global access then takes its 64-bit base from
+// scalar registers and only a 32-bit offset per lane, with no 64-bit address arithmetic per
+// lane. Callers keep the offset below 2^32.
+template <typename T>
+__device__ __forceinline__ const T* byte_at(const T* base, uint32_t off) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
+}
+template <typename T>
+__device__ __forceinline__ T* byte_at(T* base, uint32_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+
 }  // namespace mhc
