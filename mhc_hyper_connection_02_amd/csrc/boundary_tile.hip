@@ -318,6 +318,26 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   for (int j = 0; j < kN; ++j)
     sv[j] = load_nt(byte_at(p.res_in, (((uint32_t)rl * kN + j) * p.hv + va) * 16u));
 
+  // fn slice -> LDS, transposed to [logit][k] (k = stream * 256 + element of the chunk); run
+  // once every load of the item is issued, while the sublayer output is still in flight (the
+  // fn vectors were loaded first), so that this work is off the arithmetic that follows
+  // the loads, where every wave of the CU competes for the vector units
+  auto stage_fn = [&]() {
+#pragma unroll
+    for (int j = 0; j < kFnVecs; ++j) {
+      const int q = tid + j * kTileThreads;
+      const int i = q / (kTileH * 3), rem = q % (kTileH * 3);
+      const int kk = rem / 3, c0 = (rem % 3) * 8;
+      const bool ok = c * kTileH + kk < (p.hv * 8);
+      const uint32_t u[4] = {ok ? fv[j].x : 0u, ok ? fv[j].y : 0u, ok ? fv[j].z : 0u,
+                             ok ? fv[j].w : 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        S.fnT[c0 + 2 * e][i * kTileH + kk] = (uint16_t)(u[e] & 0xFFFFu);
+        S.fnT[c0 + 2 * e + 1][i * kTileH + kk] = (uint16_t)(u[e] >> 16);
+      }
+    }
+  };
   float x[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] = 0.f;
@@ -335,18 +355,18 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
         }
       }
     };
-    int t_first = 0;
-    if constexpr (DEFER_IN) {
-      // the first slices' loads go out before the pending coefficients are finished
+    {
+      // the first slices' loads go out before the fn staging (and a pending call's
+      // coefficients) run
       uint4 xv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (u < p.tp) xv[u] = load_nt(byte_at(p.xp, row_off + (uint32_t)u * slice));
-      finish_pending();
+      stage_fn();
+      if constexpr (DEFER_IN) finish_pending();
       add_batch(0, xv);
-      t_first = 8;
     }
-    for (int t0 = t_first; t0 < p.tp; t0 += 8) {
+    for (int t0 = 8; t0 < p.tp; t0 += 8) {
       uint4 xv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
@@ -365,6 +385,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
         if (!ok) wk[u] = 0.f;
       }
     }
+    stage_fn();
     if constexpr (DEFER_IN) finish_pending();
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -442,24 +463,9 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
     S.rowsum[m][1] = vsq;
   }
 
-  // --- fn slice -> LDS, transposed to [logit][k] (k = stream * 256 + element of the chunk)
   if (tid < kTileRows) {
     S.want[tid] = epoch_now + 1u;
     S.poisoned[tid] = (unsigned)(ew >> 32);
-  }
-#pragma unroll
-  for (int j = 0; j < kFnVecs; ++j) {
-    const int q = tid + j * kTileThreads;
-    const int i = q / (kTileH * 3), rem = q % (kTileH * 3);
-    const int kk = rem / 3, c0 = (rem % 3) * 8;
-    const bool ok = c * kTileH + kk < (p.hv * 8);
-    const uint32_t u[4] = {ok ? fv[j].x : 0u, ok ? fv[j].y : 0u, ok ? fv[j].z : 0u,
-                           ok ? fv[j].w : 0u};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      S.fnT[c0 + 2 * e][i * kTileH + kk] = (uint16_t)(u[e] & 0xFFFFu);
-      S.fnT[c0 + 2 * e + 1][i * kTileH + kk] = (uint16_t)(u[e] >> 16);
-    }
   }
   __syncthreads();  // fnT, sT, rowsum and want complete
 
