@@ -527,7 +527,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     if (lane == 0) {
-      *s_inv = 1.0f / sqrtf(tot / (float)p.hidden + p.eps);
+      *s_inv = fast_rsq(tot * fast_rcp((float)p.hidden) + p.eps);
       if (c == 0)
         __hip_atomic_store(p.epoch + (size_t)r * kEpochStride, want, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);

@@ -165,23 +165,23 @@ __device__ __forceinline__ float coeff_two_rows(const CoeffEpilogue& e, int L, f
                                                 float sc_l, float base_l, int* slot) {
   const int l = L & 31, hb = L & 32;
   const float ss = __shfl(acc, hb + kCoefNC, kWave);
-  const float inv = 1.0f / sqrtf(ss / (float)e.K + e.rms_eps);
+  const float inv = fast_rsq(ss * fast_rcp((float)e.K) + e.rms_eps);
   float lp = 0.f;
   if (l < kCoefNC) lp = (acc * inv) * sc_l + base_l;
   float out = 0.f;
   *slot = -1;
   if (l < kCoefN) {
-    out = 1.0f / (1.0f + expf(-lp)) + e.pre_eps;
+    out = fast_rcp(1.0f + fast_exp(-lp)) + e.pre_eps;
     *slot = l;
   } else if (l < 2 * kCoefN) {
-    out = e.alpha * (1.0f / (1.0f + expf(-lp)));
+    out = e.alpha * fast_rcp(1.0f + fast_exp(-lp));
     *slot = l;
   }
   const int ce = l - 16;  // comb entry (i, j) = 4i + j at lane 32h + 16 + 4i + j
   float a = __shfl(lp, hb + 2 * kCoefN + (ce & 15), kWave);
   float mx = fmaxf(a, dpp_f32<kDppQuadXor1>(a));
   mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
-  a = expf(a - mx);
+  a = fast_exp(a - mx);
   for (int it = 0; it < e.iters; ++it) {
     float rs = a + dpp_f32<kDppQuadXor1>(a);
     rs = rs + dpp_f32<kDppQuadXor2>(rs);
@@ -578,7 +578,7 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
         __hip_atomic_store(p.epoch + (size_t)r * kEpochStride + 1, 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    inv = 1.0f / sqrtf(tot / (float)(p.hv * 8) + p.eps);
+    inv = fast_rsq(tot * fast_rcp((float)(p.hv * 8)) + p.eps);
     if (c == 0 && row_ok && vl == 0)
       __hip_atomic_store(p.epoch + (size_t)r * kEpochStride, S.want[m], __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);

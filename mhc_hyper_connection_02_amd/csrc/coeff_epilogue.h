@@ -113,16 +113,16 @@ __device__ __forceinline__ float coeff_row_finish(const CoeffEpilogue& e, int r,
 __device__ __forceinline__ float coeff_from_sums(const CoeffEpilogue& e, int L, float acc,
                                                  float sc_l, float base_l, int* slot) {
   const float ss = __shfl(acc, kCoefNC, kWave);
-  const float inv = 1.0f / sqrtf(ss / (float)e.K + e.rms_eps);
+  const float inv = fast_rsq(ss * fast_rcp((float)e.K) + e.rms_eps);
   float lp = 0.f;
   if (L < kCoefNC) lp = (acc * inv) * sc_l + base_l;
   float out = 0.f;
   *slot = -1;
   if (L < kCoefN) {
-    out = 1.0f / (1.0f + expf(-lp)) + e.pre_eps;
+    out = fast_rcp(1.0f + fast_exp(-lp)) + e.pre_eps;
     *slot = L;
   } else if (L < 2 * kCoefN) {
-    out = e.alpha * (1.0f / (1.0f + expf(-lp)));
+    out = e.alpha * fast_rcp(1.0f + fast_exp(-lp));
     *slot = L;
   }
   // comb: the 16 entries sit in lanes 32..47 (one DPP row), entry (i, j) at lane 32 + 4i + j,
@@ -132,7 +132,7 @@ __device__ __forceinline__ float coeff_from_sums(const CoeffEpilogue& e, int L, 
   float a = __shfl(lp, 2 * kCoefN + (ce & 15), kWave);
   float mx = fmaxf(a, dpp_f32<kDppQuadXor1>(a));
   mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
-  a = expf(a - mx);
+  a = fast_exp(a - mx);
   for (int it = 0; it < e.iters; ++it) {
     float rs = a + dpp_f32<kDppQuadXor1>(a);
     rs = rs + dpp_f32<kDppQuadXor2>(rs);

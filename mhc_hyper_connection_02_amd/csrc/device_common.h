@@ -211,4 +211,15 @@ __device__ __forceinline__ T* byte_at(T* base, uint32_t off) {
   return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
 }
 
+// Reciprocal, reciprocal square root and exp on the hardware approximations (about one
+// ulp; exp through exp2 of x log2 e): the coefficient epilogue and the row norms are chains
+// of dependent steps, where the exactly rounded sequences cost 10 to 20 instructions each.
+// The results stay far inside the tolerances (1e-5 for the coefficients, the bf16 rounding
+// of the layer input).
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+}
+
 }  // namespace mhc
