@@ -40,7 +40,12 @@
  *     that a later call would accept): every later call skips that row's
  *     waits and writes its wait-dependent outputs as NaN, until mhc_reset (or
  *     mhc_get_errors with clear) restores the handoff state. The new streams
- *     never depend on a wait and stay exact.
+ *     never depend on a wait and stay exact. A row's workgroups run on one XCD (ids
+ *     congruent mod 8); where mhc_create finds the device dealing workgroup ids to its 8
+ *     XCDs round-robin (it reads the hardware's XCC id over a probe grid), the handoff
+ *     words go through that XCD's L2 (workgroup-scope stores, non-temporal polls that the
+ *     CU's L1 does not keep), else through device-scope accesses
+ *     (MHC_OPT_ROW_HANDOFF).
  *   - The only aliasing allowed is residual_out == residual (in-place update
  *     of the streams); any other overlap of inputs and outputs is undefined.
  *   - Alignment: bf16 tensors 16 bytes; fp32 and int32 tensors 4 bytes;
@@ -140,6 +145,14 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
  *         chunks' rows of fn, and a call of few rows still uses every XCD.
  *     Results are identical either way (the same arithmetic per chunk and the same order
  *     of every sum). Other values: MHC_ERR_SHAPE.
+ *   MHC_OPT_ROW_HANDOFF: how the workgroups of a row exchange their partial sums in
+ *     the layer-input kernels (mhc_boundary, mhc_finalize, mhc_first, mhc_collapse_norm and
+ *     the fused calls' fallback):
+ *       MHC_HANDOFF_XCD (default where available): through the L2 of the row's XCD;
+ *         MHC_ERR_UNSUPPORTED on a device that mhc_create did not find dealing workgroup
+ *         ids to its XCDs round-robin;
+ *       MHC_HANDOFF_DEVICE (default otherwise): device-scope stores and polls.
+ *     Results are identical either way. Other values: MHC_ERR_SHAPE.
  * Unknown options: MHC_ERR_INVALID_ARG.
  */
 enum mhc_option {
@@ -147,10 +160,12 @@ enum mhc_option {
   MHC_OPT_SPIN_LIMIT = 2,
   MHC_OPT_SCALE_LAYOUT = 3,
   MHC_OPT_LANE_ELEMS = 4,
-  MHC_OPT_TILE_PLACEMENT = 5
+  MHC_OPT_TILE_PLACEMENT = 5,
+  MHC_OPT_ROW_HANDOFF = 6
 };
 enum mhc_scale_layout { MHC_SCALE_ROW_MAJOR = 0, MHC_SCALE_SWIZZLED_128X4 = 1 };
 enum mhc_tile_placement { MHC_TILE_PER_XCD = 0, MHC_TILE_SPREAD = 1 };
+enum mhc_row_handoff { MHC_HANDOFF_DEVICE = 0, MHC_HANDOFF_XCD = 1 };
 int mhc_set_option(mhc_handle h, int option, int value);
 
 /*
@@ -231,6 +246,7 @@ int mhc_boundary(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_
  * Computes exactly what mhc_boundary computes on a handle with default options (same
  * kernels, launch shape and order of sums, so the outputs are bit-identical), with the
  * same arguments, layouts, aliasing and validation, hc_mult = 4, on the current HIP device.
+ * (The row handoff uses device-scope accesses, MHC_HANDOFF_DEVICE: the outputs are the same.)
  * The row handoff's words, epochs and marks live in a fixed array of 256.25 KiB in device
  * memory (one copy per GPU, held until the process ends) instead of a handle's scratch:
  *   rows   in [0, 1024]   (0: no-op)          else MHC_ERR_LIMIT (beyond the array)

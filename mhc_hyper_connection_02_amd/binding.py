@@ -28,6 +28,9 @@ MHC_OPT_LANE_ELEMS = 4
 MHC_OPT_TILE_PLACEMENT = 5
 MHC_TILE_PER_XCD = 0
 MHC_TILE_SPREAD = 1
+MHC_OPT_ROW_HANDOFF = 6
+MHC_HANDOFF_DEVICE = 0
+MHC_HANDOFF_XCD = 1
 MHC_SCALE_ROW_MAJOR = 0
 MHC_SCALE_SWIZZLED_128X4 = 1
 _VALUE_ERRORS = {1, 2, 3, 4, 5}

@@ -40,6 +40,10 @@ struct mhc_ctx {
   int block_many;          // ... for more rows (auto)
   int block_set;           // the size MHC_OPT_BOUNDARY_BLOCK set, 0: automatic
   int spin_limit;          // polls before a handoff wait gives up
+  bool xcd_available;      // the probe at creation found workgroup ids dealt round-robin
+                           // to the XCDs
+  bool xcd_handoff;        // a row's handoff words go through its XCD's L2 (else device
+                           // scope): MHC_OPT_ROW_HANDOFF
   int scale_layout;        // MHC_SCALE_ROW_MAJOR or MHC_SCALE_SWIZZLED_128X4
   int tile_placement;      // MHC_TILE_PER_XCD or MHC_TILE_SPREAD (the fused kernel)
   int lane_elems;          // the fewest elements per lane the layer-input kernels may use
@@ -134,6 +138,7 @@ void fill_mix(const mhc_ctx* h, mhc::BoundaryLaunch& L, const uint16_t* residual
   L.errors = h->errors;
   L.slot_stride = h->slot_stride;
   L.spin_limit = h->spin_limit;
+  L.xcd_handoff = h->xcd_handoff;
   const int block = h->block_set ? h->block_set : (rows > kSmallRows ? h->block_many : h->block);
   L.max_wgs_per_xcd = h->wgs_per_xcd[block_index(block)];
   L.block = block;
@@ -381,7 +386,14 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   h->tile_part[1] = reinterpret_cast<float*>(parts + part_bytes);
   h->tile_part_next = 0;
   h->zero_words = (slot_bytes + epoch_bytes + err_bytes + tile_bytes) / 4;
-  hipError_t e = mhc::launch_fill_u32(reinterpret_cast<unsigned*>(base), total / 4, 0u, nullptr);
+  // the scratch is far larger than the probe's words; it is zeroed right after
+  hipError_t e = hipSuccess;
+  h->xcd_available = false;
+  if (total >= mhc::kXcdProbeWgs * sizeof(unsigned))
+    e = mhc::probe_xcd_round_robin(reinterpret_cast<unsigned*>(base), &h->xcd_available);
+  h->xcd_handoff = h->xcd_available;
+  if (e == hipSuccess)
+    e = mhc::launch_fill_u32(reinterpret_cast<unsigned*>(base), total / 4, 0u, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   (void)hipSetDevice(prev);
   if (e != hipSuccess) {
@@ -416,6 +428,11 @@ int mhc_set_option(mhc_handle h, int option, int value) {
     case MHC_OPT_TILE_PLACEMENT:
       if (value != MHC_TILE_PER_XCD && value != MHC_TILE_SPREAD) return MHC_ERR_SHAPE;
       h->tile_placement = value;
+      return MHC_OK;
+    case MHC_OPT_ROW_HANDOFF:
+      if (value != MHC_HANDOFF_DEVICE && value != MHC_HANDOFF_XCD) return MHC_ERR_SHAPE;
+      if (value == MHC_HANDOFF_XCD && !h->xcd_available) return MHC_ERR_UNSUPPORTED;
+      h->xcd_handoff = value == MHC_HANDOFF_XCD;
       return MHC_OK;
     default:
       return MHC_ERR_INVALID_ARG;

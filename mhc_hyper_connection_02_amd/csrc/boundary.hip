@@ -77,6 +77,7 @@ struct BoundaryParams {
   const uint4* norm_w;      // [hv]
   float eps;
   int rows, hv, hidden, chunks;
+  int xcd_handoff;          // the row's handoff words through its XCD's L2 (publish_word)
   uint4* layer_out;         // [rows][hv]
   uint2* mx_data;           // [rows][hv] (8 E4M3 codes per vector)
   uint8_t* mx_scale;        // [rows][hidden / 32] or swizzled (scale_kt)
@@ -492,7 +493,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
     unsigned long long* row_slots = p.slots + (size_t)r * p.slot_stride;
     if (lane == 0) {
       const unsigned long long word = ((unsigned long long)want << 32) | __float_as_uint(part);
-      __hip_atomic_store(row_slots + c, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      publish_word(row_slots + c, word, p.xcd_handoff != 0);
     }
     // a row whose wait gave up once (a late workgroup of that call may have left a word with
     // a tag a later call wants) trusts no word until mhc_reset: the wait is skipped and the
@@ -503,7 +504,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
       unsigned long long wd;
       int spins = 0;
       for (;;) {
-        wd = __hip_atomic_load(row_slots + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wd = poll_word(row_slots + lane, p.xcd_handoff != 0);
         if ((unsigned)(wd >> 32) == want) break;
         if (++spins > p.spin_limit) {
           __hip_atomic_fetch_add(p.errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -821,6 +822,7 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   p.errors = L.errors;
   p.slot_stride = L.slot_stride;
   p.spin_limit = L.spin_limit;
+  p.xcd_handoff = L.xcd_handoff ? 1 : 0;
   DeferParams d;
   d.coef = L.coef;
   d.def_pre = L.defer ? L.pre_pending : nullptr;
@@ -854,6 +856,30 @@ hipError_t launch_collapse_mean(const uint16_t* streams, int rows, int hidden, u
                      reinterpret_cast<const uint4*>(streams), reinterpret_cast<uint4*>(out), rows,
                      hv);
   return hipGetLastError();
+}
+
+namespace {
+__global__ __launch_bounds__(64) void xcd_probe_kernel(unsigned* out) {
+  unsigned x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  if (threadIdx.x == 0) out[blockIdx.x] = x & 0xFu;
+}
+}  // namespace
+
+hipError_t probe_xcd_round_robin(unsigned* buf, bool* round_robin) {
+  *round_robin = false;
+  hipLaunchKernelGGL(xcd_probe_kernel, dim3(kXcdProbeWgs), dim3(64), 0, nullptr, buf);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  unsigned h[kXcdProbeWgs];
+  e = hipMemcpy(h, buf, sizeof(h), hipMemcpyDeviceToHost);  // synchronizes
+  if (e != hipSuccess) return e;
+  bool ok = true;
+  for (int i = 0; i < kXcdProbeWgs; ++i) ok = ok && h[i] == h[i % kXcds];
+  for (int i = 0; i < kXcds; ++i)
+    for (int j = 0; j < i; ++j) ok = ok && h[i] != h[j];  // eight distinct XCDs
+  *round_robin = ok;
+  return hipSuccess;
 }
 
 }  // namespace mhc

@@ -222,4 +222,24 @@ __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
 }
 
+// A row handoff word, stored and polled either at device scope or, where every workgroup of
+// the row runs on one XCD, through that XCD's L2: the store then needs only workgroup scope
+// (the CU's L1 is write-through) and the poll is a non-temporal load, which the L1 does not
+// keep, so each poll reads the L2, where the other workgroups' stores land. The empty asm
+// keeps the compiler from merging polls of a loop into one load.
+__device__ __forceinline__ void publish_word(unsigned long long* p, unsigned long long v,
+                                             bool xcd) {
+  if (xcd)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long poll_word(const unsigned long long* p, bool xcd) {
+  if (xcd) {
+    asm volatile("" ::: "memory");
+    return __builtin_nontemporal_load(p);
+  }
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace mhc

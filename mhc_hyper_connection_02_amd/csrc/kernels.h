@@ -43,6 +43,8 @@ struct BoundaryLaunch {
   unsigned* errors;             // [1] handoff timeouts
   int slot_stride;
   int spin_limit;
+  bool xcd_handoff;             // workgroups with ids congruent mod 8 share an XCD (probed at
+                                // handle creation): row handoff words go through its L2
   int max_wgs_per_xcd;          // resident workgroups of this block size on one XCD
   int block;                    // 128, 256 or 512 threads per workgroup (layer-input kernels)
   int lane_elems;               // 4 or 2: the kernels that write a layer input run that many
@@ -126,5 +128,11 @@ hipError_t launch_pre_epilogue(const PreLaunch& L, hipStream_t stream);  // epil
 CoeffEpilogue pre_epilogue_args(const PreLaunch& L);
 
 hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned value, hipStream_t stream);
+
+// Whether the device deals workgroup ids round-robin to its 8 XCDs (ids congruent mod 8 on one
+// XCD), read from the hardware's XCC id register over a grid of the size the kernels use;
+// `buf` holds kXcdProbeWgs words of device memory.
+constexpr int kXcdProbeWgs = 512;
+hipError_t probe_xcd_round_robin(unsigned* buf, bool* round_robin);
 
 }  // namespace mhc

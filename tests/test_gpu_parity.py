@@ -394,6 +394,48 @@ def _bf16_nan(bits):
     return ((bits & 0x7F80) == 0x7F80) & ((bits & 0x7F) != 0)
 
 
+def test_row_handoff_scopes_give_identical_outputs():
+    """MHC_OPT_ROW_HANDOFF changes only how a row's workgroups exchange their partial sums:
+    through the L2 of the row's XCD or at device scope, the boundary (config 1 with MXFP8,
+    a ragged 5 x 1056 call in two rounds), the finalize (config 2), the first layer's entry
+    and the head give the same bits, the first two also matching the oracle, and no wait
+    gives up. A value outside the enum is rejected."""
+    say("case: row handoff through the XCD's L2 against device scope")
+    d1 = with_stated_comb(synth.config(1), 1001)
+    d2 = with_stated_comb(synth.config(2), 1002)
+    dr = synth.boundary_inputs(7, rows=5, hidden=1056, tp=3)
+    h = handle_for(7168, 64, tp=8, top_k=8)
+    hr = handle_for(1056, 5, tp=3)
+    hr.set_option(binding.MHC_OPT_BOUNDARY_BLOCK, 128)
+    rng = np.random.default_rng(5)
+    x = codecs.f64_to_bf16_bits(rng.normal(0, 1, (32, 7168)))
+    w = codecs.f64_to_bf16_bits(rng.normal(1, 0.1, 7168))
+    outs = {}
+    for mode in (binding.MHC_HANDOFF_DEVICE, binding.MHC_HANDOFF_XCD):
+        try:
+            h.set_option(binding.MHC_OPT_ROW_HANDOFF, mode)
+            hr.set_option(binding.MHC_OPT_ROW_HANDOFF, mode)
+        except binding.MhcError:
+            assert mode == binding.MHC_HANDOFF_XCD
+            pytest.skip("this device does not deal workgroup ids to its XCDs round-robin")
+        o = {"b": gpu_boundary(h, d1), "f": gpu_finalize(h, d2), "r": gpu_boundary(hr, dr),
+             "first": {k: N(v) for k, v in binding.first(h, T(x), T(w), 1e-6, mxfp8=True).items()},
+             "head": {k: N(v) for k, v in binding.collapse_norm(
+                 h, T(d1["residual"]), T(d1["pre"]), T(d1["norm_weight"]), 1e-6,
+                 mxfp8=True).items()}}
+        torch.cuda.synchronize()
+        assert h.errors() == 0 and hr.errors() == 0, f"handoff {mode}: a wait gave up"
+        outs[mode] = o
+    a, b = outs[binding.MHC_HANDOFF_DEVICE], outs[binding.MHC_HANDOFF_XCD]
+    for call in a:
+        for k in a[call]:
+            assert np.array_equal(a[call][k], b[call][k]), f"{call}.{k} differs between scopes"
+    compare_boundary_outputs(b["b"], oracle_boundary(d1), "config 1, XCD handoff")
+    compare_boundary_outputs(b["f"], oracle_finalize(d2), "config 2, XCD handoff")
+    with pytest.raises(binding.MhcValueError):
+        h.set_option(binding.MHC_OPT_ROW_HANDOFF, 2)
+
+
 def test_zero_spin_limit_poisons_and_reset_recovers():
     """A spin limit of 0 polls once, so waits give up (counted; nothing hangs, every kernel
     exits). The data shows it: where a wait gave up the layer input is NaN, its E4M3 codes the
