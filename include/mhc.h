@@ -247,7 +247,7 @@ int mhc_boundary(mhc_handle h, const uint16_t* x_partials, int tp, const uint16_
  * kernels, launch shape and order of sums, so the outputs are bit-identical), with the
  * same arguments, layouts, aliasing and validation, hc_mult = 4, on the current HIP device.
  * (The row handoff uses device-scope accesses, MHC_HANDOFF_DEVICE: the outputs are the same.)
- * The row handoff's words, epochs and marks live in a fixed array of 256.25 KiB in device
+ * The row handoff's words, epochs and marks live in a fixed array of 1152.25 KiB in device
  * memory (one copy per GPU, held until the process ends) instead of a handle's scratch:
  *   rows   in [0, 1024]   (0: no-op)          else MHC_ERR_LIMIT (beyond the array)
  *   hidden a multiple of 8, at most 16384     else MHC_ERR_SHAPE / MHC_ERR_LIMIT

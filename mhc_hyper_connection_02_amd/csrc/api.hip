@@ -17,7 +17,6 @@ constexpr int kMaxRows = 65536;
 constexpr int kMaxTp = 64;
 constexpr int kMaxTopK = 64;
 constexpr int kMaxSinkhornIters = 1000;
-constexpr int kMinBlock = 128;      // smallest boundary workgroup: the most chunks per row
 constexpr int kDefaultBlock = 128;   // up to kSmallRows rows
 constexpr int kManyRowsBlock = 256;
 constexpr int kSmallRows = 32;
@@ -203,13 +202,14 @@ hipError_t launch_fill_u32(unsigned* p, size_t n, unsigned value, hipStream_t st
 // ---------------------------------------------------------------------------
 // The allocation-free boundary (mhc_boundary_noalloc): the row handoff's words, epochs and
 // error word live in a fixed array in device memory, one copy per GPU, instead of a
-// handle's hipMalloc. Its size bounds the rows (one 128-byte line of words and one of
-// epochs per row) and the chunks per row (16, i.e. hidden <= 16384).
+// handle's hipMalloc. Its size bounds the rows (1 KiB of words, one per wave of the row,
+// and one 128-byte line of epochs per row) and the hidden size (at most 16384, i.e. 128
+// waves per row at 512 threads).
 // ---------------------------------------------------------------------------
 namespace {
 
 constexpr int kNoAllocRows = 1024;
-constexpr int kNoAllocSlotStride = 16;
+constexpr int kNoAllocSlotStride = 128;  // boundary_handoff_words(kNoAllocMaxHidden)
 constexpr int kNoAllocMaxHidden = 16384;
 constexpr size_t kNoAllocSlotBytes = (size_t)kNoAllocRows * kNoAllocSlotStride * 8;
 constexpr size_t kNoAllocEpochBytes = (size_t)kNoAllocRows * mhc::kEpochStride * 4;
@@ -315,10 +315,11 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
   h->lane_elems = 2;
   h->tile_placement = MHC_TILE_PER_XCD;
   h->pending = false;
-  // the most chunks per row, rounded up to 16 words: each row's handoff words on a
-  // 128-byte line of their own (rows sharing a line, from different XCDs, measured
-  // 0.25 us slower per call: 5.35 against 5.08 us for 32 rows at hidden 7168)
-  h->slot_stride = (mhc::boundary_chunks(hidden, kMinBlock, true) + 15) / 16 * 16;
+  // one word per wave of the row at the most waves per row (the smallest chunks at the
+  // widest workgroup), rounded up to 16 words: each row's handoff words on 128-byte lines
+  // of their own (rows sharing a line, from different XCDs, measured 0.25 us slower per
+  // call: 5.35 against 5.08 us for 32 rows at hidden 7168)
+  h->slot_stride = mhc::boundary_handoff_words(hidden);
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
       cus < 8) {

@@ -22,16 +22,19 @@
 // form) waits for the row's RMS.
 //
 // The row RMS. The RMS needs the whole row, and a row spans several
-// workgroups. Each workgroup publishes its partial sum of y^2 as ONE 64-bit
-// word (call tag << 32 | fp32 bits) with a relaxed device-scope atomic
-// store; wave 0 of every workgroup of the row then polls the row's words
-// until all carry this call's tag and adds them in chunk order (the same
-// fixed order in every workgroup: deterministic, no float atomics). Because
-// the tag travels in the same word as the value, no fence is needed, so no
-// L2 writeback or invalidate is issued. The tag is the row's epoch + 1,
-// read at the start; chunk 0 advances the epoch once it has seen every
-// word, which is after every workgroup of the row has read it. Epochs live
-// in device memory, so graph replays stay correct.
+// workgroups. Every wave publishes its partial sum of y^2 as ONE 64-bit word
+// (call tag << 32 | fp32 bits), at its own place in the row's words; every
+// wave of the row then polls all of the row's words, one lane per word,
+// until all carry this call's tag, and adds them in a fixed tree order (the
+// same in every wave: deterministic, no float atomics, and no barrier
+// inside the workgroup). Because the tag travels in the same word as the
+// value, no fence is needed, so no L2 writeback or invalidate is issued.
+// The words stay in the XCD's L2 (workgroup-scope stores, non-temporal
+// polls that the L1 does not keep) where the device deals workgroup ids to
+// its XCDs round-robin, else they are device-scope. The tag is the row's
+// epoch + 1, read at the start; the row's first wave advances the epoch once
+// it has seen every word, which is after every workgroup of the row has
+// read it. Epochs live in device memory, so graph replays stay correct.
 //
 // Co-residency. Polling requires all workgroups of a row to be resident at
 // once. The host sizes the grid to at most half of the device's
@@ -40,7 +43,7 @@
 // workgroup w handles one (row, chunk) of a block of rows that the grid covers
 // entirely, so every row's chunks are live together. The wait is bounded
 // (spin_limit polls with s_sleep); a timeout is counted in the handle's error
-// word and the workgroup goes on.
+// word and the wave goes on.
 //
 // XCD placement. Consecutive workgroup ids are dealt round-robin to the 8
 // XCDs, so a row's chunks get ids congruent to the row mod 8: all
@@ -287,8 +290,7 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
                                                    const int* __restrict__ idx,
                                                    const float* __restrict__ ew,
                                                    const DeferArg<DEFER>& dp, int r, int c,
-                                                   float* s_red, float* s_inv, float* s_coef,
-                                                   float sc_l, float base_l) {
+                                                   float* s_coef, float sc_l, float base_l) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -307,8 +309,8 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   const bool active = v < nv;
   const int va = active ? v : 0;
 
-  // the row's epoch and poison flag (wave 0 runs the handoff), read by every wave without a
-  // branch, first, so that their latency hides under the data loads
+  // the row's epoch and poison flag, read by every wave without a branch, first, so that
+  // their latency hides under the data loads
   unsigned epoch_now = 0, poisoned = 0;
   if constexpr (HAS_PRE) {
     const unsigned long long ew = __hip_atomic_load(
@@ -483,60 +485,55 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p,
   for (int e = 0; e < EL; ++e) sq = __builtin_fmaf(y[e], y[e], sq);
   if (!active) sq = 0.f;
   sq = wave_sum(sq);
-  if (lane == 0) s_red[wave] = sq;
-  __syncthreads();
-  if (wave == 0) {
-    const unsigned want = epoch_now + 1u;
-    float part = 0.f;
-#pragma unroll
-    for (int w = 0; w < BS / kWave; ++w) part += s_red[w];
-    unsigned long long* row_slots = p.slots + (size_t)r * p.slot_stride;
-    if (lane == 0) {
-      const unsigned long long word = ((unsigned long long)want << 32) | __float_as_uint(part);
-      publish_word(row_slots + c, word, p.xcd_handoff != 0);
-    }
-    // a row whose wait gave up once (a late workgroup of that call may have left a word with
-    // a tag a later call wants) trusts no word until mhc_reset: the wait is skipped and the
-    // layer input poisoned
-    bool failed = poisoned != 0;
-    float val = 0.f;
-    if (lane < p.chunks && !failed) {
-      unsigned long long wd;
-      int spins = 0;
-      for (;;) {
-        wd = poll_word(row_slots + lane, p.xcd_handoff != 0);
-        if ((unsigned)(wd >> 32) == want) break;
-        if (++spins > p.spin_limit) {
-          __hip_atomic_fetch_add(p.errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          failed = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
+  // the row handoff: every wave publishes its partial sum of y^2 as one word of the row
+  // (chunk-major: word c * waves + wave), then waits for all of the row's words itself, one
+  // lane per word, and adds them in a fixed tree order, so every wave of the row gets the
+  // same bits without a barrier
+  constexpr int kWaves = BS / kWave;
+  const unsigned want = epoch_now + 1u;
+  const bool xcd = p.xcd_handoff != 0;
+  unsigned long long* row_slots = p.slots + (size_t)r * p.slot_stride;
+  if (lane == 0)
+    publish_word(row_slots + c * kWaves + wave,
+                 ((unsigned long long)want << 32) | __float_as_uint(sq), xcd);
+  // a row whose wait gave up once (a late wave of that call may have left a word with a tag
+  // a later call wants) trusts no word until mhc_reset: the wait is skipped and the layer
+  // input poisoned
+  bool failed = poisoned != 0;
+  float part = 0.f;
+  const int words = p.chunks * kWaves;
+  for (int k = lane; k < words && !failed; k += kWave) {
+    unsigned long long wd;
+    int spins = 0;
+    for (;;) {
+      wd = poll_word(row_slots + k, xcd);
+      if ((unsigned)(wd >> 32) == want) break;
+      if (++spins > p.spin_limit) {
+        __hip_atomic_fetch_add(p.errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        failed = true;
+        break;
       }
-      val = __uint_as_float((unsigned)wd);
+      __builtin_amdgcn_s_sleep(1);
     }
-    float tot = 0.f;
-    for (int k = 0; k < p.chunks; ++k)  // chunk order
-      tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), k));
-    // a wait that gave up makes this workgroup's share of the layer input NaN (and its
-    // MXFP8 scales the E8M0 NaN byte), so that the failure shows in the data, and marks the
-    // row (word 1 of its epoch line) for the calls after it
-    if (__ballot(failed) != 0) {
-      tot = __builtin_nanf("");
-      if (lane == 0 && !poisoned)
-        __hip_atomic_store(p.epoch + (size_t)r * kEpochStride + 1, 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (lane == 0) {
-      *s_inv = fast_rsq(tot * fast_rcp((float)p.hidden) + p.eps);
-      if (c == 0)
-        __hip_atomic_store(p.epoch + (size_t)r * kEpochStride, want, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
+    part += __uint_as_float((unsigned)wd);
   }
-  __syncthreads();
+  float tot = wave_sum(part);
+  // a wait that gave up makes this wave's share of the layer input NaN (and its MXFP8
+  // scales the E8M0 NaN byte), so that the failure shows in the data, and marks the row
+  // (word 1 of its epoch line) for the calls after it
+  if (__ballot(failed) != 0) {
+    tot = __builtin_nanf("");
+    if (lane == 0 && !poisoned)
+      __hip_atomic_store(p.epoch + (size_t)r * kEpochStride + 1, 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // every word of the row is in, so every workgroup of the row has read the epoch: the
+  // row's first wave advances it
+  if (c == 0 && wave == 0 && lane == 0)
+    __hip_atomic_store(p.epoch + (size_t)r * kEpochStride, want, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   if (!active) return;
-  const float inv = *s_inv;
+  const float inv = fast_rsq(tot * fast_rcp((float)p.hidden) + p.eps);
   float w[EL], o[EL];
   unpack_bf16(wv, w);
 #pragma unroll
@@ -589,8 +586,6 @@ __global__ __launch_bounds__(BS, DEFER ? 4 : 1) void boundary_kernel(const Bound
   prefetch_kernargs<sizeof(BoundaryParams) + 5 * sizeof(void*) + sizeof(DeferArg<DEFER>)>();
   // the layer-input kernels (with the row handoff) run one lane per vector; the
   // residual-only kernels run four lanes per vector
-  __shared__ float s_red[BS / kWave];
-  __shared__ float s_inv;
   __shared__ float s_coef[2 * kHC + kHC * kHC];
   float sc_l = 0.f, base_l = 0.f;  // deferred coefficients: this lane's scale and base
   if constexpr (DEFER) coeff_lane_scale_base(dp.coef, threadIdx.x & (kWave - 1), &sc_l, &base_l);
@@ -602,11 +597,14 @@ __global__ __launch_bounds__(BS, DEFER ? 4 : 1) void boundary_kernel(const Bound
   for (int round = 0; round < p.rounds; ++round) {
     const int r = (round * p.rows_per_round + jr) * kXcds + xcd;
     if (r >= p.rows) break;  // uniform per workgroup; later rounds only go higher
+    // the layer-input kernels have no barrier after the coefficients are read: one here
+    // keeps a later round's finish from overwriting them while a wave still reads them
+    if (DEFER && HAS_PRE && round > 0) __syncthreads();
     if constexpr (!HAS_PRE)
       boundary_item_quad<BS, FINALIZE, DEFER>(p, dp, r, c, s_coef, sc_l, base_l);
     else
       boundary_item_lane<BS, FINALIZE, HAS_PRE, MXFP8, MODE, DEFER, EL>(
-          p, post, comb, pre, idx, ew, dp, r, c, s_red, &s_inv, s_coef, sc_l, base_l);
+          p, post, comb, pre, idx, ew, dp, r, c, s_coef, sc_l, base_l);
   }
 }
 
@@ -767,6 +765,10 @@ int boundary_chunks(int hidden, int block, bool has_pre) {
   return (hv + per_wg - 1) / per_wg;
 }
 
+int boundary_handoff_words(int hidden) {
+  return (boundary_chunks(hidden, 128, true) * (512 / kWave) + 15) / 16 * 16;
+}
+
 hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   BoundaryParams p;
   p.xp = reinterpret_cast<const uint4*>(L.x_partials);
@@ -838,6 +840,8 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
     p.rows_per_round = row_blocks;
     p.rounds = 1;
   }
+  // every wave of a row owns one handoff word of the row's slot line(s)
+  if (pre && p.chunks * (block / kWave) > p.slot_stride) return hipErrorInvalidValue;
   const int grid = kXcds * p.rows_per_round * p.chunks;
   switch (block) {
     case 128: return launch_bs<128>(p, d, fin, pre, mx, L.mode, L.defer, el, grid, stream);

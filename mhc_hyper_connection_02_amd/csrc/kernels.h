@@ -115,6 +115,9 @@ bool boundary_tile_fits(int hidden, int wgs_per_xcd);
 hipError_t launch_boundary_tile(const TileLaunch& T, hipStream_t stream);
 
 int boundary_chunks(int hidden, int block, bool has_pre);
+// Row-handoff words per row: one per wave at the most waves a row can have (the
+// 128-thread chunks at 512 threads), rounded up to 16 (a 128-byte line).
+int boundary_handoff_words(int hidden);
 int boundary_resident_wgs_per_cu(int block);
 hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream);
 hipError_t launch_collapse_mean(const uint16_t* streams, int rows, int hidden, uint16_t* out,
