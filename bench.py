@@ -583,6 +583,33 @@ def main():
         log(f"  residual-only {rows['residual_only_decode']}")
         del bufs, calls
 
+        # the headline's call at 512 rows (context: the per-launch costs spread over 16x the
+        # bytes)
+        R5 = 512
+        d5 = synth.boundary_inputs(11, rows=R5, hidden=H, tp=TP, x_sigma=0.5, mxfp8=True)
+        h5 = binding.Handle(H, 4, max_rows=R5, max_tp=TP, top_k=8)
+        b5 = {k: T(d5[k]) for k in ("post", "comb", "pre", "norm_weight")}
+        n5 = bytes_boundary(R5, H, TP, pre=True, mxfp8=True)
+        s5b = n_sets(n5)
+        bufs = [{"x": T(d5["x_partials"]), "s": T(d5["residual"]),
+                 "so": torch.empty((R5, 4, H), dtype=torch.bfloat16, device=dev),
+                 "li": torch.empty((R5, H), dtype=torch.bfloat16, device=dev),
+                 "md": torch.empty((R5, H), dtype=torch.uint8, device=dev),
+                 "ms": torch.empty((R5, H // 32), dtype=torch.uint8, device=dev)}
+                for _ in range(s5b)]
+        del d5
+        calls = [(lambda b=b: binding.boundary(h5, b["x"], b["s"], b5["post"], b5["comb"],
+                                               b5["pre"], b5["norm_weight"], 1e-6, mxfp8=True,
+                                               residual_out=b["so"], layer_input_out=b["li"],
+                                               mx_out=(b["md"], b["ms"])))
+                 for b in bufs]
+        t = time_calls(torch, calls, args.steps, args.warmup)
+        rows["boundary_mxfp8_r512"] = row_entry("boundary_r512", n5, t, s5b)
+        rows["boundary_mxfp8_r512"]["note"] = ("the headline's call at 512 rows (seed 11): "
+                                               "context, where one launch carries 16x the bytes")
+        log(f"  boundary r512 {rows['boundary_mxfp8_r512']}")
+        del bufs, calls, h5
+
         # finalize at config 2
         d2 = synth.config(2)
         R2, K2 = 64, 8

@@ -217,7 +217,13 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
                                           float dbase_l) {
   constexpr bool DEFER_OUT = DEFER >= 1;
   constexpr bool DEFER_IN = DEFER == 2;
-  const int tid = threadIdx.x;
+  // the thread and chunk indices pass through an empty asm, so what derives from them is
+  // computed here, per item: hoisted before the round loop (which mostly runs once) it
+  // held scalar registers across the kernel, spilled them into vector lanes and kept
+  // ~600 instructions ahead of the first loads
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  asm volatile("" : "+s"(c));
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   // global traffic: the 32 lanes of a half wave own one row's 32 vectors of the chunk
