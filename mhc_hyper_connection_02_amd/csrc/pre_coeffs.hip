@@ -50,11 +50,17 @@ struct PrePartialParams {
   int rows, K, ks_count, steps_per_wg, nsteps;
 };
 
+// NS: the k steps a wave owns (ceil(steps per workgroup / 4), 1..8), so that the number of
+// loads is known at compile time and every load can be unconditional.
+template <int NS>
 __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const PrePartialParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t fnT[kNC][kMaxStepsPerWg * kStepK + kLdsPad];
   __shared__ float red[kPreWaves][kRB][kPartW];
-  constexpr int kMaxWaveSteps = kMaxStepsPerWg / kPreWaves;                  // 8
-  constexpr int kMaxFnVecs = kMaxStepsPerWg * kStepK * kNC / 8 / (kPreWaves * kWave);  // 12
+  static_assert(NS >= 1 && NS * kPreWaves <= kMaxStepsPerWg, "steps per wave");
+  constexpr int kMaxWaveSteps = NS;
+  // the slice's fn vectors (NS * 4 steps of 32 k, 3 vectors a k row) over the threads
+  constexpr int kMaxFnVecs = (NS * kPreWaves * kStepK * kNC / 8 + kPreWaves * kWave - 1) /
+                             (kPreWaves * kWave);
 
   const int wg = blockIdx.x;
   // (row block, split) pairs are dealt to the 8 XCDs in contiguous ranges (the grid,
@@ -75,38 +81,42 @@ __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const Pr
   const int s0 = ks * p.steps_per_wg;
   const int s1 = min(s0 + p.steps_per_wg, p.nsteps);
   const int kbase = s0 * kStepK;
-  const int kc = max(s1 - s0, 0) * kStepK;  // k values of this workgroup
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
 
-  // --- every load first: this wave's row vectors (steps s0 + wave + 4i), then the fn slice
-  const uint16_t* vrow = p.res + (size_t)(row_ok ? row : 0) * p.K + kbase + kg * 8;
-  uint4 bv[kMaxWaveSteps];
-#pragma unroll
-  for (int i = 0; i < kMaxWaveSteps; ++i) {
-    const int sl = wave + kPreWaves * i;  // step inside the slice
-    if (s0 + sl < s1) bv[i] = row_ok ? load_nt(reinterpret_cast<const uint4*>(vrow + sl * kStepK)) : zero;
-  }
-  const uint4* src = reinterpret_cast<const uint4*>(p.fn + (size_t)kbase * kNC);
-  const int nvec = kc * kNC / 8;  // 3 vectors per k row
+  // --- every load first: the fn slice (its staging into LDS then waits for it alone), then
+  // this wave's row vectors (steps s0 + wave + 4i). Every load is unconditional, its index
+  // clamped into the tensor (rows past the last read row 0, steps and vectors past the slice
+  // the tensor's last ones): those values are never used (steps, vectors) or only reach
+  // rows that are never read. A load behind a branch (a zero for the missing rows, a bound
+  // on the steps or vectors) made the compiler wait for it, or for every load, before going
+  // on.
+  const uint4* src = reinterpret_cast<const uint4*>(p.fn);
+  const int last_vec = p.nsteps * kStepK * kNC / 8 - 1;
   uint4 fv[kMaxFnVecs];
 #pragma unroll
   for (int j = 0; j < kMaxFnVecs; ++j) {
     const int i = tid + j * kPreWaves * kWave;
-    if (i < nvec) fv[j] = src[i];
+    fv[j] = src[min(kbase * kNC / 8 + i, last_vec)];
   }
-  // --- fn slice -> LDS, transposed to [logit][k]
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint16_t* vrow = p.res + (size_t)(row_ok ? row : 0) * p.K + kg * 8;
+  uint4 bv[kMaxWaveSteps];
+#pragma unroll
+  for (int i = 0; i < kMaxWaveSteps; ++i) {
+    const int gs = min(s0 + wave_u + kPreWaves * i, p.nsteps - 1);  // global step
+    bv[i] = load_nt(reinterpret_cast<const uint4*>(vrow + gs * kStepK));
+  }
+  // --- fn slice -> LDS, transposed to [logit][k]; every lane writes (past the slice, at
+  // k past the workgroup's steps inside the buffer, which no MFMA step reads)
 #pragma unroll
   for (int j = 0; j < kMaxFnVecs; ++j) {
     const int i = tid + j * kPreWaves * kWave;
-    if (i < nvec) {
-      const int e = i * 8;
-      const int kk = e / kNC, c0 = e % kNC;  // c0 in {0, 8, 16}
-      const uint32_t u[4] = {fv[j].x, fv[j].y, fv[j].z, fv[j].w};
+    const int e = i * 8;
+    const int kk = e / kNC, c0 = e % kNC;  // c0 in {0, 8, 16}; kk < kMaxStepsPerWg * kStepK
+    const uint32_t u[4] = {fv[j].x, fv[j].y, fv[j].z, fv[j].w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        fnT[c0 + 2 * q][kk] = (uint16_t)(u[q] & 0xFFFFu);
-        fnT[c0 + 2 * q + 1][kk] = (uint16_t)(u[q] >> 16);
-      }
+    for (int q = 0; q < 4; ++q) {
+      fnT[c0 + 2 * q][kk] = (uint16_t)(u[q] & 0xFFFFu);
+      fnT[c0 + 2 * q + 1][kk] = (uint16_t)(u[q] >> 16);
     }
   }
   __syncthreads();
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(kPreWaves * kWave) void pre_partial_kernel(const Pr
   const uint32_t keep = hi_ok ? ~0u : 0u;
 #pragma unroll
   for (int i = 0; i < kMaxWaveSteps; ++i) {
-    const int sl = wave + kPreWaves * i;
+    const int sl = wave_u + kPreWaves * i;
     if (s0 + sl < s1) {
       const int kl = sl * kStepK + kg * 8;  // k offset inside the slice
       const uint4 a0 = *reinterpret_cast<const uint4*>(&fnT[m][kl]);
@@ -238,7 +248,18 @@ hipError_t launch_pre_partial(const PreLaunch& L, hipStream_t stream) {
   a.steps_per_wg = spw;
   a.nsteps = a.K / kStepK;
   const int grid = ks * (rp / kRB);
-  hipLaunchKernelGGL(pre_partial_kernel, dim3(grid), dim3(kPreWaves * kWave), 0, stream, a);
+  const dim3 g(grid), b(kPreWaves * kWave);
+  switch ((spw + kPreWaves - 1) / kPreWaves) {
+    case 1: hipLaunchKernelGGL(pre_partial_kernel<1>, g, b, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(pre_partial_kernel<2>, g, b, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(pre_partial_kernel<3>, g, b, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(pre_partial_kernel<4>, g, b, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL(pre_partial_kernel<5>, g, b, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL(pre_partial_kernel<6>, g, b, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL(pre_partial_kernel<7>, g, b, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(pre_partial_kernel<8>, g, b, 0, stream, a); break;
+    default: return hipErrorInvalidConfiguration;
+  }
   return hipGetLastError();
 }
 
