@@ -249,6 +249,21 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
           p.epoch + (size_t)min(row0 + (tid & 15), p.rows - 1) * kEpochStride),
       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const unsigned epoch_now = (unsigned)ew;
+  // the finalize's expert slots next: the gathers wait for them, and a wait covers every
+  // load issued before (slots past top_k re-read the row's last one and get weight 0)
+  int pk[8];
+  float wk[8];
+  if constexpr (FINALIZE) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int uu = u < p.top_k ? u : p.top_k - 1;
+      const uint32_t o = ((uint32_t)rl * p.top_k + uu) * 4u;
+      const int pi = *byte_at(p.idx, o);
+      const float w = *byte_at(p.ew, o);
+      pk[u] = u < p.top_k ? pi : -1;
+      wk[u] = u < p.top_k ? w : 0.f;
+    }
+  }
 
   // --- DEFER_IN: the pending call's partial sums of this lane's row (the half wave's), value
   // vl (lanes past 24 repeat value 24), first: their wait then leaves the loads below in flight
@@ -302,19 +317,6 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
 #pragma unroll
     for (int i = 0; i < kN; ++i) cmb4[i] = S.cf[m][2 + i];
   };
-  int pk[8];
-  float wk[8];
-  if constexpr (FINALIZE) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int uu = u < p.top_k ? u : p.top_k - 1;
-      const uint32_t o = ((uint32_t)rl * p.top_k + uu) * 4u;
-      const int pi = *byte_at(p.idx, o);
-      const float w = *byte_at(p.ew, o);
-      pk[u] = u < p.top_k ? pi : -1;
-      wk[u] = u < p.top_k ? w : 0.f;
-    }
-  }
   // per-lane byte offsets in 32 bits (the tile kernel's tensors are below 4 GiB: rows <= 1024,
   // hidden <= 8192, tp <= 64, num_permuted * hidden * 2 < 2^32, checked by the host)
   const uint32_t row_off = ((uint32_t)rl * p.hv + va) * 16u;  // [rows][hv] tensors
@@ -382,14 +384,18 @@ __device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilog
   } else {
     // k ascending, then the shared row
     const uint4 shv = load_nt(byte_at(p.shared, row_off));
+    // every gather unconditional (a slot past top_k or out of range reads row 0 with weight
+    // 0, and only slots below top_k are added): a gather behind a branch made the compiler
+    // wait for every earlier load before issuing the first one
+    // no instruction crosses this point, so the gather addresses (each waiting for its slot)
+    // are not computed ahead of the loads above, which then stay in flight during that wait
+    __builtin_amdgcn_sched_barrier(0);
     uint4 gv[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if (u < p.top_k) {
-        const bool ok = pk[u] >= 0 && pk[u] < p.num_permuted;
-        gv[u] = load_nt(byte_at(p.g, ((uint32_t)(ok ? pk[u] : 0) * p.hv + va) * 16u));
-        if (!ok) wk[u] = 0.f;
-      }
+      const bool ok = pk[u] >= 0 && pk[u] < p.num_permuted;
+      gv[u] = load_nt(byte_at(p.g, ((uint32_t)(ok ? pk[u] : 0) * p.hv + va) * 16u));
+      if (!ok) wk[u] = 0.f;
     }
     stage_fn();
     if constexpr (DEFER_IN) finish_pending();
