@@ -134,6 +134,22 @@ def test_pre_coeffs_ragged(rows, hidden, iters):
         assert_f32_close(N(a), b, f"{name} rows={rows} hidden={hidden}")
 
 
+# The split-K kernel of the coefficient call is compiled for 1..8 k steps per wave, picked at
+# launch from the split count (about 256 workgroups over the 16-row blocks, each slice at
+# most 32 steps of 32 k). These shapes reach each of the eight, with ragged row blocks and,
+# where the split count does not divide the steps, a ragged last slice.
+@pytest.mark.parametrize("steps_per_wave,rows,hidden", [
+    (1, 1, 256), (2, 1, 10240), (3, 17, 10240), (4, 33, 8192), (5, 33, 12288),
+    (6, 65, 8192), (7, 65, 10240), (8, 65, 12288)])
+def test_pre_coeffs_every_split_k_width(steps_per_wave, rows, hidden):
+    say(f"case: pre_coeffs rows={rows} hidden={hidden} ({steps_per_wave} k steps per wave)")
+    d = synth.pre_inputs(400 + steps_per_wave, rows=rows, hidden=hidden)
+    h = handle_for(hidden, rows)
+    got = _pre_call(h, d)
+    for name, a, b in zip(("pre", "post", "comb"), got, _pre_oracle(d)):
+        assert_f32_close(a, b, f"{name} rows={rows} hidden={hidden}")
+
+
 def _pre_call(h, d, iters=None):
     it = d["sinkhorn_iters"] if iters is None else iters
     got = binding.pre_coeffs(h, T(d["residual"]), T(d["fn"]), T(d["scale"]), T(d["base"]),
