@@ -211,10 +211,22 @@ struct TileShared {
 // 2 also this call's post, comb and pre finished here from the pending call's partial sums
 // (DEFER_IN) instead of read.
 template <bool FINALIZE, bool MXFP8, int DEFER>
-__device__ __forceinline__ void tile_item(const TileParams& p, const CoeffEpilogue& coef,
-                                          const TileDeferIn* din, int tile, int c,
+__device__ __forceinline__ void tile_item(const TileParams& p_arg, const CoeffEpilogue& coef,
+                                          const TileDeferIn* din_arg, int tile, int c,
                                           TileShared& S, float sc_l, float base_l, float dsc_l,
                                           float dbase_l) {
+  // the sizes that the per-slot offsets and bounds derive from pass through an empty asm
+  // too, for the same reason as the indices below: hoisted, those uniform values were
+  // spilled into vector lanes (112 lane moves in the deferred TP kernel, 4 now)
+  TileParams p = p_arg;
+  asm volatile("" : "+s"(p.tp), "+s"(p.top_k), "+s"(p.rows), "+s"(p.hv), "+s"(p.chunks));
+  TileDeferIn dcopy;
+  const TileDeferIn* din = din_arg;
+  if constexpr (DEFER == 2) {
+    dcopy = *din_arg;
+    asm volatile("" : "+s"(dcopy.coef.ks_count));
+    din = &dcopy;
+  }
   constexpr bool DEFER_OUT = DEFER >= 1;
   constexpr bool DEFER_IN = DEFER == 2;
   // the thread and chunk indices pass through an empty asm, so what derives from them is
