@@ -410,6 +410,68 @@ def _bf16_nan(bits):
     return ((bits & 0x7F80) == 0x7F80) & ((bits & 0x7F) != 0)
 
 
+def test_many_handoffs_in_a_graph_all_complete():
+    """Thousands of row handoffs back to back (a graph of 400 config-1 boundary calls and
+    400 finalize calls over rotating buffers, replayed 5 times, with the handle's default
+    handoff scope): no wait gives up, and every call's outputs equal the same call run
+    eagerly, bit for bit."""
+    say("case: 4000 boundary and finalize calls graph-replayed, default handoff scope")
+    d1 = synth.config(1)
+    d2 = synth.config(2)
+    h = handle_for(7168, 64, tp=8, top_k=8)
+    want_b = gpu_boundary(h, d1)
+    want_f = gpu_finalize(h, d2)
+    inb = {k: T(d1[k]) for k in ("x_partials", "residual", "post", "comb", "pre", "norm_weight")}
+    inf = {k: T(d2[k]) for k in ("gemm2_permuted", "expert_weights",
+                                 "expanded_idx_to_permuted_idx", "shared_output", "residual",
+                                 "post", "comb", "pre", "norm_weight")}
+    nb = 4
+    outs_b = [{"so": torch.empty_like(inb["residual"]),
+               "li": torch.empty((32, 7168), dtype=torch.bfloat16, device="cuda"),
+               "md": torch.empty((32, 7168), dtype=torch.uint8, device="cuda"),
+               "ms": torch.empty((32, 224), dtype=torch.uint8, device="cuda")} for _ in range(nb)]
+    outs_f = [{"so": torch.empty_like(inf["residual"]),
+               "li": torch.empty((64, 7168), dtype=torch.bfloat16, device="cuda"),
+               "md": torch.empty((64, 7168), dtype=torch.uint8, device="cuda"),
+               "ms": torch.empty((64, 224), dtype=torch.uint8, device="cuda")} for _ in range(nb)]
+
+    def calls():
+        for i in range(400):
+            o = outs_b[i % nb]
+            binding.boundary(h, inb["x_partials"], inb["residual"], inb["post"], inb["comb"],
+                             inb["pre"], inb["norm_weight"], d1["eps"], mxfp8=True,
+                             residual_out=o["so"], layer_input_out=o["li"],
+                             mx_out=(o["md"], o["ms"]))
+            o = outs_f[i % nb]
+            binding.finalize(h, inf["gemm2_permuted"], inf["expert_weights"],
+                             inf["expanded_idx_to_permuted_idx"], inf["shared_output"],
+                             inf["residual"], inf["post"], inf["comb"], inf["pre"],
+                             inf["norm_weight"], d2["eps"], mxfp8=True, residual_out=o["so"],
+                             layer_input_out=o["li"], mx_out=(o["md"], o["ms"]))
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(5):
+        g.replay()
+        torch.cuda.synchronize()
+        for o in outs_b:
+            assert np.array_equal(N(o["so"]), want_b["residual"])
+            assert np.array_equal(N(o["li"]), want_b["layer_input"])
+            assert np.array_equal(N(o["md"]), want_b["mx_data"])
+            assert np.array_equal(N(o["ms"]), want_b["mx_scale"])
+        for o in outs_f:
+            assert np.array_equal(N(o["li"]), want_f["layer_input"])
+            assert np.array_equal(N(o["ms"]), want_f["mx_scale"])
+    assert h.errors() == 0, "a handoff wait gave up"
+
+
 def test_row_handoff_scopes_give_identical_outputs():
     """MHC_OPT_ROW_HANDOFF changes only how a row's workgroups exchange their partial sums:
     through the L2 of the row's XCD or at device scope, the boundary (config 1 with MXFP8,
