@@ -374,17 +374,41 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p_arg,
   } else if constexpr (MODE == kBoundaryHead) {
     // no sublayer output
   } else if constexpr (!FINALIZE) {
-    // t ascending
+    // t ascending. In each full group of eight slices the loads issue back to back without
+    // a branch, each address the previous one plus the slice stride; the stride passes
+    // through an empty asm at every step, so that the compiler keeps one 64-bit add per
+    // slice rather than forming each slice's offset as a 64-bit product in scalar
+    // registers ahead of the first load (measured: ~90 scalar instructions before the
+    // loads, the headline call 4.29 -> 4.06 us). A ragged last group takes the branchy form.
     const Vec* src = xp + (size_t)r * nv + va;
     const size_t slice = (size_t)p.rows * nv;
-    for (int t0 = 0; t0 < p.tp; t0 += 8) {
+    size_t step = slice * sizeof(Vec);
+    const int full = p.tp & ~7;
+    for (int t0 = 0; t0 < full; t0 += 8) {
+      Vec xv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        xv[u] = load_nt(src);
+        asm volatile("" : "+s"(step));
+        src = reinterpret_cast<const Vec*>(reinterpret_cast<const char*>(src) + step);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float f[EL];
+        unpack_bf16(xv[u], f);
+#pragma unroll
+        for (int e = 0; e < EL; ++e) x[e] += f[e];
+      }
+    }
+    if (full < p.tp) {
       Vec xv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (t0 + u < p.tp) xv[u] = load_nt(src + (size_t)(t0 + u) * slice);
+        if (full + u < p.tp) xv[u] = load_nt(src + (size_t)u * slice);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (t0 + u < p.tp) {
+        if (full + u < p.tp) {
           float f[EL];
           unpack_bf16(xv[u], f);
 #pragma unroll

@@ -99,6 +99,9 @@ def test_config3_pre_coeffs():
 @pytest.mark.parametrize("rows,hidden,tp,block", [
     (1, 512, 1, 128), (5, 1056, 3, 128), (9, 2080, 8, 256), (17, 7168, 8, 512),
     (13, 3072, 5, 256), (8, 33 * 32, 2, 512), (3, 8 * 40, 4, 128),
+    # slice counts past one group of eight: a full group and a ragged one, two full
+    # groups, and the largest count a handle takes
+    (6, 2080, 13, 256), (4, 1024, 16, 128), (3, 1024, 64, 128), (10, 7168, 24, 512),
 ])
 def test_boundary_ragged(rows, hidden, tp, block):
     mx = hidden % 32 == 0
