@@ -577,14 +577,19 @@ __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p_arg,
     constexpr int kPerBlock = 32 / EL;
     float q[EL];
     unpack_bf16(ob, q);
-    float amax = 0.f;
+    // the block's largest magnitude, as the unsigned maximum of the magnitudes' bit
+    // patterns (non-negative floats order as their bits): each step is then one DPP max,
+    // with no LDS swizzle (measured: headline 4.06 -> 4.02 us). The steps: the quad's
+    // xors, the half-row mirror (lane i <-> 7 - i: the other quad of the eight), and at
+    // two per lane the rotation of the 16-lane row by 8
+    uint32_t amax = 0;
 #pragma unroll
-    for (int e = 0; e < EL; ++e) amax = fmaxf(amax, fabsf(q[e]));
-    amax = fmaxf(amax, dpp_f32<kDppQuadXor1>(amax));
-    amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
-    if constexpr (EL <= 4) amax = fmaxf(amax, swizzle_xor4(amax));
-    if constexpr (EL == 2) amax = fmaxf(amax, dpp_f32<kDppRowRor8>(amax));  // xor 8 in a row
-    const int ex = e8m0_exponent(__float_as_uint(amax));
+    for (int e = 0; e < EL; ++e) amax = max(amax, __float_as_uint(q[e]) & 0x7FFFFFFFu);
+    amax = max(amax, dpp_u32<kDppQuadXor1>(amax));
+    amax = max(amax, dpp_u32<kDppQuadXor2>(amax));
+    if constexpr (EL <= 4) amax = max(amax, dpp_u32<kDppRowHalfMirror>(amax));
+    if constexpr (EL == 2) amax = max(amax, dpp_u32<kDppRowRor8>(amax));
+    const int ex = e8m0_exponent(amax);
     const float sc = __uint_as_float((uint32_t)(127 - ex) << 23);
     // |q| * 2^-e <= 448 by the choice of e: in range, exact scaling
     if constexpr (EL == 8) {

@@ -149,6 +149,7 @@ constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kDppQuadXor3 = 0x1B;   // quad_perm [3,2,1,0]
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i within each eight
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
@@ -161,12 +162,6 @@ __device__ __forceinline__ float dpp_f32(float x) {
 template <int CTRL>
 __device__ __forceinline__ uint4 dpp_u4(const uint4& v) {
   return make_uint4(dpp_u32<CTRL>(v.x), dpp_u32<CTRL>(v.y), dpp_u32<CTRL>(v.z), dpp_u32<CTRL>(v.w));
-}
-
-// x of lane i ^ 4 within each group of 32 lanes (ds_swizzle bit mode: and 0x1F, or 0,
-// xor 4; no LDS allocation).
-__device__ __forceinline__ float swizzle_xor4(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
 }
 
 // Sum over the 64 lanes on the DPP path: within each row of 16 (quad xors, then row
