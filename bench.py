@@ -41,6 +41,8 @@ COPY_CALIBRATION_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "boundary_decode_r32_h7168_traffic.json")
 KSTATS_FILE = os.path.join(ROOT, "profiles", "boundary_decode_mxfp8_r32_h7168_kernel_stats.json")
 KERNEL_SOURCES = ["boundary.hip", "device_common.h", "kernels.h"]
+# the fused tile kernel's sources: the hash its counter summaries carry
+TILE_SOURCES = ["boundary_tile.hip", "device_common.h", "kernels.h", "coeff_epilogue.h"]
 
 
 def parse():
@@ -221,9 +223,11 @@ def time_entry(t, note):
             "note": note}
 
 
-def source_hash():
+def source_hash(files=None):
+    """Short hash of the headline kernel's sources (or of `files`, names under csrc/), which
+    a profile summary carries so that a stale one is recognised."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "mhc_hyper_connection_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

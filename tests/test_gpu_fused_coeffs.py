@@ -98,6 +98,7 @@ def test_fused_matches_oracle(kind, rows, hidden):
 @pytest.mark.parametrize("kind,rows,hidden,width", [
     ("finalize", 24, 2048, 12), ("finalize", 40, 1024, 3), ("finalize", 7, 4096, 1),
     ("boundary", 24, 2048, 1), ("boundary", 40, 1024, 3), ("boundary", 9, 4096, 13),
+    ("boundary", 6, 1024, 16),
 ])
 def test_fused_other_tp_and_top_k(kind, rows, hidden, width):
     """TP slice counts and top_k other than 8: the partial-slice loop's batches and the

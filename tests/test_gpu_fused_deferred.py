@@ -69,15 +69,15 @@ def _consume(h, kind, a, e, f, nxt2, rows):
     raise ValueError(kind)
 
 
-def _run(kind, deferred, rows, hidden):
-    d = synth.boundary_inputs(300 + rows, rows=rows, hidden=hidden, tp=8, x_sigma=0.5,
+def _run(kind, deferred, rows, hidden, tp=8):
+    d = synth.boundary_inputs(300 + rows, rows=rows, hidden=hidden, tp=tp, x_sigma=0.5,
                               mxfp8=hidden % 32 == 0)
-    e = synth.boundary_inputs(400 + rows, rows=rows, hidden=hidden, tp=8, x_sigma=0.5,
+    e = synth.boundary_inputs(400 + rows, rows=rows, hidden=hidden, tp=tp, x_sigma=0.5,
                               mxfp8=hidden % 32 == 0)
     f = synth.finalize_inputs(500 + rows, rows=rows, hidden=hidden, top_k=8)
     nxt, _ = _next_args(600 + rows, hidden)
     nxt2, _ = _next_args(700 + rows, hidden)
-    h = handle_for(hidden, rows)
+    h = handle_for(hidden, rows, tp=tp)
     a = _producer(h, d, nxt, deferred, rows)
     o = _consume(h, kind, a, e, f, nxt2, rows)
     torch.cuda.synchronize()
@@ -103,6 +103,19 @@ def test_deferred_fused_equals_undeferred(kind, rows, hidden):
         assert np.array_equal(a[k], b[k]), f"{kind}: {k} differs"
     for k in ("pre", "post", "comb"):
         assert not np.isnan(b[k]).any(), f"{kind}: {k} not written"
+
+
+@pytest.mark.parametrize("tp", [3, 13, 16])
+def test_deferred_fused_other_tp(tp):
+    """Slice counts other than 8 in the deferred producer and consumer: a short batch (its
+    loads past tp re-read the last slice and are dropped), a full batch and a short one,
+    two full batches."""
+    rows, hidden = 40, 2048
+    say(f"case: deferred fused consumer tp={tp} rows={rows} hidden={hidden}")
+    a = _run("fused_deferred", False, rows, hidden, tp)
+    b = _run("fused_deferred", True, rows, hidden, tp)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), f"tp {tp}: {k} differs"
 
 
 def test_deferred_fused_coefficients_match_the_oracle():
