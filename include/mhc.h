@@ -109,8 +109,8 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
  *     per call from the row count, see mhc_create). Each thread owns 8 hidden
  *     elements of a row, so a row is split into ceil(H / (8 * block)) workgroups; a size
  *     giving more than 64 of them, or more than half an XCD's resident workgroups, is
- *     MHC_ERR_UNSUPPORTED. (The residual-only kernels use 256 threads, four per 8
- *     elements.)
+ *     MHC_ERR_UNSUPPORTED. (The residual-only kernels use 512 threads, two elements
+ *     each.)
  *     Other values: MHC_ERR_SHAPE.
  *   MHC_OPT_SPIN_LIMIT: polls (each followed by a short sleep) before a row-handoff
  *     wait gives up; >= 0, default 2^20. Negative: MHC_ERR_SHAPE.

@@ -77,7 +77,7 @@ inline int block_index(int block) {
 inline bool block_usable(const mhc_ctx* h, int block) {
   const int i = block_index(block);
   if (i < 0) return false;
-  const int chunks = mhc::boundary_chunks(h->hidden, block, true);
+  const int chunks = mhc::boundary_chunks(h->hidden, block);
   return chunks <= kMaxChunks && h->wgs_per_xcd[i] / 2 >= chunks;
 }
 
@@ -151,7 +151,7 @@ void fill_mix(const mhc_ctx* h, mhc::BoundaryLaunch& L, const uint16_t* residual
     const int bn = block * (8 / el);
     if (block_index(bn) < 0) continue;
     const int wn = h->wgs_per_xcd[block_index(bn)];
-    if (wn / 2 < mhc::boundary_chunks(h->hidden, block, true)) continue;
+    if (wn / 2 < mhc::boundary_chunks(h->hidden, block)) continue;
     L.lane_elems = el;
     L.block_n = bn;
     L.max_wgs_per_xcd_n = wn;

@@ -6,17 +6,13 @@
 // stated in include/mhc.h.
 //
 // Work decomposition. A row (token) is split into `chunks` pieces; one
-// workgroup of BS threads owns one (row, chunk). Two layouts:
-//  - kernels that write a layer input: one lane per 16-byte vector (8 hidden
-//    elements). The lane loads the vector's partial slices (or gathered expert
-//    rows), its four streams and its norm weights, computes the four new
-//    streams, the collapse and its share of the row's sum of squares; BS
-//    vectors per workgroup.
-//  - residual-only kernels: four lanes (a quad) per vector. Lane q loads stream
-//    q and a quarter of the sublayer output, the quad combines its partial sums
-//    and exchanges the streams over DPP quad permutations, and lane q computes
-//    and stores stream q; BS / 4 vectors per workgroup, so four times the waves
-//    for the same bytes and a quarter of the per-lane arithmetic.
+// workgroup of BS threads owns one (row, chunk), one lane per vector of EL
+// consecutive hidden elements (EL = 8, 4 or 2: a 16-, 8- or 4-byte vector; BS
+// vectors per workgroup). The lane loads the vector's partial slices (or
+// gathered expert rows) and its four streams and computes the four new
+// streams; the kernels that write a layer input also load its norm weights and
+// compute the collapse and its share of the row's sum of squares. The
+// residual-only kernels run at two elements per lane and 512 threads.
 // A lane issues all of its loads before the first use and stores its new
 // streams as soon as they are computed; only the layer input (and its MXFP8
 // form) waits for the row's RMS.
@@ -58,7 +54,7 @@ namespace mhc {
 
 constexpr int kHC = 4;
 constexpr int kXcds = 8;
-constexpr int kResidualOnlyBlock = 256;
+constexpr int kResidualOnlyBlock = 512;  // threads, at two elements per lane
 
 struct BoundaryParams {
   // sublayer output: TP partials ...
@@ -133,156 +129,10 @@ __device__ __forceinline__ void deferred_finish(const DeferParams& d, int r, int
   }
 }
 
-// Residual-only, four lanes per 16-byte vector: lane q loads stream q and a quarter
-// of the sublayer output (slices or expert slots q, q+4, ...), the quad combines its
-// partial sums and exchanges the streams over DPP quad permutations, and lane q
-// computes and stores output stream q (BS / 4 vectors per workgroup).
-template <int BS, bool FINALIZE, bool DEFER>
-__device__ __forceinline__ void boundary_item_quad(const BoundaryParams& p,
-                                                   const DeferArg<DEFER>& dp, int r, int c,
-                                                   float* s_coef, float sc_l, float base_l) {
-  constexpr int kGroups = BS / 4;  // 16-byte vectors (8 elements) per workgroup
-  const int tid = threadIdx.x;
-  const int q = tid & 3;                     // this lane's output stream
-  const int v = c * kGroups + (tid >> 2);    // the quad's 16-byte vector index in the row
-  const bool active = v < p.hv;
-  const int va = active ? v : 0;             // an in-bounds vector for every lane's loads
-
-  // --- loads, all issued before any use; every address is in bounds, so no load sits
-  //     behind a branch and results of the lanes or slots that do not count are dropped
-  //     by selects afterwards
-  float x[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = 0.f;
-  // finalize: this lane's expert slots k = q, q+4, ... first, since the gathers need them
-  int pk[4];
-  float wk[4];
-  if constexpr (FINALIZE) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = 4 * u + q;
-      const bool in = k < p.top_k;
-      pk[u] = in ? p.idx[r * p.top_k + k] : -1;
-      wk[u] = in ? p.ew[r * p.top_k + k] : 0.f;
-    }
-  }
-  // this lane's mixes: post_q and cq[d] = comb[q][q ^ d], the weight of the stream
-  // that a xor-d quad move brings (deferred: from LDS once wave 0 has finished them)
-  float post_q = 0.f;
-  float cq[kHC];
-  if constexpr (!DEFER) {
-    post_q = p.post[r * kHC + q];
-#pragma unroll
-    for (int d = 0; d < kHC; ++d) cq[d] = p.comb[(r * kHC + q) * kHC + (q ^ d)];
-  }
-  const uint4 sv = load_nt(p.res_in + ((size_t)r * kHC + q) * p.hv + va);
-  CoeffPrefetch<kBoundaryPrefetch> cf;
-  if constexpr (DEFER)
-    if (tid < kWave) coeff_row_prefetch<true>(dp.coef, r, tid, cf);
-
-  if constexpr (!FINALIZE) {
-    // lane q sums slices t = q, q+4, q+8, ... (ascending)
-    const uint4* src = p.xp + (size_t)r * p.hv + va;
-    const size_t slice = (size_t)p.rows * p.hv;
-    for (int t0 = 0; t0 < p.tp; t0 += 16) {
-      uint4 xv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (t0 + 4 * u < p.tp) {  // uniform: some lane of the quad has slice t0 + 4u + q
-          const int t = t0 + 4 * u + q;
-          xv[u] = load_nt(src + (size_t)(t < p.tp ? t : 0) * slice);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (t0 + 4 * u < p.tp) {
-          const bool in = t0 + 4 * u + q < p.tp;
-          float f[8];
-          unpack8(xv[u], f);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] += in ? f[e] : 0.f;
-        }
-      }
-    }
-  } else {
-    // lane q gathers slots k = q, q+4, ... (ascending); lane 3 also adds the shared row
-    const uint4 shv = load_nt(p.shared + (size_t)r * p.hv + va);
-    uint4 gv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (4 * u < p.top_k) {
-        const bool ok = pk[u] >= 0 && pk[u] < p.num_permuted;
-        gv[u] = load_nt(p.g + (size_t)(ok ? pk[u] : 0) * p.hv + va);
-        if (!ok) wk[u] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (4 * u < p.top_k) {
-        float f[8];
-        unpack8(gv[u], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(wk[u], f[e], x[e]);
-      }
-    }
-    // top_k beyond 16: further slots, in the same lane order
-    for (int k0 = 16; k0 < p.top_k; k0 += 4) {
-      const int k = k0 + q;
-      const bool in = k < p.top_k;
-      const int pi = in ? p.idx[r * p.top_k + k] : -1;
-      const bool ok = pi >= 0 && pi < p.num_permuted;
-      const float w = ok ? p.ew[r * p.top_k + k] : 0.f;
-      const uint4 g = load_nt(p.g + (size_t)(ok ? pi : 0) * p.hv + va);
-      float f[8];
-      unpack8(g, f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(w, f[e], x[e]);
-    }
-    float f[8];
-    unpack8(shv, f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] += (q == 3) ? f[e] : 0.f;
-  }
-
-  // the quad's four partial sums -> the full sum in every lane (a + b == b + a exactly)
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    x[e] += dpp_f32<kDppQuadXor1>(x[e]);
-    x[e] += dpp_f32<kDppQuadXor2>(x[e]);
-  }
-  round8_bf16(x);  // the reduced output is a bf16 tensor
-  if constexpr (DEFER) {
-    if (tid < kWave) deferred_finish(dp, r, c, cf, sc_l, base_l, s_coef);
-    __syncthreads();
-    post_q = s_coef[kHC + q];
-#pragma unroll
-    for (int d = 0; d < kHC; ++d) cq[d] = s_coef[2 * kHC + q * kHC + (q ^ d)];
-  }
-
-  // --- mHC post for stream q: s'_q = post_q x + sum_j comb_qj s_j -------------------
-  uint4 sj[kHC];
-  sj[0] = sv;
-  sj[1] = dpp_u4<kDppQuadXor1>(sv);
-  sj[2] = dpp_u4<kDppQuadXor2>(sv);
-  sj[3] = dpp_u4<kDppQuadXor3>(sv);
-  float o[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = post_q * x[e];
-#pragma unroll
-  for (int d = 0; d < kHC; ++d) {
-    float f[8];
-    unpack8(sj[d], f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(cq[d], f[e], o[e]);
-  }
-  if (active) store_nt(p.res_out + ((size_t)r * kHC + q) * p.hv + v, pack8_round(o));
-  if constexpr (DEFER) __syncthreads();  // s_coef is rewritten for the next row
-}
-
 // One lane per vector of EL consecutive elements (EL = 8, 4 or 2: 16-, 8- or 4-byte
 // vectors): the lane owns those elements of the row and all four streams of them (BS
-// vectors per workgroup). The quad layout's dataflow, plus the collapse, the row handoff
-// and the layer input.
+// vectors per workgroup). Every kernel computes the new streams here; with HAS_PRE also
+// the collapse, the row handoff and the layer input.
 template <int BS, bool FINALIZE, bool HAS_PRE, bool MXFP8, int MODE, bool DEFER, int EL>
 __device__ __forceinline__ void boundary_item_lane(const BoundaryParams& p_arg,
                                                    const float* __restrict__ post,
@@ -624,8 +474,6 @@ __global__ __launch_bounds__(BS, DEFER ? 4 : 1) void boundary_kernel(const Bound
                                                       const float* __restrict__ ew,
                                                       const DeferArg<DEFER> dp) {
   prefetch_kernargs<sizeof(BoundaryParams) + 5 * sizeof(void*) + sizeof(DeferArg<DEFER>)>();
-  // the layer-input kernels (with the row handoff) run one lane per vector; the
-  // residual-only kernels run four lanes per vector
   __shared__ float s_coef[2 * kHC + kHC * kHC];
   float sc_l = 0.f, base_l = 0.f;  // deferred coefficients: this lane's scale and base
   if constexpr (DEFER) coeff_lane_scale_base(dp.coef, threadIdx.x & (kWave - 1), &sc_l, &base_l);
@@ -640,11 +488,8 @@ __global__ __launch_bounds__(BS, DEFER ? 4 : 1) void boundary_kernel(const Bound
     // the layer-input kernels have no barrier after the coefficients are read: one here
     // keeps a later round's finish from overwriting them while a wave still reads them
     if (DEFER && HAS_PRE && round > 0) __syncthreads();
-    if constexpr (!HAS_PRE)
-      boundary_item_quad<BS, FINALIZE, DEFER>(p, dp, r, c, s_coef, sc_l, base_l);
-    else
-      boundary_item_lane<BS, FINALIZE, HAS_PRE, MXFP8, MODE, DEFER, EL>(
-          p, post, comb, pre, idx, ew, dp, r, c, s_coef, sc_l, base_l);
+    boundary_item_lane<BS, FINALIZE, HAS_PRE, MXFP8, MODE, DEFER, EL>(
+        p, post, comb, pre, idx, ew, dp, r, c, s_coef, sc_l, base_l);
   }
 }
 
@@ -691,6 +536,13 @@ static hipError_t launch_one(const BoundaryParams& p, const DeferParams& d, int 
 template <int BS, bool DEFER>
 static hipError_t launch_mix(const BoundaryParams& p, const DeferParams& d, bool fin, bool pre,
                              bool mx, int el, int grid, hipStream_t st) {
+  if (!pre) {  // residual-only: always two elements per lane at 512 threads
+    if constexpr (BS == kResidualOnlyBlock)
+      if (el == 2)
+        return fin ? launch_one<BS, true, false, false, kBoundaryMix, DEFER, 2>(p, d, grid, st)
+                   : launch_one<BS, false, false, false, kBoundaryMix, DEFER, 2>(p, d, grid, st);
+    return hipErrorInvalidValue;
+  }
   if constexpr (BS == 512) {
     if (el == 2 && pre) {  // two elements per lane (the layer-input kernels)
       if (!fin)
@@ -709,12 +561,9 @@ static hipError_t launch_mix(const BoundaryParams& p, const DeferParams& d, bool
                 : launch_one<BS, true, true, false, kBoundaryMix, DEFER, 4>(p, d, grid, st);
     }
   }
-  if (!fin) {
-    if (!pre) return launch_one<BS, false, false, false, kBoundaryMix, DEFER>(p, d, grid, st);
+  if (!fin)
     return mx ? launch_one<BS, false, true, true, kBoundaryMix, DEFER>(p, d, grid, st)
               : launch_one<BS, false, true, false, kBoundaryMix, DEFER>(p, d, grid, st);
-  }
-  if (!pre) return launch_one<BS, true, false, false, kBoundaryMix, DEFER>(p, d, grid, st);
   return mx ? launch_one<BS, true, true, true, kBoundaryMix, DEFER>(p, d, grid, st)
             : launch_one<BS, true, true, false, kBoundaryMix, DEFER>(p, d, grid, st);
 }
@@ -799,14 +648,13 @@ int boundary_resident_wgs_per_cu(int block) {
   }
 }
 
-int boundary_chunks(int hidden, int block, bool has_pre) {
-  const int hv = hidden / 8;
-  const int per_wg = has_pre ? block : block / 4;  // 16-byte vectors per workgroup
-  return (hv + per_wg - 1) / per_wg;
+int boundary_chunks(int hidden, int block) {
+  const int hv = hidden / 8;  // 16-byte vectors; `block` of them per workgroup
+  return (hv + block - 1) / block;
 }
 
 int boundary_handoff_words(int hidden) {
-  return (boundary_chunks(hidden, 128, true) * (512 / kWave) + 15) / 16 * 16;
+  return (boundary_chunks(hidden, 128) * (512 / kWave) + 15) / 16 * 16;
 }
 
 hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
@@ -844,14 +692,15 @@ hipError_t launch_boundary(const BoundaryLaunch& L, hipStream_t stream) {
   // the shorter per-lane work saves). Deferred and undeferred calls choose alike, so their
   // results stay bit-identical. Not the first layer's entry, which has almost no arithmetic
   // to share (measured 4.19 at eight against 4.22 us at four per lane, 32 rows).
-  const int chunks8 = boundary_chunks(L.hidden, pre ? L.block : kResidualOnlyBlock, pre);
+  // (the residual-only kernels: 512 threads at two per lane, the chunks of 128 at eight)
+  const int chunks8 = boundary_chunks(L.hidden, pre ? L.block : kResidualOnlyBlock / 4);
   bool narrow = L.lane_elems < 8 && pre && L.mode != kBoundaryFirst && L.block_n >= 256;
   if (narrow) {
     const int r8 = rows_per_round(L.max_wgs_per_xcd, chunks8);
     const int rn = rows_per_round(L.max_wgs_per_xcd_n, chunks8);
     narrow = (row_blocks + rn - 1) / rn <= (row_blocks + r8 - 1) / r8;
   }
-  const int el = narrow ? L.lane_elems : 8;
+  const int el = !pre ? 2 : (narrow ? L.lane_elems : 8);
   const int block = !pre ? kResidualOnlyBlock : (narrow ? L.block_n : L.block);
   const int max_wgs_per_xcd = narrow ? L.max_wgs_per_xcd_n : L.max_wgs_per_xcd;
   p.chunks = chunks8;

@@ -146,7 +146,6 @@ __device__ __forceinline__ size_t mx_scale_offset(int r, int kb, int kblocks, in
 // within each group of 4 lanes; row rotations within each row of 16 lanes.
 constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
-constexpr int kDppQuadXor3 = 0x1B;   // quad_perm [3,2,1,0]
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i within each eight
@@ -158,10 +157,6 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ uint4 dpp_u4(const uint4& v) {
-  return make_uint4(dpp_u32<CTRL>(v.x), dpp_u32<CTRL>(v.y), dpp_u32<CTRL>(v.z), dpp_u32<CTRL>(v.w));
 }
 
 // Sum over the 64 lanes on the DPP path: within each row of 16 (quad xors, then row

@@ -114,7 +114,8 @@ int boundary_tile_part_ks(int hidden);
 bool boundary_tile_fits(int hidden, int wgs_per_xcd);
 hipError_t launch_boundary_tile(const TileLaunch& T, hipStream_t stream);
 
-int boundary_chunks(int hidden, int block, bool has_pre);
+// chunks of a row: ceil(hidden / 8 / block), `block` 16-byte vectors per workgroup
+int boundary_chunks(int hidden, int block);
 // Row-handoff words per row: one per wave at the most waves a row can have (the
 // 128-thread chunks at 512 threads), rounded up to 16 (a 128-byte line).
 int boundary_handoff_words(int hidden);

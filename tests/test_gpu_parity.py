@@ -55,10 +55,10 @@ def test_config1_residual_only_equals_full_streams():
     full = gpu_boundary(h, d)
     o = oracle_boundary(d, residual_only=True)
     assert_bf16_close(ro["residual"], o["residual"], "config 1 residual-only")
-    # the two kernels sum in different orders: equal within the bf16 tolerance, mostly bitwise
-    same = assert_bf16_close(ro["residual"], full["residual"], "residual-only vs full streams")
-    say(f"  residual-only and full streams bit-identical in {same:.4%} of elements")
-    assert same > 0.99
+    # both run the same lane code for the streams (two elements per lane, the same slice
+    # and mix order): bit-identical
+    assert np.array_equal(ro["residual"], full["residual"]), "residual-only vs full streams"
+    assert h.errors() == 0
 
 
 def test_config2_moe_finalize_mxfp8():
@@ -70,7 +70,10 @@ def test_config2_moe_finalize_mxfp8():
     st = compare_boundary_outputs(g, o, "config 2")
     say(f"  {st}")
     ro = gpu_finalize(h, d, pre=False)
-    assert assert_bf16_close(ro["residual"], g["residual"], "finalize residual-only vs full") > 0.99
+    # the same lane code for the streams (elementwise arithmetic does not depend on how many
+    # elements a lane holds): bit-identical
+    assert np.array_equal(ro["residual"], g["residual"]), "finalize residual-only vs full"
+    assert h.errors() == 0
 
 
 def test_config3_pre_coeffs():
