@@ -114,6 +114,36 @@ def test_boundary_ragged(rows, hidden, tp, block):
     compare_boundary_outputs(gpu_boundary(h, d), oracle_boundary(d), f"ragged {rows}x{hidden}")
 
 
+@pytest.mark.parametrize("rows,hidden,tp", [
+    (1, 512, 1), (5, 1056, 3), (13, 3072, 13), (3, 8 * 40, 16), (9, 2080, 8), (40, 7168, 8),
+])
+def test_residual_only_ragged(rows, hidden, tp):
+    """The residual-only kernel (no layer input) on ragged shapes: one partly idle chunk
+    (hidden 320), a ragged last chunk, ragged slice groups; its streams match the oracle and
+    are bit-identical to a full call's on the same inputs."""
+    say(f"case: residual-only rows={rows} hidden={hidden} tp={tp}")
+    d = synth.boundary_inputs(150 + rows, rows=rows, hidden=hidden, tp=tp, mxfp8=False)
+    h = handle_for(hidden, rows, tp=tp)
+    ro = gpu_boundary(h, d, residual_only=True)
+    assert_bf16_close(ro["residual"], oracle_boundary(d, residual_only=True)["residual"],
+                      f"residual-only {rows}x{hidden}")
+    full = gpu_boundary(h, d)
+    assert np.array_equal(ro["residual"], full["residual"]), "residual-only vs full streams"
+    assert h.errors() == 0
+
+
+@pytest.mark.parametrize("rows,hidden,top_k", [(7, 1056, 3), (4, 2048, 12), (33, 7168, 8)])
+def test_finalize_residual_only_ragged(rows, hidden, top_k):
+    say(f"case: finalize residual-only rows={rows} hidden={hidden} top_k={top_k}")
+    d = synth.finalize_inputs(250 + rows, rows=rows, hidden=hidden, top_k=top_k, mxfp8=False)
+    h = handle_for(hidden, rows, tp=1, top_k=top_k)
+    ro = gpu_finalize(h, d, pre=False)
+    assert_bf16_close(ro["residual"], oracle_finalize(d, pre=False)["residual"],
+                      f"finalize residual-only {rows}x{hidden}")
+    assert np.array_equal(ro["residual"], gpu_finalize(h, d)["residual"])
+    assert h.errors() == 0
+
+
 @pytest.mark.parametrize("rows,hidden,top_k,block", [
     (1, 512, 1, 128), (7, 1056, 3, 256), (20, 7168, 8, 512), (4, 2048, 12, 256),
 ])
