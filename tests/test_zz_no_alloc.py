@@ -63,6 +63,27 @@ def test_noalloc_boundary_equals_the_handle_boundary_on_two_calls():
         compare_boundary_outputs(got, oracle_boundary(d), f"allocation-free, {what}")
 
 
+def test_noalloc_residual_only_equals_the_handle_call():
+    """pre = NULL: the residual-only form (no layer input, no row handoff) through the
+    allocation-free entry, bit-identical to mhc_residual_only on a handle and within the
+    oracle's tolerance."""
+    d = synth.boundary_inputs(43, rows=9, hidden=3072, tp=8)
+    say("case: allocation-free residual-only rows=9 hidden=3072 tp=8")
+    fn = _lib()
+    tp, rows, hidden = d["x_partials"].shape
+    t = {k: T(d[k]) for k in ("x_partials", "residual", "post", "comb")}
+    ro = torch.empty_like(t["residual"])
+    st = fn(hidden, _vp(t["x_partials"].data_ptr()), tp, _vp(t["residual"].data_ptr()),
+            _vp(t["post"].data_ptr()), _vp(t["comb"].data_ptr()), None, None, 0.0, rows,
+            _vp(ro.data_ptr()), None, None, None, 0, _vp(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, binding.load_library().mhc_status_string(st)
+    torch.cuda.synchronize()
+    want = gpu_boundary(handle_for(hidden, rows, tp=tp), d, residual_only=True)
+    assert np.array_equal(N(ro), want["residual"])
+    compare_boundary_outputs({"residual": N(ro)}, oracle_boundary(d, residual_only=True),
+                             "allocation-free residual-only")
+
+
 def test_noalloc_boundary_rejects_sizes_beyond_its_scratch():
     say("case: allocation-free boundary, limits")
     fn = _lib()
