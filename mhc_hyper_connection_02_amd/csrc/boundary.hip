@@ -485,9 +485,10 @@ __global__ __launch_bounds__(BS, DEFER ? 4 : 1) void boundary_kernel(const Bound
   for (int round = 0; round < p.rounds; ++round) {
     const int r = (round * p.rows_per_round + jr) * kXcds + xcd;
     if (r >= p.rows) break;  // uniform per workgroup; later rounds only go higher
-    // the layer-input kernels have no barrier after the coefficients are read: one here
+    // the lane kernels have no barrier after the deferred coefficients are read: one here
     // keeps a later round's finish from overwriting them while a wave still reads them
-    if (DEFER && HAS_PRE && round > 0) __syncthreads();
+    // (the residual-only calls take one round, so it never runs for them)
+    if (DEFER && round > 0) __syncthreads();
     boundary_item_lane<BS, FINALIZE, HAS_PRE, MXFP8, MODE, DEFER, EL>(
         p, post, comb, pre, idx, ew, dp, r, c, s_coef, sc_l, base_l);
   }
