@@ -140,9 +140,10 @@ int mhc_create(int hidden, int hc_mult, int max_rows, int max_tp, int top_k, int
  *     MHC_ERR_SHAPE.
  *   MHC_OPT_TILE_PLACEMENT: where the fused calls' single kernel (mhc_boundary_coeffs,
  *     mhc_finalize_coeffs) runs the 256-element chunks of a 16-row tile:
- *       MHC_TILE_PER_XCD (default): all chunks of a tile on one XCD (tiles dealt to XCDs);
- *       MHC_TILE_SPREAD: chunk c of every tile on XCD c % 8, so each XCD reads only its
- *         chunks' rows of fn, and a call of few rows still uses every XCD.
+ *       MHC_TILE_SPREAD (default): chunk c of every tile on XCD c % 8, so each XCD reads
+ *         only its chunks' rows of fn, and a call of few rows still uses every XCD;
+ *       MHC_TILE_PER_XCD: all chunks of a tile on one XCD (tiles dealt to XCDs), ahead
+ *         when the same fn is reused by consecutive calls while it is still cached.
  *     Results are identical either way (the same arithmetic per chunk and the same order
  *     of every sum). Other values: MHC_ERR_SHAPE.
  *   MHC_OPT_ROW_HANDOFF: how the workgroups of a row exchange their partial sums in
